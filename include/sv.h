@@ -1,0 +1,183 @@
+/*
+ * sv.h -- SparseVILA decoupled visual sparsity: the data-parallel hot path on
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * Method (arXiv 2510.17777, "SparseVILA: Decoupling Visual Sparsity for
+ * Efficient VLM Inference"): prefill prunes visual tokens by query-agnostic
+ * salience computed from the vision encoder's self-attention; decode keeps
+ * the retained visual KV cache and, per query, activates only the top-k most
+ * relevant visual tokens for attention.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or writes its inputs; outputs and the
+ *    caller-provided workspace are the only memory it writes.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Nothing synchronises; results are valid once the stream has
+ *    executed the enqueued work.  Device-side faults surface at the caller's
+ *    next synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    non-OK status means nothing was launched (except SV_EHIP, which reports
+ *    a failed launch); sv_last_error() then returns a thread-local message.
+ *  - Element strides are in ELEMENTS, not bytes.  Within a token row the
+ *    layout is [H][D] with D contiguous (head stride D).
+ *  - Outputs that are indices are int32; scores, salience and attention
+ *    outputs are fp32.  No C++ exception crosses this boundary.
+ *  - NaN or Inf inputs give unspecified (but memory-safe) results.
+ *  - Concurrent calls on different streams are safe if their workspaces and
+ *    outputs do not overlap.
+ */
+#ifndef SV_H_
+#define SV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_EINVAL = 1,        /* bad shape, count, pointer or stride           */
+  SV_EUNSUPPORTED = 2,  /* valid request outside the compiled kernels     */
+  SV_EWORKSPACE = 3,    /* workspace_bytes below the *_workspace() size   */
+  SV_EHIP = 4           /* a HIP runtime call or kernel launch failed     */
+} sv_status;
+
+typedef enum {
+  SV_F32 = 0,           /* IEEE binary32                                  */
+  SV_BF16 = 1           /* bfloat16 (upper half of binary32)              */
+} sv_dtype;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sv_version(void);
+
+/* Message describing the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* sv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Query-aware retrieval (decode stage)
+ *
+ * SparseVILA velog summary, Sec. 3.2 "Query-Aware Token Selection": the
+ * current text query is the Query, the cached vision tokens are the Keys,
+ * and the aggregated attention strength ranks the tokens; high scorers are
+ * activated, the rest stay cached but deactivated.  xllm-io review,
+ * core formulas: Selected = TopK(Query . KV_Cache, k).
+ *
+ * Computes, per sequence b,
+ *     s[b,t] = sum_{tau<Tq} sum_{h<Hq} q[b,tau,h,:] . K[b,t,h/G,:]   (G = Hq/Hkv)
+ * (raw logits, no 1/sqrt(D)), then the k largest s[b,.] with ties broken
+ * toward the lower token index, written in ascending index order.
+ *
+ *  q          [B][Tq][Hq][D], contiguous, dtype `dtype`.  Tq = 1 scores the
+ *             current decode token; Tq > 1 scores a whole question.
+ *  k_vis      retained visual keys: element (b,t,g,d) at
+ *             k_vis[b*k_bstride + t*k_tstride + g*D + d].  Read only.
+ *  N          visual tokens per sequence (N >= 1).
+ *  k          tokens to select, 0 <= k <= N.
+ *  idx_out    [B][k] int32, ascending, distinct, each in [0, N).
+ *  scores_out optional [B][N] fp32 scores s (NULL to skip).
+ *  workspace  at least sv_retrieve_workspace(B, N, k) bytes, 256-byte
+ *             aligned; contents on entry are ignored.
+ * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hkv*D <= 8192 (bf16)
+ * or <= 4096 (fp32); Hq % Hkv == 0; Hq/Hkv <= 64; B <= 65535.
+ * Errors: SV_EINVAL (k > N, k < 0, N < 1, B < 1, Tq < 1, Hq % Hkv != 0,
+ * NULL q/k_vis/idx_out/workspace, strides smaller than a row),
+ * SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_retrieve_workspace(int B, int N, int k);
+
+sv_status sv_retrieve(const void* q, int B, int Tq, int Hq,
+                      const void* k_vis, int64_t k_bstride, int64_t k_tstride,
+                      int N, int Hkv, int D, sv_dtype dtype, int k,
+                      int32_t* idx_out, float* scores_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse decode attention over the retrieved visual entries plus the text
+ * entries (decode stage)
+ *
+ * SparseVILA velog summary, Sec. 3.2 (only the query-relevant subset of the
+ * visual cache is activated; the cache itself is kept) and Sec. 4.5
+ * (decoding attention over the reduced effective KV cache).
+ *
+ * For each sequence b and query head h (KV head g = h / G):
+ *     E = { visual idx[b][0..k) } U { text rows 0..txt_len[b]-1 }
+ *     z_j = scale * q[b,h,:] . K_j[g,:]
+ *     out[b,h,:] = sum_j softmax(z)_j V_j[g,:]
+ * Visual indices outside [0, N) are skipped; txt_len[b] is clamped to
+ * [0, Tmax].  If E is empty for some b, out[b,:,:] = 0.
+ *
+ *  q          [B][Hq][D], contiguous, dtype `dtype` (the current token's
+ *             post-RoPE queries).
+ *  k_vis,v_vis visual cache, element (b,t,g,d) at
+ *             ptr[b*vis_bstride + t*vis_tstride + g*D + d].  Read only.
+ *  idx        [B][k] int32 visual token indices (any order; distinct).
+ *  k_txt,v_txt text cache, element (b,t,g,d) at
+ *             ptr[b*txt_bstride + t*txt_tstride + g*D + d], t < Tmax.
+ *             May be NULL only if Tmax == 0.
+ *  txt_len    [B] int32 device array, text rows attended per sequence.
+ *  scale      softmax scale; <= 0 selects 1/sqrt(D).
+ *  out        [B][Hq][D] fp32.
+ *  workspace  at least sv_sparse_decode_attn_workspace(B, Hq, Hkv, D, k, Tmax)
+ *             bytes, 256-byte aligned.
+ * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hq/Hkv in 1..8.
+ * Errors: SV_EINVAL (k < 0, k + Tmax == 0, k > N, Hq % Hkv != 0, NULL
+ * required pointer, B < 1), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax);
+
+sv_status sv_sparse_decode_attn(const void* q, int B, int Hq,
+                                const void* k_vis, const void* v_vis,
+                                int64_t vis_bstride, int64_t vis_tstride, int N,
+                                int Hkv, int D, const int32_t* idx, int k,
+                                const void* k_txt, const void* v_txt,
+                                int64_t txt_bstride, int64_t txt_tstride,
+                                const int32_t* txt_len, int Tmax,
+                                sv_dtype dtype, float scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Query-agnostic salience and per-frame pruning (prefill stage)
+ *
+ * SparseVILA velog summary, Sec. 3.1: salience is read off the vision
+ * encoder's self-attention; for encoders without a summary token (SigLIP,
+ * QwenVL) it is the intra-visual attention averaged over all tokens, and the
+ * lowest-salience tokens are pruned before the cache is stored.  The same
+ * section's kernel streams the softmax normalisation and the salience
+ * accumulation without materialising the attention matrix.  xllm-io review,
+ * core formulas: Salience(t_i) = (1/N) sum_j Attention(., .), read as the
+ * attention token i receives (column mean).
+ *
+ * For each frame f (an independent attention of N tokens) and head h:
+ *     A_h = row_softmax(scale * Q_h K_h^T)                 (never stored)
+ *     sal[f,j] = (1/H) sum_h (1/N) sum_i A_h[i,j]           (sums to 1)
+ * then the `keep` largest sal[f,.] (ties toward the lower index) in
+ * ascending order.
+ *
+ *  vis_q,vis_k [F][H][N][D] contiguous bf16 (one encoder layer's Q and K).
+ *  scale       softmax scale; <= 0 selects 1/sqrt(D).
+ *  keep        tokens kept per frame, 0 <= keep <= N.
+ *  salience_out optional [F][N] fp32 (NULL to skip).
+ *  idx_out     [F][keep] int32 ascending (may be NULL if keep == 0).
+ *  workspace   at least sv_salience_prune_workspace(F, H, N) bytes,
+ *              256-byte aligned.
+ * Supported: dtype SV_BF16; D a multiple of 8 with 8 <= D <= 96;
+ * 1 <= N <= 768 (one frame-head's keys stay in LDS); F*H <= 2^31-1.
+ * Errors: SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_salience_prune_workspace(int F, int H, int N);
+
+sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H,
+                            int N, int D, sv_dtype dtype, float scale, int keep,
+                            float* salience_out, int32_t* idx_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H_ */

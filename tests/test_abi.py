@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before anything is launched.
+
+Only calls that fail host-side validation are made here (plus the workspace
+size queries), so no kernel is ever enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import visual_token_sparsity_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sv.lib_path()), reason="libsv.so not built")
+
+FAKE = 0x10000  # 16-byte aligned non-NULL address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = sv.load()
+    names = declared_functions()
+    assert {"sv_retrieve", "sv_sparse_decode_attn", "sv_salience_prune"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_empty_error():
+    lib = sv.load()
+    assert lib.sv_version() >= 100
+    assert isinstance(lib.sv_last_error(), bytes)
+
+
+def test_workspace_sizes():
+    assert sv.retrieve_workspace_bytes(8, 1440, 360) >= 8 * 1440 * 4
+    assert sv.retrieve_workspace_bytes(8, 1440, 360) % 256 == 0
+    w = sv.sparse_decode_attn_workspace_bytes(8, 32, 32, 128, 360, 256)
+    assert w >= 8 * 32 * 130 * 4 and w % 256 == 0
+    assert sv.salience_prune_workspace_bytes(256, 16, 729) >= 256 * 16 * 729 * 4
+
+
+def _retrieve(**kw):
+    a = dict(q=FAKE, B=1, Tq=1, Hq=32, kv=FAKE, bs=576 * 4096, ts=4096, N=576, Hkv=32, D=128,
+             dt=sv.SV_BF16, k=144, idx=FAKE, sc=None, ws=FAKE, wsb=1 << 20, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_retrieve(a["q"], a["B"], a["Tq"], a["Hq"], a["kv"], a["bs"], a["ts"], a["N"],
+                           a["Hkv"], a["D"], a["dt"], a["k"], a["idx"], a["sc"], a["ws"], a["wsb"],
+                           a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=577), 1), (dict(k=-1), 1), (dict(N=0), 1), (dict(B=0), 1), (dict(Tq=0), 1),
+    (dict(Hq=30, Hkv=4), 1), (dict(q=None), 1), (dict(idx=None), 1), (dict(ws=None), 1),
+    (dict(ts=100), 1), (dict(ts=4100), 1), (dict(q=FAKE + 2), 1),
+    (dict(D=96), 2), (dict(dt=7), 2), (dict(Hkv=128, Hq=128), 2),
+    (dict(wsb=100), 3),
+])
+def test_retrieve_rejects(kw, status):
+    assert _retrieve(**kw) == status
+    assert sv.load().sv_last_error()
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, B=1, Hq=28, kv=FAKE, vv=FAKE, vbs=0, vts=512, N=100, Hkv=4, D=128, idx=FAKE,
+             k=10, kt=FAKE, vt=FAKE, tbs=0, tts=512, tl=FAKE, Tmax=8, dt=sv.SV_BF16, scale=0.0,
+             out=FAKE, ws=FAKE, wsb=1 << 22, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_sparse_decode_attn(a["q"], a["B"], a["Hq"], a["kv"], a["vv"], a["vbs"], a["vts"],
+                                     a["N"], a["Hkv"], a["D"], a["idx"], a["k"], a["kt"], a["vt"],
+                                     a["tbs"], a["tts"], a["tl"], a["Tmax"], a["dt"], a["scale"],
+                                     a["out"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=101), 1), (dict(k=-1), 1), (dict(k=0, Tmax=0), 1), (dict(Hq=30), 1),
+    (dict(idx=None), 1), (dict(kt=None), 1), (dict(tl=None), 1), (dict(out=None), 1),
+    (dict(vts=500), 1), (dict(B=0), 1),
+    (dict(Hq=36, Hkv=4), 2), (dict(D=80), 2), (dict(dt=3), 2),
+    (dict(wsb=16), 3),
+])
+def test_attn_rejects(kw, status):
+    assert _attn(**kw) == status
+
+
+def _sal(**kw):
+    a = dict(q=FAKE, k=FAKE, F=2, H=16, N=729, D=72, dt=sv.SV_BF16, scale=0.0, keep=364,
+             sal=None, idx=FAKE, ws=FAKE, wsb=1 << 24, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_salience_prune(a["q"], a["k"], a["F"], a["H"], a["N"], a["D"], a["dt"],
+                                 a["scale"], a["keep"], a["sal"], a["idx"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(keep=730), 1), (dict(keep=-1), 1), (dict(F=0), 1), (dict(idx=None), 1),
+    (dict(q=None), 1), (dict(q=FAKE + 8), 1),
+    (dict(dt=sv.SV_F32), 2), (dict(N=769), 2), (dict(D=100), 2), (dict(D=70), 2),
+    (dict(wsb=1024), 3),
+])
+def test_salience_rejects(kw, status):
+    assert _sal(**kw) == status
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sv.retrieve(q, kv, 2)

@@ -1,0 +1,236 @@
+"""SparseVILA decoupled visual sparsity on MI355X: Python binding of libsv.
+
+A thin ctypes layer over the C ABI in include/sv.h.  It marshals torch
+tensors (device memory and the current HIP stream) into pointers and sizes;
+every step of the computation runs in the HIP kernels of libsv.so.  There is
+no CPU fallback: if libsv.so is missing or a tensor is not on a GPU, the call
+raises.
+
+    idx = retrieve(q, k_vis, k)                          # query-aware retrieval
+    out = sparse_decode_attn(q, k_vis, v_vis, idx,       # attention over the
+                             k_txt, v_txt, txt_len)      #   selected + text entries
+    sal, keep_idx = salience_prune(vis_q, vis_k, keep)   # prefill salience prune
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loaded first so libsv binds to torch's HIP runtime
+
+__all__ = [
+    "SvError", "lib_path", "load", "retrieve", "retrieve_workspace_bytes",
+    "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
+    "salience_prune_workspace_bytes", "SV_F32", "SV_BF16",
+]
+
+SV_F32, SV_BF16 = 0, 1
+_STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EWORKSPACE", 4: "SV_EHIP"}
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class SvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libsv.so (built in-tree by visual_token_sparsity_amd.build)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m visual_token_sparsity_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_i, c_i64, c_p, c_sz, c_f = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    lib.sv_version.restype = c_i
+    lib.sv_last_error.restype = ctypes.c_char_p
+    lib.sv_retrieve_workspace.argtypes = [c_i, c_i, c_i]
+    lib.sv_retrieve_workspace.restype = c_sz
+    lib.sv_retrieve.argtypes = [c_p, c_i, c_i, c_i, c_p, c_i64, c_i64, c_i, c_i, c_i, c_i, c_i,
+                                c_p, c_p, c_p, c_sz, c_p]
+    lib.sv_retrieve.restype = c_i
+    lib.sv_sparse_decode_attn_workspace.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i]
+    lib.sv_sparse_decode_attn_workspace.restype = c_sz
+    lib.sv_sparse_decode_attn.argtypes = [c_p, c_i, c_i, c_p, c_p, c_i64, c_i64, c_i, c_i, c_i,
+                                          c_p, c_i, c_p, c_p, c_i64, c_i64, c_p, c_i, c_i, c_f,
+                                          c_p, c_p, c_sz, c_p]
+    lib.sv_sparse_decode_attn.restype = c_i
+    lib.sv_salience_prune_workspace.argtypes = [c_i, c_i, c_i]
+    lib.sv_salience_prune_workspace.restype = c_sz
+    lib.sv_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_p, c_p,
+                                      c_p, c_sz, c_p]
+    lib.sv_salience_prune.restype = c_i
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SvError(status, load().sv_last_error().decode())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _on_gpu(*ts: torch.Tensor) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libsv runs on the GPU only: every tensor must be on a HIP device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _cache_strides(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    """[B][T][H][D] cache with contiguous [H][D] rows; returns (batch, token) strides."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B][T][H][D]")
+    if t.stride(3) != 1 or t.stride(2) != t.shape[3]:
+        raise ValueError(f"{name}: each token row must be a contiguous [H][D] block")
+    return t.stride(0), t.stride(1)
+
+
+def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+def retrieve_workspace_bytes(B: int, N: int, k: int) -> int:
+    return int(load().sv_retrieve_workspace(B, N, k))
+
+
+def retrieve(q: torch.Tensor, k_vis: torch.Tensor, k: int, *, scores: bool = False,
+             workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Top-k visual tokens per sequence for the query ``q``.
+
+    q      [B][Tq][Hq][D] (or [B][Hq][D]) bf16/fp32, contiguous
+    k_vis  [B][N][Hkv][D] same dtype, token rows contiguous
+    returns idx int32 [B][k] ascending (and fp32 scores [B][N] if ``scores``)
+    """
+    lib = load()
+    if q.dim() == 3:
+        q = q.unsqueeze(1)
+    dev = _on_gpu(q, k_vis)
+    if q.dtype != k_vis.dtype:
+        raise TypeError("q and k_vis must share a dtype")
+    q = q.contiguous()
+    B, Tq, Hq, D = q.shape
+    _, N, Hkv, Dk = k_vis.shape
+    if Dk != D or k_vis.shape[0] != B:
+        raise ValueError("q and k_vis shapes disagree")
+    bs, ts = _cache_strides(k_vis, "k_vis")
+    idx = out if out is not None else torch.empty((B, max(k, 0)), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, N), dtype=torch.float32, device=dev) if scores else None
+    ws = _workspace(retrieve_workspace_bytes(B, N, k), dev, workspace)
+    _check(lib.sv_retrieve(q.data_ptr(), B, Tq, Hq, k_vis.data_ptr(), bs, ts, N, Hkv, D,
+                           _dtype(q), k, idx.data_ptr(), sc.data_ptr() if sc is not None else None,
+                           ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev)))
+    return (idx, sc) if scores else idx
+
+
+def sparse_decode_attn_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, k: int, Tmax: int) -> int:
+    return int(load().sv_sparse_decode_attn_workspace(B, Hq, Hkv, D, k, Tmax))
+
+
+def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor,
+                       idx: torch.Tensor, k_txt: Optional[torch.Tensor],
+                       v_txt: Optional[torch.Tensor], txt_len: Optional[torch.Tensor],
+                       scale: Optional[float] = None, *,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention of the current token over the selected visual entries plus the text entries.
+
+    q        [B][Hq][D] (or [B][1][Hq][D])
+    k_vis, v_vis  [B][N][Hkv][D] (same strides)
+    idx      int32 [B][k]
+    k_txt, v_txt  [B][Tmax][Hkv][D] (same strides) or None
+    txt_len  int32 [B] on the device (rows attended), or None when there is no text
+    returns fp32 [B][Hq][D]
+    """
+    lib = load()
+    if q.dim() == 4:
+        q = q[:, 0]
+    dev = _on_gpu(q, k_vis, v_vis, idx, k_txt, v_txt, txt_len)
+    q = q.contiguous()
+    B, Hq, D = q.shape
+    _, N, Hkv, _ = k_vis.shape
+    if k_vis.stride() != v_vis.stride() or k_vis.shape != v_vis.shape:
+        raise ValueError("k_vis and v_vis must share shape and strides")
+    vbs, vts = _cache_strides(k_vis, "k_vis")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    idx = idx.contiguous()
+    k = idx.shape[1]
+    if k_txt is not None:
+        if k_txt.stride() != v_txt.stride() or k_txt.shape != v_txt.shape:
+            raise ValueError("k_txt and v_txt must share shape and strides")
+        tbs, tts = _cache_strides(k_txt, "k_txt")
+        Tmax = k_txt.shape[1]
+        if txt_len is None or txt_len.dtype != torch.int32:
+            raise TypeError("txt_len must be an int32 device tensor")
+        txt_len = txt_len.contiguous()
+    else:
+        tbs = tts = Tmax = 0
+    res = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = _workspace(sparse_decode_attn_workspace_bytes(B, Hq, Hkv, D, k, Tmax), dev, workspace)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.sv_sparse_decode_attn(
+        q.data_ptr(), B, Hq, k_vis.data_ptr(), v_vis.data_ptr(), vbs, vts, N, Hkv, D,
+        idx.data_ptr(), k, ptr(k_txt), ptr(v_txt), tbs, tts, ptr(txt_len) if Tmax else None, Tmax,
+        _dtype(q), float(scale) if scale else 0.0, res.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(dev)))
+    return res
+
+
+def salience_prune_workspace_bytes(F: int, H: int, N: int) -> int:
+    return int(load().sv_salience_prune_workspace(F, H, N))
+
+
+def salience_prune(vis_q: torch.Tensor, vis_k: torch.Tensor, keep: int,
+                   scale: Optional[float] = None, *, workspace: Optional[torch.Tensor] = None,
+                   salience_out: Optional[torch.Tensor] = None,
+                   idx_out: Optional[torch.Tensor] = None):
+    """Column-mean salience per token and the ``keep`` most salient tokens per frame.
+
+    vis_q, vis_k  [F][H][N][D] bf16, contiguous
+    returns (salience fp32 [F][N], idx int32 [F][keep] ascending)
+    """
+    lib = load()
+    dev = _on_gpu(vis_q, vis_k)
+    if vis_q.shape != vis_k.shape or vis_q.dim() != 4:
+        raise ValueError("vis_q and vis_k must both be [F][H][N][D]")
+    vis_q, vis_k = vis_q.contiguous(), vis_k.contiguous()
+    F, H, N, D = vis_q.shape
+    sal = salience_out if salience_out is not None else torch.empty((F, N), dtype=torch.float32, device=dev)
+    idx = idx_out if idx_out is not None else torch.empty((F, max(keep, 0)), dtype=torch.int32, device=dev)
+    ws = _workspace(salience_prune_workspace_bytes(F, H, N), dev, workspace)
+    _check(lib.sv_salience_prune(vis_q.data_ptr(), vis_k.data_ptr(), F, H, N, D, _dtype(vis_q),
+                                 float(scale) if scale else 0.0, keep, sal.data_ptr(),
+                                 idx.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(dev)))
+    return sal, idx

@@ -1,0 +1,175 @@
+// C ABI of libsv (declared in include/sv.h): argument validation, workspace
+// carving and kernel launches.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "sv.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sv_status fail(sv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+sv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SV_OK;
+  return fail(SV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int vec_elems(sv_dtype dt) { return dt == SV_BF16 ? 8 : 4; }
+
+bool dtype_ok(sv_dtype dt) { return dt == SV_BF16 || dt == SV_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int sv_version(void) { return 100; }
+
+const char* sv_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------- retrieval
+size_t sv_retrieve_workspace(int B, int N, int k) {
+  (void)k;
+  if (B < 1 || N < 1) return 256;
+  return align256((size_t)B * (size_t)N * sizeof(float));
+}
+
+sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, int64_t k_bstride,
+                      int64_t k_tstride, int N, int Hkv, int D, sv_dtype dtype, int k,
+                      int32_t* idx_out, float* scores_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!q || !k_vis || !workspace) return fail(SV_EINVAL, "sv_retrieve: NULL q, k_vis or workspace");
+  if (B < 1 || B > 65535 || Tq < 1 || Hq < 1 || Hkv < 1 || N < 1)
+    return fail(SV_EINVAL, "sv_retrieve: bad sizes B=%d Tq=%d Hq=%d Hkv=%d N=%d", B, Tq, Hq, Hkv, N);
+  if (k < 0 || k > N) return fail(SV_EINVAL, "sv_retrieve: k=%d outside [0, N=%d]", k, N);
+  if (k > 0 && !idx_out) return fail(SV_EINVAL, "sv_retrieve: NULL idx_out");
+  if (Hq % Hkv) return fail(SV_EINVAL, "sv_retrieve: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (!dtype_ok(dtype)) return fail(SV_EUNSUPPORTED, "sv_retrieve: dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(SV_EUNSUPPORTED, "sv_retrieve: D=%d (64 or 128)", D);
+  if (Hq / Hkv > 64) return fail(SV_EUNSUPPORTED, "sv_retrieve: group size %d > 64", Hq / Hkv);
+  const int64_t R = (int64_t)Hkv * D;
+  if (R > (dtype == SV_BF16 ? 8192 : 4096))
+    return fail(SV_EUNSUPPORTED, "sv_retrieve: row Hkv*D=%lld too long", (long long)R);
+  const int ve = vec_elems(dtype);
+  if (k_tstride < R || k_bstride < 0 || k_tstride % ve || k_bstride % ve)
+    return fail(SV_EINVAL, "sv_retrieve: strides (%lld, %lld) must be >= row and multiples of %d",
+                (long long)k_bstride, (long long)k_tstride, ve);
+  if (!aligned16(q) || !aligned16(k_vis))
+    return fail(SV_EINVAL, "sv_retrieve: q and k_vis must be 16-byte aligned");
+  if (workspace_bytes < sv_retrieve_workspace(B, N, k))
+    return fail(SV_EWORKSPACE, "sv_retrieve: workspace %zu < %zu bytes", workspace_bytes,
+                sv_retrieve_workspace(B, N, k));
+  hipStream_t st = (hipStream_t)stream;
+  float* scores = scores_out ? scores_out : (float*)workspace;
+  sv_status s = hip_status(
+      sv::launch_scan(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D, (int)dtype, scores, st),
+      "sv_retrieve scan");
+  if (s != SV_OK) return s;
+  return hip_status(sv::launch_topk_rows(scores, B, N, N, k, idx_out, st), "sv_retrieve select");
+}
+
+// ---------------------------------------------------------------- attention
+size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || k < 0 || Tmax < 0) return 256;
+  size_t best = 0;
+  for (int dt = 0; dt < 2; ++dt) {
+    const int C = sv::attn_splits(B, Hkv, D, dt, k, Tmax, nullptr);
+    const size_t bytes = (size_t)B * Hq * C * (D + 2) * sizeof(float);
+    if (bytes > best) best = bytes;
+  }
+  return align256(best);
+}
+
+sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
+                                int64_t vis_bstride, int64_t vis_tstride, int N, int Hkv, int D,
+                                const int32_t* idx, int k, const void* k_txt, const void* v_txt,
+                                int64_t txt_bstride, int64_t txt_tstride, const int32_t* txt_len,
+                                int Tmax, sv_dtype dtype, float scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !out || !workspace) return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL q, out or workspace");
+  if (B < 1 || B > 65535 || Hq < 1 || Hkv < 1 || N < 0 || k < 0 || Tmax < 0)
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: bad sizes B=%d Hq=%d Hkv=%d N=%d k=%d Tmax=%d",
+                B, Hq, Hkv, N, k, Tmax);
+  if (k > N) return fail(SV_EINVAL, "sv_sparse_decode_attn: k=%d > N=%d", k, N);
+  if (k + Tmax == 0) return fail(SV_EINVAL, "sv_sparse_decode_attn: nothing to attend (k + Tmax == 0)");
+  if (k > 0 && (!k_vis || !v_vis || !idx))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL k_vis, v_vis or idx");
+  if (Tmax > 0 && (!k_txt || !v_txt || !txt_len))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL k_txt, v_txt or txt_len");
+  if (Hq % Hkv) return fail(SV_EINVAL, "sv_sparse_decode_attn: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (!dtype_ok(dtype)) return fail(SV_EUNSUPPORTED, "sv_sparse_decode_attn: dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(SV_EUNSUPPORTED, "sv_sparse_decode_attn: D=%d (64 or 128)", D);
+  if (Hq / Hkv > 8) return fail(SV_EUNSUPPORTED, "sv_sparse_decode_attn: group size %d > 8", Hq / Hkv);
+  const int ve = vec_elems(dtype);
+  const int64_t R = (int64_t)Hkv * D;
+  if (k > 0 && (vis_tstride < R || vis_bstride < 0 || vis_tstride % ve || vis_bstride % ve))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: visual strides must be >= row and multiples of %d", ve);
+  if (Tmax > 0 && (txt_tstride < R || txt_bstride < 0 || txt_tstride % ve || txt_bstride % ve))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: text strides must be >= row and multiples of %d", ve);
+  if (!aligned16(q) || (k > 0 && (!aligned16(k_vis) || !aligned16(v_vis))) ||
+      (Tmax > 0 && (!aligned16(k_txt) || !aligned16(v_txt))))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: q and caches must be 16-byte aligned");
+  const size_t need = sv_sparse_decode_attn_workspace(B, Hq, Hkv, D, k, Tmax);
+  if (workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "sv_sparse_decode_attn: workspace %zu < %zu bytes", workspace_bytes, need);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  return hip_status(sv::launch_attn(q, B, Hq, k_vis, v_vis, vis_bstride, vis_tstride, N, Hkv, D, idx,
+                                    k, k_txt, v_txt, txt_bstride, txt_tstride, txt_len, Tmax,
+                                    (int)dtype, sc, out, (float*)workspace, (hipStream_t)stream),
+                    "sv_sparse_decode_attn");
+}
+
+// ---------------------------------------------------------------- salience
+size_t sv_salience_prune_workspace(int F, int H, int N) {
+  if (F < 1 || H < 1 || N < 1) return 256;
+  return align256((size_t)F * H * N * sizeof(float)) + align256((size_t)F * N * sizeof(float));
+}
+
+sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, int N, int D,
+                            sv_dtype dtype, float scale, int keep, float* salience_out,
+                            int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!vis_q || !vis_k || !workspace) return fail(SV_EINVAL, "sv_salience_prune: NULL q, k or workspace");
+  if (F < 1 || H < 1 || N < 1 || D < 1)
+    return fail(SV_EINVAL, "sv_salience_prune: bad sizes F=%d H=%d N=%d D=%d", F, H, N, D);
+  if ((int64_t)F * H > 2147483647LL) return fail(SV_EINVAL, "sv_salience_prune: F*H too large");
+  if (keep < 0 || keep > N) return fail(SV_EINVAL, "sv_salience_prune: keep=%d outside [0, N=%d]", keep, N);
+  if (keep > 0 && !idx_out) return fail(SV_EINVAL, "sv_salience_prune: NULL idx_out");
+  if (dtype != SV_BF16) return fail(SV_EUNSUPPORTED, "sv_salience_prune: only SV_BF16");
+  if (!sv::salience_supported(N, D))
+    return fail(SV_EUNSUPPORTED, "sv_salience_prune: N=%d, D=%d outside the on-chip kernel", N, D);
+  if (!aligned16(vis_q) || !aligned16(vis_k))
+    return fail(SV_EINVAL, "sv_salience_prune: q and k must be 16-byte aligned");
+  const size_t need = sv_salience_prune_workspace(F, H, N);
+  if (workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "sv_salience_prune: workspace %zu < %zu bytes", workspace_bytes, need);
+  float* colsum = (float*)workspace;
+  float* sal = salience_out ? salience_out
+                            : (float*)((char*)workspace + align256((size_t)F * H * N * sizeof(float)));
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  hipStream_t st = (hipStream_t)stream;
+  sv_status s = hip_status(sv::launch_salience(vis_q, vis_k, F, H, N, D, sc, colsum, sal, st),
+                           "sv_salience_prune salience");
+  if (s != SV_OK) return s;
+  return hip_status(sv::launch_topk_rows(sal, F, N, N, keep, idx_out, st), "sv_salience_prune select");
+}
+
+}  // extern "C"
