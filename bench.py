@@ -1,0 +1,303 @@
+"""Throughput of the SparseVILA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode step of the whole batch through every layer: for each
+layer, query-aware retrieval (relevance scan + top-k select) followed by
+sparse decode attention over the selected visual entries plus the text
+entries (split-K partials + combine).  The default workload is LLaVA-NeXT-7B
+shaped: 8 sequences, 32 layers x 32 heads, head dim 128, bf16, 1440 retained
+visual tokens, k = 360, 256 text entries.  All caches are resident in HBM
+before timing starts (7.1 GB, far above the 256 MB Infinity Cache, so every
+step streams from HBM).  The step's launches are captured once in a HIP
+graph and replayed.
+
+Printed: one JSON line with steps/s (whole job), algorithmic HBM GB/s, the
+roofline of the dominant kernel (the relevance scan, timed live with HIP
+events on the stream it runs on), the prefill salience workload (256 frames
+x 729 tokens, 16 heads, D = 72: tokens/s and MFMA utilisation), and the CPU
+oracle timed on a bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llava_next_7b")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--no-salience", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one step, and of one relevance-scan launch (one layer)."""
+    e = 2 if w.dtype.itemsize == 2 else 4
+    row = w.Hkv * w.D * e
+    q = w.Hq * w.D * e
+    scan = w.N * row + q + w.N * 4                       # keys once, query, fp32 scores out
+    select = w.N * 4 + w.k * 4                            # scores in, indices out
+    attn = (w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4   # K,V of the attended rows
+    per_seq_layer = scan + select + attn
+    return per_seq_layer * w.B * w.L, scan * w.B
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "visual_token_sparsity_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_key, src_hash, launches_per_unit=1):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def gpu_time(fn, reps, stream):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def capture(fn, stream):
+    """Capture fn's launches (on ``stream``) into a HIP graph; returns the graph or None."""
+    import torch
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+    except Exception as e:  # capture unsupported: fall back to eager launches
+        print(f"[bench] graph capture failed ({e}); timing eager launches", file=sys.stderr, flush=True)
+        return None
+
+
+def cpu_info():
+    n = len(os.sched_getaffinity(0))
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.load()
+    w = synthetic.DECODE[a.workload]
+    print(f"[bench] workload {w.name}: B={w.B} L={w.L} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} "
+          f"k={w.k} T={w.T}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ inputs (resident in HBM)
+    layers = [synthetic.make_decode_layer(w, a.seed, layer=l, device=dev, gen_device="cuda")
+              for l in range(w.L)]
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in range(w.L)]
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(w.L)]
+    scores = [torch.empty((w.B, w.N), dtype=torch.float32, device=dev) for _ in range(w.L)]
+    ws_r = torch.empty(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax),
+                       dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for l, d in enumerate(layers):
+            sv.retrieve(d["q"], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
+            sv.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
+                                  d["txt_len"], workspace=ws_a, out=out[l])
+
+    def scan_only():
+        for l, d in enumerate(layers):
+            # k = 0: the scan kernel alone, scores written to scores[l]
+            sv.load().sv_retrieve(d["q"].data_ptr(), w.B, 1, w.Hq, d["k_vis"].data_ptr(),
+                                  d["k_vis"].stride(0), d["k_vis"].stride(1), w.N, w.Hkv, w.D,
+                                  sv.SV_BF16 if w.dtype == torch.bfloat16 else sv.SV_F32, 0, None,
+                                  scores[l].data_ptr(), ws_r.data_ptr(), ws_r.numel(),
+                                  torch.cuda.current_stream().cuda_stream)
+
+    stream = torch.cuda.Stream(device=dev)      # default priority
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, a.warmup)):
+            step()
+        torch.cuda.synchronize()
+        g_step = None if a.no_graph else capture(step, stream)
+        g_scan = None if a.no_graph else capture(scan_only, stream)
+        run_step = g_step.replay if g_step is not None else step
+        run_scan = g_scan.replay if g_scan is not None else scan_only
+        for _ in range(a.warmup):
+            run_step()
+        # ---------------------------------------------------- timed region: exactly K steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        secs = gpu_time(run_step, a.steps, stream)
+        wall = time.perf_counter() - t0
+        # ---------------------------------------------------- dominant kernel: relevance scan
+        for _ in range(3):
+            run_scan()
+        scan_reps = max(5, a.steps // 2)
+        scan_secs = gpu_time(run_scan, scan_reps, stream)
+    scan_avg = scan_secs / (scan_reps * w.L)
+
+    step_bytes, scan_launch_bytes = decode_bytes(w)
+    steps_per_s = a.steps / secs
+    gbs = step_bytes * steps_per_s / 1e9
+    scan_gbs = scan_launch_bytes / scan_avg / 1e9
+    traffic = committed_traffic(f"scan_{w.name}", source_hash("retrieve.hip", "common.h"))
+
+    dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    res = {
+        "metric": "decode steps/s (retrieval + sparse attention, all layers, whole batch)",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(secs / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded Gaussian caches, 5% planted relevant tokens; no weights)",
+        "config": {"workload": w.name, "batch": w.B, "layers": w.L, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "visual_tokens": w.N, "k": w.k,
+                   "text_tokens": w.T, "launch": "hipgraph" if g_step is not None else "eager",
+                   "parallelism": "none (1 GPU)"},
+        "hbm_gbs_algorithmic": round(gbs, 1),
+        "hbm_frac_algorithmic": round(gbs / HBM_PEAK_GBS, 4),
+        "step_bytes_algorithmic": step_bytes,
+        "roofline": {"kernel": "scan_kernel (relevance scan, one layer x batch per launch)",
+                     "bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": scan_launch_bytes,
+                     "avg_launch_us": round(scan_avg * 1e6, 3)},
+        "wall_s_timed": round(wall, 4),
+    }
+
+    # ------------------------------------------------------------ prefill salience
+    if not a.no_salience:
+        res["salience"] = bench_salience(a, dev, stream)
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(a, w, layers)
+
+    print(json.dumps(res), flush=True)
+
+
+def bench_salience(a, dev, stream):
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+    sw = synthetic.SALIENCE["siglip_256f"]
+    Q, K = synthetic.make_salience(sw, a.seed, device=dev, gen_device="cuda")
+    sal = torch.empty((sw.F, sw.N), dtype=torch.float32, device=dev)
+    keep = torch.empty((sw.F, sw.keep), dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.salience_prune_workspace_bytes(sw.F, sw.H, sw.N), dtype=torch.uint8, device=dev)
+
+    def once():
+        sv.salience_prune(Q, K, sw.keep, workspace=ws, salience_out=sal, idx_out=keep)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            once()
+        g = None if a.no_graph else capture(once, stream)
+        run = g.replay if g is not None else once
+        reps = max(5, a.steps // 4)
+        secs = gpu_time(run, reps, stream) / reps
+    flops = synthetic.flop_count_salience(sw)
+    tflops = flops / secs / 1e12
+    return {"workload": sw.name, "frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
+            "head_dim": sw.D, "keep": sw.keep, "ms_per_call": round(secs * 1e3, 4),
+            "tokens_per_s": round(sw.F * sw.N / secs, 1),
+            "roofline": {"kernel": "salience_colsum_kernel + mean + top-k (whole call)",
+                         "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "flops_algorithmic": flops}}
+
+
+def cpu_baseline(a, w, layers):
+    """The fp64 oracle on the host, over as many whole layers as fit the time budget."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    ncores, model = cpu_info()
+    done, spent = 0, 0.0
+    for d in layers:
+        host = {k: v.cpu() for k, v in d.items()}
+        t0 = time.perf_counter()
+        idx = oracle.retrieve(host["q"], host["k_vis"], w.k)
+        oracle.sparse_decode_attn(host["q"], host["k_vis"], host["v_vis"], idx, host["k_txt"],
+                                  host["v_txt"], host["txt_len"])
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= a.cpu_seconds:
+            break
+    steps_per_s = done / w.L / spent
+    return {"value": round(steps_per_s, 5), "unit": "steps/s", "cores": threads,
+            "host_cores_visible": ncores, "cpu_model": model, "kind": "oracle",
+            "sample": f"{done} of {w.L} layers x {w.B} sequences (retrieve + sparse attention, "
+                      f"fp64 NumPy), {spent:.1f} s, scaled to whole steps"}
+
+
+if __name__ == "__main__":
+    main()
