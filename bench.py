@@ -150,9 +150,8 @@ def main():
     idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in range(w.L)]
     out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(w.L)]
     scores = [torch.empty((w.B, w.N), dtype=torch.float32, device=dev) for _ in range(w.L)]
-    ws_r = torch.empty(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dtype=torch.uint8, device=dev)
-    ws_a = torch.empty(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax),
-                       dtype=torch.uint8, device=dev)
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
+    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
     torch.cuda.synchronize()
 
     def step():
@@ -248,7 +247,7 @@ def bench_salience(a, dev, stream):
     Q, K = synthetic.make_salience(sw, a.seed, device=dev, gen_device="cuda")
     sal = torch.empty((sw.F, sw.N), dtype=torch.float32, device=dev)
     keep = torch.empty((sw.F, sw.keep), dtype=torch.int32, device=dev)
-    ws = torch.empty(sv.salience_prune_workspace_bytes(sw.F, sw.H, sw.N), dtype=torch.uint8, device=dev)
+    ws = sv.new_workspace(sv.salience_prune_workspace_bytes(sw.F, sw.H, sw.N), dev)
 
     def once():
         sv.salience_prune(Q, K, sw.keep, workspace=ws, salience_out=sal, idx_out=keep)

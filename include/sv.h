@@ -81,7 +81,11 @@ const char* sv_last_error(void);
  *  idx_out    [B][k] int32, ascending, distinct, each in [0, N).
  *  scores_out optional [B][N] fp32 scores s (NULL to skip).
  *  workspace  at least sv_retrieve_workspace(B, N, k) bytes, 256-byte
- *             aligned; contents on entry are ignored.
+ *             aligned, ZERO-FILLED before its first use.  It holds the
+ *             scores and one completion counter per sequence; every call
+ *             returns the counters to zero, so the same workspace can be
+ *             reused (and a call can be captured in a HIP graph) without
+ *             clearing it again.
  * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hkv*D <= 8192 (bf16)
  * or <= 4096 (fp32); Hq % Hkv == 0; Hq/Hkv <= 64; B <= 65535.
  * Errors: SV_EINVAL (k > N, k < 0, N < 1, B < 1, Tq < 1, Hq % Hkv != 0,
@@ -123,7 +127,10 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq,
  *  scale      softmax scale; <= 0 selects 1/sqrt(D).
  *  out        [B][Hq][D] fp32.
  *  workspace  at least sv_sparse_decode_attn_workspace(B, Hq, Hkv, D, k, Tmax)
- *             bytes, 256-byte aligned.
+ *             bytes, 256-byte aligned, ZERO-FILLED before its first use.  It
+ *             holds the split partials and one completion counter per
+ *             (sequence, KV head); every call returns the counters to zero,
+ *             so the workspace can be reused without clearing.
  * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hq/Hkv in 1..8.
  * Errors: SV_EINVAL (k < 0, k + Tmax == 0, k > N, Hq % Hkv != 0, NULL
  * required pointer, B < 1), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.

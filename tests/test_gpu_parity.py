@@ -240,3 +240,73 @@ def test_salience_explicit_scale_and_rerun():
     assert torch.equal(a, b) and torch.equal(ia, ib)
     ok, rel, sm = accept.check_salience(a.cpu().numpy(), s_ref)
     assert ok, (rel, sm)
+
+
+# ---------------------------------------------------------------- workspaces and graphs
+def test_workspace_reuse_leaves_counters_zero():
+    """One zero-filled workspace serves many calls; the completion counters return to zero."""
+    w = synthetic.scaled_decode(synthetic.DECODE["qwen2_7b_video"], N=5000, k=300, T=40, Tmax=64)
+    _say("workspace reuse", w)
+    d = synthetic.make_decode_layer(w, seed=8)
+    g = _to(d)
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), DEV)
+    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), DEV)
+    outs = []
+    for _ in range(3):
+        idx = sv.retrieve(g["q"], g["k_vis"], w.k, workspace=ws_r)
+        out = sv.sparse_decode_attn(g["q"], g["k_vis"], g["v_vis"], idx, g["k_txt"], g["v_txt"],
+                                    g["txt_len"], workspace=ws_a)
+        outs.append((idx.clone(), out.clone()))
+    torch.cuda.synchronize()
+    for idx, out in outs[1:]:
+        assert torch.equal(idx, outs[0][0]) and torch.equal(out, outs[0][1])
+    # counters live after the scores / partials, 256-byte aligned
+    n_scores = ((w.B * w.N * 4 + 255) // 256) * 256
+    assert torch.count_nonzero(ws_r[n_scores:n_scores + 4 * w.B]) == 0
+    tail = ws_a[-((w.B * w.Hkv * 4 + 255) // 256) * 256:]
+    assert torch.count_nonzero(tail) == 0
+    s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])
+    ok, _, msgs = accept.check_index_sets(outs[0][0].cpu().numpy(), s_ref, w.k)
+    assert ok, msgs[:3]
+
+
+def test_decode_step_graph_replays_match_eager():
+    """A captured two-layer decode step, replayed with eager work in between, matches eager runs."""
+    w = synthetic.scaled_decode(synthetic.DECODE["llava_next_7b"], B=3, L=2)
+    _say("graph replay", w)
+    layers = [_to(synthetic.make_decode_layer(w, seed=9, layer=l)) for l in range(w.L)]
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), DEV)
+    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), DEV)
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=DEV) for _ in layers]
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV) for _ in layers]
+
+    def step():
+        for l, d in enumerate(layers):
+            sv.retrieve(d["q"], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
+            sv.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
+                                  d["txt_len"], workspace=ws_a, out=out[l])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    ref_idx = [t.clone() for t in idx]
+    ref_out = [t.clone() for t in out]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    for rep in range(4):
+        for t in idx + out:
+            t.fill_(-7)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(w.L):
+            assert torch.equal(idx[l], ref_idx[l]), (rep, l)
+            assert torch.equal(out[l], ref_out[l]), (rep, l)
+    for l, d in enumerate(layers):
+        host = {k: v.cpu() for k, v in d.items()}
+        ref = oracle.sparse_decode_attn(host["q"], host["k_vis"], host["v_vis"], ref_idx[l].cpu().numpy(),
+                                        host["k_txt"], host["v_txt"], host["txt_len"])
+        ok, err = accept.check_attention(ref_out[l].cpu().numpy(), ref)
+        assert ok, err

@@ -22,7 +22,7 @@ import torch  # loaded first so libsv binds to torch's HIP runtime
 __all__ = [
     "SvError", "lib_path", "load", "retrieve", "retrieve_workspace_bytes",
     "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
-    "salience_prune_workspace_bytes", "SV_F32", "SV_BF16",
+    "salience_prune_workspace_bytes", "new_workspace", "SV_F32", "SV_BF16",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -113,11 +113,21 @@ def _cache_strides(t: torch.Tensor, name: str) -> Tuple[int, int]:
 
 
 def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace, or a fresh zero-filled one.
+
+    Workspaces must be zero-filled before their first use; each call leaves
+    its completion counters at zero, so a workspace can be reused as is.
+    """
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of ``nbytes`` bytes, reusable across calls."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def retrieve_workspace_bytes(B: int, N: int, k: int) -> int:

@@ -46,10 +46,13 @@ int sv_version(void) { return 100; }
 const char* sv_last_error(void) { return g_err.c_str(); }
 
 // ---------------------------------------------------------------- retrieval
+// Workspace of sv_retrieve: [scores B*N fp32][counters B uint32].
+static size_t retrieve_scores_bytes(int B, int N) { return align256((size_t)B * (size_t)N * sizeof(float)); }
+
 size_t sv_retrieve_workspace(int B, int N, int k) {
   (void)k;
   if (B < 1 || N < 1) return 256;
-  return align256((size_t)B * (size_t)N * sizeof(float));
+  return retrieve_scores_bytes(B, N) + align256((size_t)B * sizeof(uint32_t));
 }
 
 sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, int64_t k_bstride,
@@ -77,18 +80,17 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
   if (workspace_bytes < sv_retrieve_workspace(B, N, k))
     return fail(SV_EWORKSPACE, "sv_retrieve: workspace %zu < %zu bytes", workspace_bytes,
                 sv_retrieve_workspace(B, N, k));
-  hipStream_t st = (hipStream_t)stream;
   float* scores = scores_out ? scores_out : (float*)workspace;
-  sv_status s = hip_status(
-      sv::launch_scan(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D, (int)dtype, scores, st),
-      "sv_retrieve scan");
-  if (s != SV_OK) return s;
-  return hip_status(sv::launch_topk_rows(scores, B, N, N, k, idx_out, st), "sv_retrieve select");
+  uint32_t* counters = (uint32_t*)((char*)workspace + retrieve_scores_bytes(B, N));
+  return hip_status(sv::launch_retrieve(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D,
+                                        (int)dtype, scores, k, idx_out, counters,
+                                        (hipStream_t)stream),
+                    "sv_retrieve");
 }
 
 // ---------------------------------------------------------------- attention
-size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || k < 0 || Tmax < 0) return 256;
+// Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+2) fp32][counters B*Hkv uint32].
+static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax) {
   size_t best = 0;
   for (int dt = 0; dt < 2; ++dt) {
     const int C = sv::attn_splits(B, Hkv, D, dt, k, Tmax, nullptr);
@@ -96,6 +98,11 @@ size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int
     if (bytes > best) best = bytes;
   }
   return align256(best);
+}
+
+size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || k < 0 || Tmax < 0) return 256;
+  return attn_partial_bytes(B, Hq, Hkv, D, k, Tmax) + align256((size_t)B * Hkv * sizeof(uint32_t));
 }
 
 sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
@@ -131,9 +138,12 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
   if (workspace_bytes < need)
     return fail(SV_EWORKSPACE, "sv_sparse_decode_attn: workspace %zu < %zu bytes", workspace_bytes, need);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  uint32_t* counters =
+      (uint32_t*)((char*)workspace + attn_partial_bytes(B, Hq, Hkv, D, k, Tmax));
   return hip_status(sv::launch_attn(q, B, Hq, k_vis, v_vis, vis_bstride, vis_tstride, N, Hkv, D, idx,
                                     k, k_txt, v_txt, txt_bstride, txt_tstride, txt_len, Tmax,
-                                    (int)dtype, sc, out, (float*)workspace, (hipStream_t)stream),
+                                    (int)dtype, sc, out, (float*)workspace, counters,
+                                    (hipStream_t)stream),
                     "sv_sparse_decode_attn");
 }
 

@@ -5,31 +5,35 @@
 // (decoding attention kernel): decode is memory-bound, so the win comes from
 // reading fewer KV bytes.
 //
-// Split-K flash-decode.  Workgroup (c, g, b) takes entries [c*SE, (c+1)*SE) of
-// the attended list E = idx[b][0..k) ++ text rows [0, txt_len[b]) and computes,
-// for the G query heads of KV head g, a partial (m, l, acc) with an online
-// softmax in base 2 (the query is pre-scaled by scale*log2(e)).  Each lane
-// group of LPE lanes owns one entry at a time and reads its K and V head rows
-// as 16-byte vectors straight from the cache (a gather: no packed copy is
-// made), so each selected row is read once per KV head.  The combine kernel
-// merges the C partials of each (b, h) by max-rescaling.
+// Split-K flash-decode, one kernel.  Workgroup (c, g, b) takes entries
+// [c*SE, (c+1)*SE) of the attended list E = idx[b][0..k) ++ text rows
+// [0, txt_len[b]) and computes, for the G query heads of KV head g, a partial
+// (m, l, acc) with the softmax in base 2 (the query is pre-scaled by
+// scale*log2(e)).  Each lane group of LPE lanes owns EPL entries and reads
+// their K and V head rows as 16-byte vectors straight from the cache (a
+// gather: no packed copy is made), all loads in flight before any math.  With
+// one split the workgroup normalises and writes the output; otherwise it
+// publishes its partial with device-coherent stores, waits for them and bumps
+// a counter for (b, g); the last workgroup reads the C partials with
+// device-coherent loads, merges them by max-rescaling, writes the output and
+// resets the counter to zero.
 #include "common.h"
 
 namespace sv {
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnEplMax = 4;  // entries per lane group per workgroup
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
+template <typename T, int D, int G, int EPL>
+__global__ __launch_bounds__(kAttnWaves* kWave) void attn_kernel(
     const T* __restrict__ q, int Hq, const T* __restrict__ kv, const T* __restrict__ vv,
     int64_t vbs, int64_t vts, int N, const int32_t* __restrict__ idx, int k,
     const T* __restrict__ kt, const T* __restrict__ vt, int64_t tbs, int64_t tts,
-    const int32_t* __restrict__ txt_len, int Tmax, float qscale, int epl, int C,
-    float* __restrict__ part) {
+    const int32_t* __restrict__ txt_len, int Tmax, float qscale, int C,
+    float* __restrict__ part, uint32_t* __restrict__ counters, float* __restrict__ out) {
   constexpr int VE = Vec<T>::kElems;
   constexpr int LPE = D / VE;        // lanes per entry row of one head
   constexpr int EPW = kWave / LPE;   // entries per wave per step
+  constexpr int SE = kAttnWaves * EPW * EPL;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -38,49 +42,55 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
   int tl = txt_len ? txt_len[b] : 0;
   tl = tl < 0 ? 0 : (tl > Tmax ? Tmax : tl);
   const int E = k + tl;
-  const int SE = kAttnWaves * EPW * epl;
   const int e_begin = c * SE;
+
+  // Entry -> cache row.  Visual indices outside [0, N) are skipped.
+  int tok[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = e_begin + (j * kAttnWaves + wave) * EPW + eg;
+    tok[j] = -1;
+    if (e < k) tok[j] = idx[(int64_t)b * k + e];
+  }
+  Vec<T> qx[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) qx[i].load(q + ((int64_t)b * Hq + g * G + i) * D + d0);
+
+  Vec<T> kx[EPL], vx[EPL];
+  bool ok[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = e_begin + (j * kAttnWaves + wave) * EPW + eg;
+    const T* kp = nullptr;
+    const T* vp = nullptr;
+    if (e < k) {
+      const int t = tok[j];
+      if (t >= 0 && t < N) {
+        const int64_t off = (int64_t)b * vbs + (int64_t)t * vts + (int64_t)g * D + d0;
+        kp = kv + off;
+        vp = vv + off;
+      }
+    } else if (e < E) {
+      const int64_t off = (int64_t)b * tbs + (int64_t)(e - k) * tts + (int64_t)g * D + d0;
+      kp = kt + off;
+      vp = vt + off;
+    }
+    ok[j] = kp != nullptr;
+    if (ok[j]) {
+      kx[j].load(kp);
+      vx[j].load(vp);
+    } else {
+      kx[j].zero();
+      vx[j].zero();
+    }
+  }
 
   float qv[G][VE];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    Vec<T> x;
-    x.load(q + ((int64_t)b * Hq + g * G + i) * D + d0);
-    x.to_f32(qv[i]);
+    qx[i].to_f32(qv[i]);
 #pragma unroll
     for (int v = 0; v < VE; ++v) qv[i][v] *= qscale;
-  }
-
-  // Issue every load of this lane group's entries first (K and V vectors).
-  Vec<T> kx[kAttnEplMax], vx[kAttnEplMax];
-  bool ok[kAttnEplMax];
-#pragma unroll
-  for (int j = 0; j < kAttnEplMax; ++j) {
-    ok[j] = false;
-    kx[j].zero();
-    vx[j].zero();
-    if (j < epl) {
-      const int e = e_begin + (j * kAttnWaves + wave) * EPW + eg;
-      const T* kp = nullptr;
-      const T* vp = nullptr;
-      if (e < k) {
-        const int t = idx[(int64_t)b * k + e];
-        if (t >= 0 && t < N) {
-          const int64_t off = (int64_t)b * vbs + (int64_t)t * vts + (int64_t)g * D + d0;
-          kp = kv + off;
-          vp = vv + off;
-        }
-      } else if (e < E) {
-        const int64_t off = (int64_t)b * tbs + (int64_t)(e - k) * tts + (int64_t)g * D + d0;
-        kp = kt + off;
-        vp = vt + off;
-      }
-      if (kp) {
-        ok[j] = true;
-        kx[j].load(kp);
-        vx[j].load(vp);
-      }
-    }
   }
 
   float m[G], l[G], acc[G][VE];
@@ -93,30 +103,28 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
   }
 
 #pragma unroll
-  for (int j = 0; j < kAttnEplMax; ++j) {
-    if (j < epl) {
-      float kf[VE], vf[VE];
-      kx[j].to_f32(kf);
-      vx[j].to_f32(vf);
-      float z[G];
+  for (int j = 0; j < EPL; ++j) {
+    float kf[VE], vf[VE];
+    kx[j].to_f32(kf);
+    vx[j].to_f32(vf);
+    float z[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
+      z[i] = group_sum<LPE>(s);
+    }
+    if (ok[j]) {
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        float s = 0.f;
+        const float mn = fmaxf(m[i], z[i]);
+        const float a = fast_exp2(m[i] - mn);  // m = -inf -> 0
+        const float p = fast_exp2(z[i] - mn);
+        l[i] = l[i] * a + p;
 #pragma unroll
-        for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
-        z[i] = group_sum<LPE>(s);
-      }
-      if (ok[j]) {
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-          const float mn = fmaxf(m[i], z[i]);
-          const float a = fast_exp2(m[i] - mn);  // m = -inf -> 0
-          const float p = fast_exp2(z[i] - mn);
-          l[i] = l[i] * a + p;
-#pragma unroll
-          for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * a);
-          m[i] = mn;
-        }
+        for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * a);
+        m[i] = mn;
       }
     }
   }
@@ -144,6 +152,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
   // Merge the waves through LDS.
   __shared__ float s_ml[kAttnWaves][G][2];
   __shared__ float s_acc[kAttnWaves][G][D];
+  __shared__ uint32_t s_last;
   if (eg == 0) {
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -156,6 +165,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
     }
   }
   __syncthreads();
+  const int64_t head0 = (int64_t)b * Hq + g * G;
   for (int t = threadIdx.x; t < G * D; t += kAttnWaves * kWave) {
     const int i = t / D, d = t % D;
     float mm = -INFINITY;
@@ -169,35 +179,46 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(
       ll += s_ml[w][i][1] * f;
       aa += s_acc[w][i][d] * f;
     }
-    float* pp = part + (((int64_t)b * Hq + g * G + i) * C + c) * (D + 2);
-    pp[d] = aa;
-    if (d == 0) {
-      pp[D] = mm;
-      pp[D + 1] = ll;
-    }
-  }
-}
-
-// out[b,h,d] = sum_c 2^(m_c - M) acc_c[d] / sum_c 2^(m_c - M) l_c
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int C,
-                                                           int D, float* __restrict__ out) {
-  const int bh = blockIdx.x;
-  const float* pp = part + (int64_t)bh * C * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < C; ++c) M = fmaxf(M, pp[c * (D + 2) + D]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int c = 0; c < C; ++c) {
-        const float mc = pp[c * (D + 2) + D];
-        if (mc == -INFINITY) continue;
-        const float f = fast_exp2(mc - M);
-        num = fmaf(f, pp[c * (D + 2) + d], num);
-        den = fmaf(f, pp[c * (D + 2) + D + 1], den);
+    if (C == 1) {
+      out[(head0 + i) * D + d] = ll > 0.f ? aa / ll : 0.f;
+    } else {
+      float* pp = part + ((head0 + i) * C + c) * (D + 2);
+      store_shared_dev(pp + d, aa);
+      if (d == 0) {
+        store_shared_dev(pp + D, mm);
+        store_shared_dev(pp + D + 1, ll);
       }
     }
-    out[(int64_t)bh * D + d] = den > 0.f ? num / den : 0.f;
   }
+  if (C == 1) return;
+
+  wait_stores_complete();
+  __syncthreads();
+  uint32_t* ctr = counters + (int64_t)b * gridDim.y + g;
+  if (threadIdx.x == 0) s_last = counter_add(ctr, 1u) == (uint32_t)C - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+
+  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c
+  for (int t = threadIdx.x; t < G * D; t += kAttnWaves * kWave) {
+    const int i = t / D, d = t % D;
+    const float* pp = part + (head0 + i) * C * (D + 2);
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, load_shared_dev(pp + cc * (D + 2) + D));
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int cc = 0; cc < C; ++cc) {
+        const float mc = load_shared_dev(pp + cc * (D + 2) + D);
+        const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+        num = fmaf(f, load_shared_dev(pp + cc * (D + 2) + d), num);
+        den = fmaf(f, load_shared_dev(pp + cc * (D + 2) + D + 1), den);
+      }
+    }
+    out[(head0 + i) * D + d] = den > 0.f ? num / den : 0.f;
+  }
+  if (threadIdx.x == 0) counter_reset(ctr);
 }
 
 static int entries_per_step(int D, int dtype) {
@@ -206,10 +227,11 @@ static int entries_per_step(int D, int dtype) {
 }
 
 int attn_splits(int B, int Hkv, int D, int dtype, int k, int Tmax, int* epl_out) {
-  const int Emax = k + Tmax;
+  const int Emax = k + Tmax > 0 ? k + Tmax : 1;
   const int step = entries_per_step(D, dtype);
-  // Smallest split that still gives every CU a few workgroups.
-  int epl = kAttnEplMax;
+  // Most entries per lane (fewest partials, deepest load queue) that still
+  // gives about four workgroups per CU.
+  int epl = 8;
   while (epl > 1) {
     const int se = step * epl;
     const long wgs = (long)((Emax + se - 1) / se) * Hkv * B;
@@ -221,33 +243,48 @@ int attn_splits(int B, int Hkv, int D, int dtype, int k, int Tmax, int* epl_out)
   return (Emax + se - 1) / se;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int EPL>
 static hipError_t attn_go(const void* q, int B, int Hq, const void* kv, const void* vv, int64_t vbs,
                           int64_t vts, int N, int Hkv, const int32_t* idx, int k, const void* kt,
                           const void* vt, int64_t tbs, int64_t tts, const int32_t* txt_len,
-                          int Tmax, int dtype, float qscale, float* out, float* part,
+                          int Tmax, float qscale, int C, float* out, float* part, uint32_t* ctr,
                           hipStream_t st) {
-  int epl = 1;
-  const int C = attn_splits(B, Hkv, D, dtype, k, Tmax, &epl);
-  hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), dim3(C, Hkv, B), dim3(kAttnWaves * kWave), 0,
-                     st, (const T*)q, Hq, (const T*)kv, (const T*)vv, vbs, vts, N, idx, k,
-                     (const T*)kt, (const T*)vt, tbs, tts, txt_len, Tmax, qscale, epl, C, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(D), 0, st, part, C, D, out);
+  hipLaunchKernelGGL((attn_kernel<T, D, G, EPL>), dim3(C, Hkv, B), dim3(kAttnWaves * kWave), 0, st,
+                     (const T*)q, Hq, (const T*)kv, (const T*)vv, vbs, vts, N, idx, k, (const T*)kt,
+                     (const T*)vt, tbs, tts, txt_len, Tmax, qscale, C, part, ctr, out);
   return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+static hipError_t attn_epl(int epl, const void* q, int B, int Hq, const void* kv, const void* vv,
+                           int64_t vbs, int64_t vts, int N, int Hkv, const int32_t* idx, int k,
+                           const void* kt, const void* vt, int64_t tbs, int64_t tts,
+                           const int32_t* txt_len, int Tmax, float qs, int C, float* out,
+                           float* part, uint32_t* ctr, hipStream_t st) {
+#define SV_EPL_CASE(E)                                                                          \
+  case E:                                                                                       \
+    return attn_go<T, D, G, E>(q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,    \
+                               txt_len, Tmax, qs, C, out, part, ctr, st);
+  switch (epl) {
+    SV_EPL_CASE(1)
+    SV_EPL_CASE(2)
+    SV_EPL_CASE(4)
+    SV_EPL_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SV_EPL_CASE
+}
+
 template <typename T, int D>
-static hipError_t attn_g(int G, const void* q, int B, int Hq, const void* kv, const void* vv,
-                         int64_t vbs, int64_t vts, int N, int Hkv, const int32_t* idx, int k,
-                         const void* kt, const void* vt, int64_t tbs, int64_t tts,
-                         const int32_t* txt_len, int Tmax, int dtype, float qs, float* out,
-                         float* part, hipStream_t st) {
+static hipError_t attn_g(int G, int epl, const void* q, int B, int Hq, const void* kv,
+                         const void* vv, int64_t vbs, int64_t vts, int N, int Hkv,
+                         const int32_t* idx, int k, const void* kt, const void* vt, int64_t tbs,
+                         int64_t tts, const int32_t* txt_len, int Tmax, float qs, int C,
+                         float* out, float* part, uint32_t* ctr, hipStream_t st) {
 #define SV_ATTN_CASE(GG)                                                                        \
   case GG:                                                                                      \
-    return attn_go<T, D, GG>(q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,      \
-                             txt_len, Tmax, dtype, qs, out, part, st);
+    return attn_epl<T, D, GG>(epl, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts, \
+                              txt_len, Tmax, qs, C, out, part, ctr, st);
   switch (G) {
     SV_ATTN_CASE(1)
     SV_ATTN_CASE(2)
@@ -266,21 +303,23 @@ hipError_t launch_attn(const void* q, int B, int Hq, const void* kv, const void*
                        int64_t vts, int N, int Hkv, int D, const int32_t* idx, int k,
                        const void* kt, const void* vt, int64_t tbs, int64_t tts,
                        const int32_t* txt_len, int Tmax, int dtype, float scale, float* out,
-                       float* part, hipStream_t st) {
+                       float* part, uint32_t* counters, hipStream_t st) {
   const int G = Hq / Hkv;
+  int epl = 1;
+  const int C = attn_splits(B, Hkv, D, dtype, k, Tmax, &epl);
   const float qs = scale * 1.4426950408889634f;  // log2(e): the softmax runs in base 2
   if (dtype == 1) {
     if (D == 128)
-      return attn_g<bf16_t, 128>(G, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
-                                 txt_len, Tmax, dtype, qs, out, part, st);
-    return attn_g<bf16_t, 64>(G, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
-                              txt_len, Tmax, dtype, qs, out, part, st);
+      return attn_g<bf16_t, 128>(G, epl, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs,
+                                 tts, txt_len, Tmax, qs, C, out, part, counters, st);
+    return attn_g<bf16_t, 64>(G, epl, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
+                              txt_len, Tmax, qs, C, out, part, counters, st);
   }
   if (D == 128)
-    return attn_g<float, 128>(G, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
-                              txt_len, Tmax, dtype, qs, out, part, st);
-  return attn_g<float, 64>(G, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
-                           txt_len, Tmax, dtype, qs, out, part, st);
+    return attn_g<float, 128>(G, epl, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
+                              txt_len, Tmax, qs, C, out, part, counters, st);
+  return attn_g<float, 64>(G, epl, q, B, Hq, kv, vv, vbs, vts, N, Hkv, idx, k, kt, vt, tbs, tts,
+                           txt_len, Tmax, qs, C, out, part, counters, st);
 }
 
 }  // namespace sv

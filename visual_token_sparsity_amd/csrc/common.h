@@ -78,11 +78,33 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- cross-workgroup hand-off
+// Each XCD has its own L2, and an agent-scope fence would write back or
+// invalidate a whole L2.  Data handed from one workgroup to another inside a
+// kernel therefore goes through agent-scope relaxed atomic stores and loads
+// (coherent at device scope, no cache maintenance); the writer waits for its
+// stores to complete (vmcnt = 0) before its workgroup bumps the counter.
+__device__ __forceinline__ void store_shared_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+}
+__device__ __forceinline__ uint32_t counter_add(uint32_t* c, uint32_t v) {
+  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void counter_reset(uint32_t* c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
-hipError_t launch_scan(const void* q, int B, int Tq, int Hq, const void* kv, int64_t bstride,
-                       int64_t tstride, int N, int Hkv, int D, int dtype, float* scores,
-                       hipStream_t stream);
+hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv, int64_t bstride,
+                           int64_t tstride, int N, int Hkv, int D, int dtype, float* scores, int k,
+                           int32_t* idx_out, uint32_t* counters, hipStream_t stream);
 
 hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int N, int k,
                             int32_t* out, hipStream_t stream);
@@ -93,7 +115,7 @@ hipError_t launch_attn(const void* q, int B, int Hq, const void* kv, const void*
                        int64_t vbs, int64_t vts, int N, int Hkv, int D, const int32_t* idx,
                        int k, const void* kt, const void* vt, int64_t tbs, int64_t tts,
                        const int32_t* txt_len, int Tmax, int dtype, float scale, float* out,
-                       float* partials, hipStream_t stream);
+                       float* partials, uint32_t* counters, hipStream_t stream);
 
 bool salience_supported(int N, int D);
 
