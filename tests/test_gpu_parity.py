@@ -310,3 +310,41 @@ def test_decode_step_graph_replays_match_eager():
                                         host["k_txt"], host["v_txt"], host["txt_len"])
         ok, err = accept.check_attention(ref_out[l].cpu().numpy(), ref)
         assert ok, err
+
+
+@pytest.mark.parametrize("mode", ["all_rows", "some_rows"])
+def test_salience_large_logits_use_exact_row_max(mode):
+    """Rows whose Cauchy-Schwarz shift could underflow take the exact-max path."""
+    w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=2, H=2)
+    Q, K = synthetic.make_salience(w, seed=11)
+    Q = Q.float()
+    if mode == "all_rows":
+        Q *= 12.0
+    else:
+        Q[:, :, 100:180] *= 12.0            # spans several 16-row blocks
+    Q = Q.to(torch.bfloat16)
+    K = (K.float() * 4.0).to(torch.bfloat16)
+    _say("salience large logits", mode)
+    s_ref = oracle.salience(Q, K)
+    sal, idx = sv.salience_prune(Q.to(DEV), K.to(DEV), w.keep)
+    torch.cuda.synchronize()
+    ok, rel, sm = accept.check_salience(sal.cpu().numpy(), s_ref)
+    assert ok, (rel, sm)
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.keep)
+    assert ok, msgs[:3]
+
+
+@pytest.mark.parametrize("D", [64, 72, 80, 96])
+@pytest.mark.parametrize("N", [32, 129, 729])
+def test_salience_head_dim_grid(D, N):
+    """Every head dim of the column-stationary kernel, with and without ragged tiles."""
+    w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=1, H=2, N=N, D=D, keep=N // 2)
+    _say("salience grid", N, D)
+    Q, K = synthetic.make_salience(w, seed=3)
+    s_ref = oracle.salience(Q, K)
+    sal, idx = sv.salience_prune(Q.to(DEV), K.to(DEV), w.keep)
+    torch.cuda.synchronize()
+    ok, rel, sm = accept.check_salience(sal.cpu().numpy(), s_ref)
+    assert ok, (rel, sm)
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.keep)
+    assert ok, msgs[:3]

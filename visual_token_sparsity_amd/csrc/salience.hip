@@ -183,6 +183,419 @@ __global__ __launch_bounds__(kSalWaves* kWave, 1) void salience_colsum_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------
+// Persistent column-stationary variant for the common head dims
+// (D in {64, 72, 80, 96}).
+//
+// One workgroup of 8 waves per CU loops over (frame, head) items.  Wave w
+// owns a fixed eighth of the key columns: its MFMA B fragments (TPW tiles of
+// 16 keys x ceil(D/32) 32-wide k-steps) stay in registers for
+// the whole item, so the inner loop reads no LDS.  Query rows stream from
+// global memory as A fragments, two 16-row blocks per iteration, loaded one
+// iteration ahead.  The keys of the next item are copied into an LDS staging
+// buffer with direct global->LDS loads while the current item is computed.
+// A head dim that is not a multiple of 32 gets one more 32-wide step whose
+// lanes beyond D feed zeros (one step shape for every D keeps the MFMA
+// accumulation chains uniform).
+//
+// Row shift.  Softmax is shift-invariant, so any shift >= the row max works.
+// The kernel uses the Cauchy-Schwarz bound c_i = |q_i| * max_j |k_j| * scale
+// (in log2 units, times 1 + 2^-10 to cover rounding): every exponent is then
+// <= 0 without a max pass, and the waves only have to add their partial row
+// sums.  A row block whose bound exceeds 48 (the row maximum could sit below
+// 2^-96) uses the exact maximum of each wave's columns instead, and the
+// partial sums are then merged with max-rescaling.
+// ----------------------------------------------------------------------------
+constexpr int kColWaves = 8;  // waves per workgroup, each owning a column slice
+constexpr int kRowBlocks = 1;  // 16-row blocks per iteration
+
+__device__ __forceinline__ float sumsq8(const bf16x8& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fmaf((float)v[i], (float)v[i], s);
+  return s;
+}
+
+// Cross-lane steps inside a row of 16 lanes with DPP (VALU modifiers, no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Every lane gets the sum (or max) over its 16-lane row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
+template <int D, int TPW>
+__global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
+    const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
+    float* __restrict__ colsum) {
+  // 32-wide k-steps; lanes whose 8-element chunk lies beyond D feed zeros.
+  constexpr int KS = (D + 31) / 32;
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static_assert(D % 8 == 0, "D must be a multiple of 8");
+  constexpr int NT = kColWaves * kWave;
+  constexpr int CPW = TPW * 16;               // columns per wave
+  constexpr int Ncp = kColWaves * CPW;        // padded key rows in the staging buffer
+  constexpr int RPI = kRowBlocks * 16;        // query rows per iteration
+  extern __shared__ uint4 smem_u4[];
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem_u4);            // [Ncp][D] staged keys
+  float* xch = reinterpret_cast<float*>(sK + Ncp * D);        // [2][RPI][2][kColWaves]
+  float* qn2 = xch + 2 * RPI * 2 * kColWaves;                 // [Ncp] query-row norms |q_r|
+  uint32_t* maxu = reinterpret_cast<uint32_t*>(qn2 + Ncp);    // [2][2] max |k|^2, max |q|^2
+  uint32_t* arrived = maxu + 4;                                // partial-sum arrivals (bound loop)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const int c0 = wave * CPW;
+  const int RB = (N + 15) / 16;
+  const int iters = (RB + kRowBlocks - 1) / kRowBlocks;
+  const int kbytes = N * D * 2;
+
+  // Staging rows >= N stay zero for every item; so do their query norms.
+  for (int c = N * D / 8 + tid; c < Ncp * D / 8; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
+  if (tid < 5) maxu[tid] = 0u;  // key/query maxima of both parities, arrival counter
+  // Direct global->LDS copy of one item's keys (1 KB per wave instruction).
+  auto stage_keys = [&](int item) {
+    const char* src = reinterpret_cast<const char*>(Kg + (int64_t)item * N * D);
+    char* dst = reinterpret_cast<char*>(sK);
+    for (int chunk = wave; chunk * 1024 < kbytes; chunk += kColWaves) {
+      const int off = chunk * 1024 + lane * 16;
+      if (off < kbytes)
+        __builtin_amdgcn_global_load_lds(src + off, dst + chunk * 1024, 16, 0, 0);
+    }
+  };
+  // Unconditional loads (no exec-masked branch, so no early vmcnt wait).  A
+  // lane whose d-chunk lies beyond D may load any finite data because its key
+  // partner is zero; a row beyond N loads row N-1 and uses that row's shift, so
+  // its probabilities stay <= 1 and are dropped by a zero weight.
+  auto load_a_raw = [&](const bf16_t* q, int rb, bf16x8 (&af)[KS]) {
+    int row = rb * 16 + li;
+    row = row < N ? row : N - 1;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int dd = 32 * s + 8 * lg;
+      af[s] = load_bf16x8(q + (int64_t)row * D + (dd < D ? dd : 0));
+    }
+  };
+  auto load_a = [&](const bf16_t* q, int rb, bf16x8 (&af)[KS]) {
+    const int row = rb * 16 + li;
+    const bool ok = rb < RB && row < N;
+    const int64_t rowc = ok ? row : 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int dd = 32 * s + 8 * lg;
+      const bool in = ok && dd < D;
+      const uint4 u = *reinterpret_cast<const uint4*>(q + rowc * D + (dd < D ? dd : 0));
+      af[s] = __builtin_bit_cast(bf16x8, in ? u : make_uint4(0, 0, 0, 0));
+    }
+  };
+  auto scores = [&](const bf16x8 (&af)[KS], const bf16x8 (&bk)[TPW][KS], int t) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bk[t][s], acc, 0, 0, 0);
+    if (c0 + 16 * t + 16 > N && c0 + 16 * t + li >= N)  // padded key columns
+      acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    return acc;
+  };
+
+  int item = blockIdx.x;
+  if (item < FH) stage_keys(item);
+  int buf = 0, par = 0;
+  for (; item < FH; item += gridDim.x, par ^= 1) {
+    wait_stores_complete();  // this wave's direct loads have landed (vmcnt = 0)
+    __syncthreads();
+    const bf16_t* q = Qg + (int64_t)item * N * D;
+
+    // This wave's key fragments and the largest key norm; every query-row norm.
+    bf16x8 bk[TPW][KS];
+    float kn2 = 0.f;  // padded columns are zero
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int col = c0 + 16 * t + li;
+      float n2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dd = 32 * s + 8 * lg;
+        bk[t][s] = dd < D ? load_bf16x8(sK + col * D + dd) : zero_bf16x8();
+        n2 += sumsq8(bk[t][s]);
+      }
+      // the 4 lanes li, li+16, li+32, li+48 hold the chunks of one key row
+      n2 += __shfl_xor(n2, 16, kWave);
+      n2 += __shfl_xor(n2, 32, kWave);
+      kn2 = fmaxf(kn2, n2);
+    }
+    float qmax2 = 0.f;
+    for (int r = tid; r < N; r += NT) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) n2 += sumsq8(load_bf16x8(q + (int64_t)r * D + 8 * c));
+      qn2[r] = __builtin_amdgcn_sqrtf(n2);  // |q_r|
+      qmax2 = fmaxf(qmax2, n2);
+    }
+    kn2 = group_max<kWave>(kn2);
+    qmax2 = group_max<kWave>(qmax2);
+    // Rows N..Ncp-1 (padding of the last row block) reuse row N-1's norm.
+    if (tid == 0) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) n2 += sumsq8(load_bf16x8(q + (int64_t)(N - 1) * D + 8 * c));
+      const float nn = __builtin_amdgcn_sqrtf(n2);
+      for (int r = N; r < Ncp; ++r) qn2[r] = nn;
+    }
+    if (lane == 0) {  // non-negative floats: uint order
+      atomicMax(&maxu[2 * par], __float_as_uint(kn2));
+      atomicMax(&maxu[2 * par + 1], __float_as_uint(qmax2));
+    }
+    __syncthreads();  // fragments are in registers: the staging buffer is free
+    const float kc = __builtin_amdgcn_sqrtf(__uint_as_float(maxu[2 * par])) * c2 * 1.0009765625f;
+    const float cmax = __builtin_amdgcn_sqrtf(__uint_as_float(maxu[2 * par + 1])) * kc;
+    if (tid < 2) maxu[2 * (par ^ 1) + tid] = 0u;
+    const int nxt = item + gridDim.x;
+    if (nxt < FH) stage_keys(nxt);
+
+    float colacc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) colacc[t] = 0.f;
+
+    if (cmax <= 48.f) {
+      // Bound shift for the whole item: c_i = |q_i| * max|k| * scale (log2 units).
+      // Every wave uses the same shift for a row, so only partial sums are exchanged.
+      // Software pipeline over iterations of kRowBlocks row blocks:
+      //   MFMA(it) | column update of it-1 (independent, overlaps the MFMAs)
+      //   exp(it) -> partial row sums -> LDS | barrier | 1/L(it)
+      // Padded key columns (zero rows, so S = 0 exactly) each add exactly
+      // 2^-c_i to a row sum; the lanes owning them subtract that instead of
+      // masking every score.
+      int npad = 0;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) npad += (c0 + 16 * t + li >= N) ? 1 : 0;
+      const float fpad = (float)npad;
+      const bool padw = __any(npad > 0);  // only the wave(s) owning columns >= N
+      bf16x8 af[kRowBlocks][KS];
+#pragma unroll
+      for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, h, af[h]);
+
+      auto mfma_phase = [&](f32x4 (&S)[kRowBlocks][TPW], int it) {
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h][s2], bk[t][s2], acc, 0, 0, 0);
+            S[h][t] = acc;
+          }
+        }
+        // The A fragments are consumed: the next row blocks load into the same registers.
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * (it + 1) + h, af[h]);
+      };
+      auto update_phase = [&](const f32x4 (&S)[kRowBlocks][TPW], const float (&f)[kRowBlocks][4]) {
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) {
+            float c = colacc[t];
+            c = fmaf(S[h][t][0], f[h][0], c);
+            c = fmaf(S[h][t][1], f[h][1], c);
+            c = fmaf(S[h][t][2], f[h][2], c);
+            c = fmaf(S[h][t][3], f[h][3], c);
+            colacc[t] = c;
+          }
+        }
+      };
+      // exp + partial row sums of iteration it -> LDS, then this wave's arrival.
+      auto publish = [&](f32x4 (&S)[kRowBlocks][TPW], int it) {
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+          const int r0 = (kRowBlocks * it + h) * 16 + 4 * lg;
+          const float4 n4 = *reinterpret_cast<const float4*>(qn2 + r0);
+          const float cb[4] = {n4.x * kc, n4.y * kc, n4.z * kc, n4.w * kc};
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
+          if (padw) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[r] = -fpad * fast_exp2(-cb[r]);
+          }
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = fast_exp2(fmaf(S[h][t][r], c2, -cb[r]));
+              S[h][t][r] = p;
+              part[r] += p;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[r] = row16_sum(part[r]);
+          if (li == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              xch[((it & 1) * RPI + h * 16 + 4 * lg + r) * kColWaves + wave] = part[r];
+          }
+        }
+        // LDS operations of one wave complete in order: the partials land before the count.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      };
+      // Wait until all waves published iteration it, then the row weights 1/L.
+      // Every wave publishes it before it waits on it-1, so the wait always ends;
+      // the spin is bounded all the same.  Double-buffered partials are safe: a
+      // wave overwrites buffer (it & 1) only after seeing every wave's it+1,
+      // which each wave publishes after reading buffer (it & 1).
+      auto collect = [&](int it, float (&f)[kRowBlocks][4]) {
+        const uint32_t target = (uint32_t)kColWaves * (uint32_t)(it + 1);
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          if (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+          // Lane (quad position r) sums the 8 wave partials of row 4*lg + r;
+          // quad broadcasts then give every lane the weights of its 4 rows.
+          const int r = li & 3;
+          const float* x = xch + ((it & 1) * RPI + h * 16 + 4 * lg + r) * kColWaves;
+          const float4 l0 = *reinterpret_cast<const float4*>(x);
+          const float4 l1 = *reinterpret_cast<const float4*>(x + 4);
+          const float L = ((l0.x + l0.y) + (l0.z + l0.w)) + ((l1.x + l1.y) + (l1.z + l1.w));
+          const int row = (kRowBlocks * it + h) * 16 + 4 * lg + r;
+          const float fr = row < N ? __builtin_amdgcn_rcpf(L) : 0.f;
+          f[h][0] = dpp_f32<0x00>(fr);  // quad_perm [0,0,0,0]
+          f[h][1] = dpp_f32<0x55>(fr);  // quad_perm [1,1,1,1]
+          f[h][2] = dpp_f32<0xAA>(fr);  // quad_perm [2,2,2,2]
+          f[h][3] = dpp_f32<0xFF>(fr);  // quad_perm [3,3,3,3]
+        }
+      };
+
+      f32x4 SA[kRowBlocks][TPW], SB[kRowBlocks][TPW];
+      float fA[kRowBlocks][4], fB[kRowBlocks][4];
+      // MFMA(it) | wait for it-1's partials, weights, column update of it-1 | publish(it)
+      mfma_phase(SA, 0);
+      publish(SA, 0);
+      int it = 1;
+      for (; it + 1 < iters; it += 2) {
+        mfma_phase(SB, it);
+        collect(it - 1, fA);
+        update_phase(SA, fA);
+        publish(SB, it);
+        mfma_phase(SA, it + 1);
+        collect(it, fB);
+        update_phase(SB, fB);
+        publish(SA, it + 1);
+      }
+      if (it < iters) {
+        mfma_phase(SB, it);
+        collect(it - 1, fA);
+        update_phase(SA, fA);
+        publish(SB, it);
+        collect(it, fB);
+        update_phase(SB, fB);
+      } else {
+        collect(it - 1, fA);
+        update_phase(SA, fA);
+      }
+      __syncthreads();  // every wave is done with the partials and the counter
+      if (tid == 0) *arrived = 0u;  // ordered before the next publish by the item-start barrier
+    } else {
+      // Exact row max: each wave shifts by the max over its own columns and the
+      // partial (max, sum) pairs are merged with max-rescaling.
+      for (int it = 0; it < iters; ++it) {
+        bf16x8 af[kRowBlocks][KS];
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) load_a(q, kRowBlocks * it + h, af[h]);
+        f32x4 S[kRowBlocks][TPW];
+        float sh[kRowBlocks][4];
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) S[h][t] = scores(af[h], bk, t);
+          float part[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) m = fmaxf(m, S[h][t][r]);
+            m = row16_max(m);
+            sh[h][r] = m == -INFINITY ? -INFINITY : m * c2;
+            const float base = m == -INFINITY ? 0.f : m * c2;
+            float sum = 0.f;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+              const float p = fast_exp2(fmaf(S[h][t][r], c2, -base));
+              S[h][t][r] = p;
+              sum += p;
+            }
+            part[r] = row16_sum(sum);
+          }
+          if (li == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float* x = xch + ((buf * RPI + h * 16 + 4 * lg + r) * 2) * kColWaves + wave;
+              x[0] = sh[h][r];
+              x[kColWaves] = part[r];
+            }
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+          float f[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float* x = xch + ((buf * RPI + h * 16 + 4 * lg + r) * 2) * kColWaves;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kColWaves; ++w) M = fmaxf(M, x[w]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kColWaves; ++w)
+              L += x[w] == -INFINITY ? 0.f : x[kColWaves + w] * fast_exp2(x[w] - M);
+            const float a_own = sh[h][r] == -INFINITY ? 0.f : fast_exp2(sh[h][r] - M);
+            const int row = (kRowBlocks * it + h) * 16 + 4 * lg + r;
+            f[r] = (row < N && L > 0.f) ? a_own / L : 0.f;
+          }
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) {
+            float c = colacc[t];
+            c = fmaf(S[h][t][0], f[0], c);
+            c = fmaf(S[h][t][1], f[1], c);
+            c = fmaf(S[h][t][2], f[2], c);
+            c = fmaf(S[h][t][3], f[3], c);
+            colacc[t] = c;
+          }
+        }
+        buf ^= 1;
+      }
+    }
+
+    // Column totals: lanes li, li+16, li+32, li+48 hold the same column.
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float c = colacc[t];
+      c += __shfl_xor(c, 16, kWave);
+      c += __shfl_xor(c, 32, kWave);
+      const int col = c0 + 16 * t + li;
+      if (lg == 0 && col < N) colsum[(int64_t)item * N + col] = c;
+    }
+  }
+}
+
 // sal[f][j] = (1 / (H*N)) * sum_h colsum[f][h][j]
 __global__ __launch_bounds__(256) void salience_mean_kernel(const float* __restrict__ colsum,
                                                            int H, int N, float inv,
@@ -244,11 +657,88 @@ static hipError_t sal_ks(const void* q, const void* k, int FH, int N, int D, flo
   }
 }
 
+static int pick_tpw_colstat(int N) {
+  const int per = ((N + 15) / 16 + kColWaves - 1) / kColWaves;
+  const int opts[] = {1, 2, 3, 4, 6};
+  for (int o : opts)
+    if (o >= per) return o;
+  return -1;
+}
+
+static size_t colstat_lds_bytes(int tpw, int D) {
+  const int ncp = kColWaves * tpw * 16;
+  return (size_t)ncp * D * 2 + (size_t)2 * kRowBlocks * 16 * 2 * kColWaves * 4 + (size_t)ncp * 4 +
+         32;
+}
+
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <int D, int TPW>
+static hipError_t colstat_go(const void* q, const void* k, int FH, int N, float c2, float* colsum,
+                             hipStream_t st) {
+  const size_t lds = colstat_lds_bytes(TPW, D);
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)salience_colstat_kernel<D, TPW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSalMaxLds);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  int grid = cu_count();
+  if (grid > FH) grid = FH;
+  hipLaunchKernelGGL((salience_colstat_kernel<D, TPW>), dim3(grid), dim3(kColWaves * kWave), lds, st,
+                     (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t colstat_tpw(int tpw, const void* q, const void* k, int FH, int N, float c2,
+                              float* colsum, hipStream_t st) {
+  switch (tpw) {
+    case 1: return colstat_go<D, 1>(q, k, FH, N, c2, colsum, st);
+    case 2: return colstat_go<D, 2>(q, k, FH, N, c2, colsum, st);
+    case 3: return colstat_go<D, 3>(q, k, FH, N, c2, colsum, st);
+    case 4: return colstat_go<D, 4>(q, k, FH, N, c2, colsum, st);
+    case 6: return colstat_go<D, 6>(q, k, FH, N, c2, colsum, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The column-stationary kernel covers D in {64, 72, 80, 96} when its LDS fits.
+static bool colstat_ok(int N, int D) {
+  if (D != 64 && D != 72 && D != 80 && D != 96) return false;
+  const int tpw = pick_tpw_colstat(N);
+  return tpw > 0 && colstat_lds_bytes(tpw, D) <= (size_t)kSalMaxLds;
+}
+
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D, float scale,
                            float* colsum_ws, float* sal, hipStream_t st) {
   const float c2 = scale * 1.4426950408889634f;
   const int FH = F * H;
   hipError_t e;
+  if (colstat_ok(N, D)) {
+    const int tpw = pick_tpw_colstat(N);
+    switch (D) {
+      case 64: e = colstat_tpw<64>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
+      case 72: e = colstat_tpw<72>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
+      case 80: e = colstat_tpw<80>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
+      default: e = colstat_tpw<96>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
+    }
+    if (e != hipSuccess) return e;
+    dim3 grid((N + 255) / 256, F);
+    hipLaunchKernelGGL(salience_mean_kernel, grid, dim3(256), 0, st, colsum_ws, H, N,
+                       1.0f / ((float)H * (float)N), sal);
+    return hipGetLastError();
+  }
   switch (pick_tpw(N)) {
     case 4: e = sal_ks<4>(q, k, FH, N, D, c2, colsum_ws, st); break;
     case 8: e = sal_ks<8>(q, k, FH, N, D, c2, colsum_ws, st); break;
