@@ -148,6 +148,49 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Retrieval + sparse decode attention of one layer in one launch
+ *
+ * The same computation as sv_retrieve (Tq = 1) followed by
+ * sv_sparse_decode_attn on its indices (SparseVILA velog summary, Sec. 3.2:
+ * the current query selects the top-k visual tokens, and only those plus the
+ * text entries are attended; Sec. 4.5: decode attention over the reduced
+ * cache), as one kernel: the select of a sequence overlaps the attention
+ * over its text entries and the other sequences' work.
+ *
+ *  q          [B][Hq][D], contiguous (Tq = 1: one decode token).
+ *  k_vis,v_vis visual cache, element (b,t,g,d) at
+ *             ptr[b*vis_bstride + t*vis_tstride + g*D + d], t < N.
+ *  k          visual tokens to select and attend, 1 <= k <= N.
+ *  k_txt,v_txt,txt_len,Tmax,scale  as for sv_sparse_decode_attn.
+ *  idx_out    [B][k] int32: the selected indices, ascending (as sv_retrieve).
+ *  scores_out optional [B][N] fp32 scores (NULL: kept in the workspace).
+ *  out        [B][Hq][D] fp32 attention output.
+ *  workspace  at least sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax)
+ *             bytes, 256-byte aligned, ZERO-FILLED before its first use.  It
+ *             holds the scores, the split partials and a control block
+ *             (work ticket, completion counters, per-sequence ready flags);
+ *             every call leaves the control block zero again, so the
+ *             workspace can be reused and the call captured in a HIP graph.
+ *             Two calls that share a workspace must not run concurrently.
+ * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hq/Hkv in 1..8;
+ * Hkv*D <= 8192 (bf16) or <= 4096 (fp32); B <= 65535.
+ * Errors: SV_EINVAL (k < 1, k > N, Hq % Hkv != 0, NULL required pointer,
+ * bad strides or alignment), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax);
+
+sv_status sv_retrieve_attend(const void* q, int B, int Hq,
+                             const void* k_vis, const void* v_vis,
+                             int64_t vis_bstride, int64_t vis_tstride, int N,
+                             int Hkv, int D, int k,
+                             const void* k_txt, const void* v_txt,
+                             int64_t txt_bstride, int64_t txt_tstride,
+                             const int32_t* txt_len, int Tmax,
+                             sv_dtype dtype, float scale,
+                             int32_t* idx_out, float* scores_out, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Query-agnostic salience and per-frame pruning (prefill stage)
  *
  * SparseVILA velog summary, Sec. 3.1: salience is read off the vision

@@ -120,9 +120,11 @@ def multiturn_text_lengths(rounds: int = 3, steps: int = 128, system: int = 64,
 
 
 def scaled_decode(w: DecodeWorkload, *, B=None, L=None, N=None, T=None, Tmax=None,
-                  k=None, planted=None, name=None) -> DecodeWorkload:
-    """A smaller copy of a workload (for tests that the oracle finishes in seconds)."""
-    kw = dict(B=B, L=L, N=N, T=T, Tmax=Tmax, k=k, planted=planted, name=name)
+                  k=None, planted=None, name=None, Hq=None, Hkv=None, D=None,
+                  dtype=None) -> DecodeWorkload:
+    """A smaller (or reshaped) copy of a workload, for tests the oracle finishes in seconds."""
+    kw = dict(B=B, L=L, N=N, T=T, Tmax=Tmax, k=k, planted=planted, name=name, Hq=Hq, Hkv=Hkv,
+              D=D, dtype=dtype)
     kw = {a: b for a, b in kw.items() if b is not None}
     if "T" in kw and "Tmax" not in kw:
         kw["Tmax"] = max(kw["T"], w.Tmax if w.Tmax >= kw["T"] else kw["T"])

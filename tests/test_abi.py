@@ -29,7 +29,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = sv.load()
     names = declared_functions()
-    assert {"sv_retrieve", "sv_sparse_decode_attn", "sv_salience_prune"} <= set(names)
+    assert {"sv_retrieve", "sv_sparse_decode_attn", "sv_salience_prune",
+            "sv_retrieve_attend"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -46,6 +47,16 @@ def test_workspace_sizes():
     w = sv.sparse_decode_attn_workspace_bytes(8, 32, 32, 128, 360, 256)
     assert w >= 8 * 32 * 130 * 4 and w % 256 == 0
     assert sv.salience_prune_workspace_bytes(256, 16, 729) >= 256 * 16 * 729 * 4
+    f = sv.retrieve_attend_workspace_bytes(8, 32, 32, 128, 1440, 360, 256)
+    assert f % 256 == 0
+    assert f >= sv.retrieve_workspace_bytes(8, 1440, 360) + w
+
+
+def test_retrieve_rejects_slices_of_2gib():
+    # 131072 rows of 8192 bf16 elements = 2 GiB per sequence: past 32-bit offsets.
+    assert _retrieve(N=131072, k=4096, Hkv=64, Hq=64, ts=8192, bs=131072 * 8192,
+                     wsb=1 << 30) == 2
+    assert b"2 GiB" in sv.load().sv_last_error()
 
 
 def _retrieve(**kw):
@@ -118,3 +129,28 @@ def test_python_binding_refuses_cpu_tensors():
     kv = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         sv.retrieve(q, kv, 2)
+
+
+def _fused(**kw):
+    a = dict(q=FAKE, B=2, Hq=28, kv=FAKE, vv=FAKE, vbs=100 * 512, vts=512, N=100, Hkv=4, D=128,
+             k=10, kt=FAKE, vt=FAKE, tbs=8 * 512, tts=512, tl=FAKE, Tmax=8, dt=sv.SV_BF16,
+             scale=0.0, idx=FAKE, sc=None, out=FAKE, ws=FAKE, wsb=1 << 22, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_retrieve_attend(a["q"], a["B"], a["Hq"], a["kv"], a["vv"], a["vbs"], a["vts"],
+                                  a["N"], a["Hkv"], a["D"], a["k"], a["kt"], a["vt"], a["tbs"],
+                                  a["tts"], a["tl"], a["Tmax"], a["dt"], a["scale"], a["idx"],
+                                  a["sc"], a["out"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), 1), (dict(k=101), 1), (dict(N=0), 1), (dict(B=0), 1), (dict(Hq=30), 1),
+    (dict(q=None), 1), (dict(vv=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(ws=None), 1), (dict(kt=None), 1), (dict(tl=None), 1), (dict(vts=500), 1),
+    (dict(tts=100), 1), (dict(q=FAKE + 4), 1), (dict(Tmax=-1), 1),
+    (dict(Hq=36, Hkv=4), 2), (dict(D=96), 2), (dict(dt=5), 2), (dict(Hkv=128, Hq=128), 2),
+    (dict(wsb=64), 3),
+])
+def test_retrieve_attend_rejects(kw, status):
+    assert _fused(**kw) == status
+    assert sv.load().sv_last_error()

@@ -1,0 +1,183 @@
+"""GPU parity of the one-launch decode layer (sv_retrieve_attend).
+
+Against the fp64 oracle: the selected set (index-set rule of tests/accept.py)
+and the attention output over the GPU's own selection (2e-3 max-abs-relative
+per (b, h)).  Against the two-call path (sv_retrieve then
+sv_sparse_decode_attn): identical indices and bit-identical outputs, since
+both run the same work items with the same split plan.
+"""
+import numpy as np
+import pytest
+import torch
+
+import accept
+import oracle
+import synthetic
+import visual_token_sparsity_amd as sv
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _to(d, dev=DEV):
+    return {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d.items()}
+
+
+def _txt_lens(w):
+    return torch.tensor([max(0, w.T - 3 * b) for b in range(w.B)], dtype=torch.int32)
+
+
+FUSED_CASES = [
+    # name, workload, overrides
+    ("llava_b2", "llava_next_7b", dict(B=2)),
+    ("llava_b8_full_layer", "llava_next_7b", {}),
+    ("image576_fp32", "image576_fp32", {}),
+    ("qwen2_gqa7_n4096", "qwen2_7b_video", dict(N=4096, k=512, T=100, Tmax=128)),
+    ("qwen2_gqa7_ragged", "qwen2_7b_video", dict(N=3001, k=333, T=37, Tmax=40)),
+    ("multiturn_n8192", "multiturn_128k", dict(B=2, N=8192, k=1024, T=130, Tmax=256)),
+    ("visual_only", "llava_next_7b", dict(B=2, N=300, k=40, T=0, Tmax=0, planted=0)),
+    ("k_one", "llava_next_7b", dict(B=3, N=77, k=1, T=5, Tmax=8, planted=0)),
+    ("n_one", "llava_next_7b", dict(B=2, N=1, k=1, T=4, Tmax=4, planted=0)),
+    ("hkv28_rows448", "llava_next_7b", dict(B=2, N=500, k=64, Hq=28, Hkv=28, planted=0)),
+    ("hkv25_d64_ragged", "llava_next_7b", dict(B=2, N=300, k=50, Hq=25, Hkv=25, D=64, T=20,
+                                               Tmax=24, planted=0)),
+    ("hkv25_d64_fp32", "image576_fp32", dict(N=200, k=20, Hq=25, Hkv=25, D=64, planted=0)),
+    ("fp32_rows_two_segments", "image576_fp32", dict(N=130, k=30, T=10, Tmax=12, planted=0)),
+    ("bf16_rows_two_segments", "llava_next_7b", dict(B=2, N=130, k=30, Hq=64, Hkv=64, T=10,
+                                                     Tmax=12, planted=0)),
+]
+
+
+@pytest.mark.parametrize("name,wl,ov", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_retrieve_attend_parity(name, wl, ov):
+    w = synthetic.scaled_decode(synthetic.DECODE[wl], **ov)
+    _say("retrieve_attend", name, w)
+    d = synthetic.make_decode_layer(w, seed=11)
+    tl = _txt_lens(w)
+    g = _to(d)
+    out, idx, sc = sv.retrieve_attend(g["q"], g["k_vis"], g["v_vis"], w.k,
+                                      g["k_txt"] if w.Tmax else None,
+                                      g["v_txt"] if w.Tmax else None,
+                                      tl.to(DEV) if w.Tmax else None, scores=True)
+    torch.cuda.synchronize()
+    s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.k)
+    assert ok, msgs[:3]
+    scale = np.abs(s_ref).max(axis=1, keepdims=True) + 1e-30
+    assert (np.abs(sc.cpu().numpy() - s_ref) / scale).max() < 1e-5
+    ref = oracle.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx.cpu().numpy(), d["k_txt"],
+                                    d["v_txt"], tl.numpy() if w.Tmax else np.zeros(w.B, np.int64))
+    ok, err = accept.check_attention(out.cpu().numpy(), ref)
+    assert ok, err
+    if w.planted and w.k >= w.planted:
+        for b in range(w.B):
+            assert set(d["planted"][b].tolist()) <= set(idx[b].cpu().tolist())
+
+    # The two-call path runs the same items with the same plan: identical results.
+    idx2, sc2 = sv.retrieve(g["q"], g["k_vis"], w.k, scores=True)
+    out2 = sv.sparse_decode_attn(g["q"], g["k_vis"], g["v_vis"], idx2,
+                                 g["k_txt"] if w.Tmax else None, g["v_txt"] if w.Tmax else None,
+                                 tl.to(DEV) if w.Tmax else None)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc2)
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+
+
+def test_retrieve_attend_strided_caches():
+    """Cache views with spare capacity (token stride > row, batch stride > N rows)."""
+    w = synthetic.scaled_decode(synthetic.DECODE["llava_next_7b"], B=2, N=600, k=150, T=30, Tmax=40)
+    _say("retrieve_attend strided", w)
+    d = synthetic.make_decode_layer(w, seed=12)
+
+    def pad(t, rows):
+        big = torch.zeros(t.shape[0], rows, 40, t.shape[3], dtype=t.dtype)
+        big[:, :t.shape[1], :t.shape[2]] = t
+        return big.to(DEV)[:, :t.shape[1], :t.shape[2]]
+
+    kv, vv = pad(d["k_vis"], 700), pad(d["v_vis"], 700)
+    kt, vt = pad(d["k_txt"], 50), pad(d["v_txt"], 50)
+    tl = d["txt_len"].to(DEV)
+    out, idx = sv.retrieve_attend(d["q"].to(DEV), kv, vv, w.k, kt, vt, tl)
+    torch.cuda.synchronize()
+    s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.k)
+    assert ok, msgs[:3]
+    ref = oracle.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx.cpu().numpy(), d["k_txt"],
+                                    d["v_txt"], d["txt_len"])
+    ok, err = accept.check_attention(out.cpu().numpy(), ref)
+    assert ok, err
+
+
+def test_retrieve_attend_k_equals_n_matches_dense():
+    w = synthetic.scaled_decode(synthetic.DECODE["qwen2_7b_video"], N=700, k=700, T=64, Tmax=64)
+    _say("retrieve_attend k=N", w)
+    d = synthetic.make_decode_layer(w, seed=13)
+    g = _to(d)
+    out, idx = sv.retrieve_attend(g["q"], g["k_vis"], g["v_vis"], w.k, g["k_txt"], g["v_txt"],
+                                  g["txt_len"])
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [list(range(700))]
+    ref = oracle.dense_decode_attn(d["q"], d["k_vis"], d["v_vis"], d["k_txt"], d["v_txt"],
+                                   d["txt_len"])
+    ok, err = accept.check_attention(out.cpu().numpy(), ref)
+    assert ok, err
+
+
+def test_retrieve_attend_workspace_reuse_and_graph_replay():
+    """One zero-filled workspace across eager calls and graph replays of a two-layer step;
+    every call leaves the control block zero and gives identical results."""
+    w = synthetic.scaled_decode(synthetic.DECODE["llava_next_7b"], B=3, L=2, T=40, Tmax=64)
+    _say("retrieve_attend reuse + graph", w)
+    layers = [_to(synthetic.make_decode_layer(w, seed=14, layer=l)) for l in range(w.L)]
+    nbytes = sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax)
+    ws = sv.new_workspace(nbytes, DEV)
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=DEV) for _ in layers]
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV) for _ in layers]
+
+    def step():
+        for l, d in enumerate(layers):
+            sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
+                               d["txt_len"], workspace=ws, out=out[l], idx_out=idx[l])
+
+    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256   # one 128-byte line per word
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[-ctl_bytes:]) == 0
+    ref_idx = [t.clone() for t in idx]
+    ref_out = [t.clone() for t in out]
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    for l in range(w.L):
+        assert torch.equal(idx[l], ref_idx[l]) and torch.equal(out[l], ref_out[l])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    for rep in range(4):
+        for t in idx + out:
+            t.fill_(-7)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[-ctl_bytes:]) == 0, rep
+        for l in range(w.L):
+            assert torch.equal(idx[l], ref_idx[l]), (rep, l)
+            assert torch.equal(out[l], ref_out[l]), (rep, l)
+    for l, d in enumerate(layers):
+        host = {k: v.cpu() for k, v in d.items()}
+        s_ref = oracle.retrieval_scores(host["q"], host["k_vis"])
+        ok, _, msgs = accept.check_index_sets(ref_idx[l].cpu().numpy(), s_ref, w.k)
+        assert ok, msgs[:3]
+        ref = oracle.sparse_decode_attn(host["q"], host["k_vis"], host["v_vis"],
+                                        ref_idx[l].cpu().numpy(), host["k_txt"], host["v_txt"],
+                                        host["txt_len"])
+        ok, err = accept.check_attention(ref_out[l].cpu().numpy(), ref)
+        assert ok, err

@@ -9,6 +9,8 @@ raises.
     idx = retrieve(q, k_vis, k)                          # query-aware retrieval
     out = sparse_decode_attn(q, k_vis, v_vis, idx,       # attention over the
                              k_txt, v_txt, txt_len)      #   selected + text entries
+    out, idx = retrieve_attend(q, k_vis, v_vis, k,       # both, one launch per layer
+                               k_txt, v_txt, txt_len)
     sal, keep_idx = salience_prune(vis_q, vis_k, keep)   # prefill salience prune
 """
 from __future__ import annotations
@@ -22,7 +24,8 @@ import torch  # loaded first so libsv binds to torch's HIP runtime
 __all__ = [
     "SvError", "lib_path", "load", "retrieve", "retrieve_workspace_bytes",
     "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
-    "salience_prune_workspace_bytes", "new_workspace", "SV_F32", "SV_BF16",
+    "salience_prune_workspace_bytes", "new_workspace", "retrieve_attend",
+    "retrieve_attend_workspace_bytes", "SV_F32", "SV_BF16",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -63,6 +66,12 @@ def load() -> ctypes.CDLL:
                                           c_p, c_i, c_p, c_p, c_i64, c_i64, c_p, c_i, c_i, c_f,
                                           c_p, c_p, c_sz, c_p]
     lib.sv_sparse_decode_attn.restype = c_i
+    lib.sv_retrieve_attend_workspace.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_i]
+    lib.sv_retrieve_attend_workspace.restype = c_sz
+    lib.sv_retrieve_attend.argtypes = [c_p, c_i, c_i, c_p, c_p, c_i64, c_i64, c_i, c_i, c_i, c_i,
+                                       c_p, c_p, c_i64, c_i64, c_p, c_i, c_i, c_f, c_p, c_p, c_p,
+                                       c_p, c_sz, c_p]
+    lib.sv_retrieve_attend.restype = c_i
     lib.sv_salience_prune_workspace.argtypes = [c_i, c_i, c_i]
     lib.sv_salience_prune_workspace.restype = c_sz
     lib.sv_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_p, c_p,
@@ -215,6 +224,67 @@ def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor
         _dtype(q), float(scale) if scale else 0.0, res.data_ptr(), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(dev)))
     return res
+
+
+def retrieve_attend_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, N: int, k: int,
+                                    Tmax: int) -> int:
+    return int(load().sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax))
+
+
+def retrieve_attend(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor, k: int,
+                    k_txt: Optional[torch.Tensor], v_txt: Optional[torch.Tensor],
+                    txt_len: Optional[torch.Tensor], scale: Optional[float] = None, *,
+                    scores: bool = False, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None):
+    """One decode layer in one launch: top-k retrieval for ``q`` and attention over
+    the selected visual entries plus the text entries.
+
+    q        [B][Hq][D] (or [B][1][Hq][D]): one decode token
+    k_vis, v_vis  [B][N][Hkv][D] (same strides)
+    k        visual tokens selected and attended (1 <= k <= N)
+    k_txt, v_txt  [B][Tmax][Hkv][D] (same strides) or None
+    txt_len  int32 [B] on the device, or None when there is no text
+    returns (out fp32 [B][Hq][D], idx int32 [B][k] ascending[, scores fp32 [B][N]])
+    """
+    lib = load()
+    if q.dim() == 4:
+        if q.shape[1] != 1:
+            raise ValueError("retrieve_attend takes one decode token per sequence")
+        q = q[:, 0]
+    dev = _on_gpu(q, k_vis, v_vis, k_txt, v_txt, txt_len)
+    if q.dtype != k_vis.dtype or v_vis.dtype != k_vis.dtype:
+        raise TypeError("q, k_vis and v_vis must share a dtype")
+    q = q.contiguous()
+    B, Hq, D = q.shape
+    _, N, Hkv, Dk = k_vis.shape
+    if Dk != D or k_vis.shape[0] != B:
+        raise ValueError("q and k_vis shapes disagree")
+    if k_vis.stride() != v_vis.stride() or k_vis.shape != v_vis.shape:
+        raise ValueError("k_vis and v_vis must share shape and strides")
+    vbs, vts = _cache_strides(k_vis, "k_vis")
+    if k_txt is not None:
+        if k_txt.stride() != v_txt.stride() or k_txt.shape != v_txt.shape:
+            raise ValueError("k_txt and v_txt must share shape and strides")
+        if k_txt.dtype != q.dtype:
+            raise TypeError("k_txt must share the dtype of q")
+        tbs, tts = _cache_strides(k_txt, "k_txt")
+        Tmax = k_txt.shape[1]
+        if txt_len is None or txt_len.dtype != torch.int32:
+            raise TypeError("txt_len must be an int32 device tensor")
+        txt_len = txt_len.contiguous()
+    else:
+        tbs = tts = Tmax = 0
+    res = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    idx = idx_out if idx_out is not None else torch.empty((B, max(k, 0)), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, N), dtype=torch.float32, device=dev) if scores else None
+    ws = _workspace(retrieve_attend_workspace_bytes(B, Hq, Hkv, D, N, k, Tmax), dev, workspace)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.sv_retrieve_attend(
+        q.data_ptr(), B, Hq, k_vis.data_ptr(), v_vis.data_ptr(), vbs, vts, N, Hkv, D, k,
+        ptr(k_txt), ptr(v_txt), tbs, tts, ptr(txt_len) if Tmax else None, Tmax, _dtype(q),
+        float(scale) if scale else 0.0, idx.data_ptr(), ptr(sc), res.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(dev)))
+    return (res, idx, sc) if scores else (res, idx)
 
 
 def salience_prune_workspace_bytes(F: int, H: int, N: int) -> int:

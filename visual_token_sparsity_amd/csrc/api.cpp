@@ -2,6 +2,7 @@
 // carving and kernel launches.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -37,11 +38,38 @@ int vec_elems(sv_dtype dt) { return dt == SV_BF16 ? 8 : 4; }
 
 bool dtype_ok(sv_dtype dt) { return dt == SV_BF16 || dt == SV_F32; }
 
+// The kernels address one sequence's cache slice (rows 0..n-1 at `tstride`
+// elements apart, each `row` elements long) with 32-bit byte offsets.
+bool extent_ok(int64_t n, int64_t tstride, int64_t row, sv_dtype dt) {
+  if (n <= 0) return true;
+  const int64_t es = dt == SV_BF16 ? 2 : 4;
+  return ((n - 1) * tstride + row) * es < ((int64_t)1 << 31);
+}
+
 }  // namespace
+
+namespace sv {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace sv
 
 extern "C" {
 
-int sv_version(void) { return 100; }
+int sv_version(void) { return 110; }
 
 const char* sv_last_error(void) { return g_err.c_str(); }
 
@@ -49,10 +77,13 @@ const char* sv_last_error(void) { return g_err.c_str(); }
 // Workspace of sv_retrieve: [scores B*N fp32][counters B uint32].
 static size_t retrieve_scores_bytes(int B, int N) { return align256((size_t)B * (size_t)N * sizeof(float)); }
 
+// Control words: one 128-byte line each.
+static size_t ctr_bytes(size_t n) { return align256(n * sv::kCtrStride * sizeof(uint32_t)); }
+
 size_t sv_retrieve_workspace(int B, int N, int k) {
   (void)k;
   if (B < 1 || N < 1) return 256;
-  return retrieve_scores_bytes(B, N) + align256((size_t)B * sizeof(uint32_t));
+  return retrieve_scores_bytes(B, N) + ctr_bytes((size_t)B);
 }
 
 sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, int64_t k_bstride,
@@ -77,13 +108,15 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
                 (long long)k_bstride, (long long)k_tstride, ve);
   if (!aligned16(q) || !aligned16(k_vis))
     return fail(SV_EINVAL, "sv_retrieve: q and k_vis must be 16-byte aligned");
+  if (!extent_ok(N, k_tstride, R, dtype))
+    return fail(SV_EUNSUPPORTED, "sv_retrieve: one sequence's key slice spans 2 GiB or more");
   if (workspace_bytes < sv_retrieve_workspace(B, N, k))
     return fail(SV_EWORKSPACE, "sv_retrieve: workspace %zu < %zu bytes", workspace_bytes,
                 sv_retrieve_workspace(B, N, k));
   float* scores = scores_out ? scores_out : (float*)workspace;
   uint32_t* counters = (uint32_t*)((char*)workspace + retrieve_scores_bytes(B, N));
   return hip_status(sv::launch_retrieve(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D,
-                                        (int)dtype, scores, k, idx_out, counters,
+                                        (int)dtype, scores, k, idx_out, counters, 0,
                                         (hipStream_t)stream),
                     "sv_retrieve");
 }
@@ -92,9 +125,9 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
 // Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+2) fp32][counters B*Hkv uint32].
 static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax) {
   size_t best = 0;
-  for (int dt = 0; dt < 2; ++dt) {
-    const int C = sv::attn_splits(B, Hkv, D, dt, k, Tmax, nullptr);
-    const size_t bytes = (size_t)B * Hq * C * (D + 2) * sizeof(float);
+  for (int ve = 4; ve <= 8; ve += 4) {
+    const sv::AttnPlan p = sv::attn_plan(B, Hkv, D, ve, k, Tmax, sv::kAttnTargetItems);
+    const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * (D + 2) * sizeof(float);
     if (bytes > best) best = bytes;
   }
   return align256(best);
@@ -102,7 +135,7 @@ static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax)
 
 size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || k < 0 || Tmax < 0) return 256;
-  return attn_partial_bytes(B, Hq, Hkv, D, k, Tmax) + align256((size_t)B * Hkv * sizeof(uint32_t));
+  return attn_partial_bytes(B, Hq, Hkv, D, k, Tmax) + ctr_bytes((size_t)B * Hkv);
 }
 
 sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
@@ -134,6 +167,8 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
   if (!aligned16(q) || (k > 0 && (!aligned16(k_vis) || !aligned16(v_vis))) ||
       (Tmax > 0 && (!aligned16(k_txt) || !aligned16(v_txt))))
     return fail(SV_EINVAL, "sv_sparse_decode_attn: q and caches must be 16-byte aligned");
+  if ((k > 0 && !extent_ok(N, vis_tstride, R, dtype)) || !extent_ok(Tmax, txt_tstride, R, dtype))
+    return fail(SV_EUNSUPPORTED, "sv_sparse_decode_attn: one sequence's cache slice spans 2 GiB or more");
   const size_t need = sv_sparse_decode_attn_workspace(B, Hq, Hkv, D, k, Tmax);
   if (workspace_bytes < need)
     return fail(SV_EWORKSPACE, "sv_sparse_decode_attn: workspace %zu < %zu bytes", workspace_bytes, need);
@@ -142,9 +177,91 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
       (uint32_t*)((char*)workspace + attn_partial_bytes(B, Hq, Hkv, D, k, Tmax));
   return hip_status(sv::launch_attn(q, B, Hq, k_vis, v_vis, vis_bstride, vis_tstride, N, Hkv, D, idx,
                                     k, k_txt, v_txt, txt_bstride, txt_tstride, txt_len, Tmax,
-                                    (int)dtype, sc, out, (float*)workspace, counters,
+                                    (int)dtype, sc, out, (float*)workspace, counters, 0,
                                     (hipStream_t)stream),
                     "sv_sparse_decode_attn");
+}
+
+// ---------------------------------------------------------------- fused layer
+// Workspace of sv_retrieve_attend:
+//   [scores B*N fp32][partials][control: seq B | ready B | vis_done B | comb B*Hkv],
+// every control word on its own 128-byte line.
+static size_t fused_ctl_bytes(int B, int Hkv) { return ctr_bytes((size_t)B * (3 + Hkv)); }
+
+size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return 256;
+  return retrieve_scores_bytes(B, N) + attn_partial_bytes(B, Hq, Hkv, D, k, Tmax) +
+         fused_ctl_bytes(B, Hkv);
+}
+
+sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
+                             int64_t vis_bstride, int64_t vis_tstride, int N, int Hkv, int D,
+                             int k, const void* k_txt, const void* v_txt, int64_t txt_bstride,
+                             int64_t txt_tstride, const int32_t* txt_len, int Tmax,
+                             sv_dtype dtype, float scale, int32_t* idx_out, float* scores_out,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "sv_retrieve_attend";
+  if (!q || !k_vis || !v_vis || !idx_out || !out || !workspace)
+    return fail(SV_EINVAL, "%s: NULL q, k_vis, v_vis, idx_out, out or workspace", fn);
+  if (B < 1 || B > 65535 || Hq < 1 || Hkv < 1 || N < 1 || Tmax < 0)
+    return fail(SV_EINVAL, "%s: bad sizes B=%d Hq=%d Hkv=%d N=%d Tmax=%d", fn, B, Hq, Hkv, N, Tmax);
+  if (k < 1 || k > N) return fail(SV_EINVAL, "%s: k=%d outside [1, N=%d]", fn, k, N);
+  if (Tmax > 0 && (!k_txt || !v_txt || !txt_len))
+    return fail(SV_EINVAL, "%s: NULL k_txt, v_txt or txt_len", fn);
+  if (Hq % Hkv) return fail(SV_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (!dtype_ok(dtype)) return fail(SV_EUNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (D != 64 && D != 128) return fail(SV_EUNSUPPORTED, "%s: D=%d (64 or 128)", fn, D);
+  if (Hq / Hkv > 8) return fail(SV_EUNSUPPORTED, "%s: group size %d > 8", fn, Hq / Hkv);
+  const int64_t R = (int64_t)Hkv * D;
+  if (R > (dtype == SV_BF16 ? 8192 : 4096))
+    return fail(SV_EUNSUPPORTED, "%s: row Hkv*D=%lld too long", fn, (long long)R);
+  const int ve = vec_elems(dtype);
+  if (vis_tstride < R || vis_bstride < 0 || vis_tstride % ve || vis_bstride % ve)
+    return fail(SV_EINVAL, "%s: visual strides must be >= row and multiples of %d", fn, ve);
+  if (Tmax > 0 && (txt_tstride < R || txt_bstride < 0 || txt_tstride % ve || txt_bstride % ve))
+    return fail(SV_EINVAL, "%s: text strides must be >= row and multiples of %d", fn, ve);
+  if (!aligned16(q) || !aligned16(k_vis) || !aligned16(v_vis) ||
+      (Tmax > 0 && (!aligned16(k_txt) || !aligned16(v_txt))))
+    return fail(SV_EINVAL, "%s: q and caches must be 16-byte aligned", fn);
+  if (!extent_ok(N, vis_tstride, R, dtype) || !extent_ok(Tmax, txt_tstride, R, dtype))
+    return fail(SV_EUNSUPPORTED, "%s: one sequence's cache slice spans 2 GiB or more", fn);
+  const size_t need = sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax);
+  if (workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+
+  char* ws = (char*)workspace;
+  sv::FusedLaunch f{};
+  f.q = q;
+  f.B = B;
+  f.Hq = Hq;
+  f.Hkv = Hkv;
+  f.D = D;
+  f.dtype = (int)dtype;
+  f.k_vis = k_vis;
+  f.v_vis = v_vis;
+  f.vbs = vis_bstride;
+  f.vts = vis_tstride;
+  f.N = N;
+  f.k = k;
+  f.k_txt = k_txt;
+  f.v_txt = v_txt;
+  f.tbs = txt_bstride;
+  f.tts = txt_tstride;
+  f.txt_len = txt_len;
+  f.Tmax = Tmax;
+  f.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  f.idx = idx_out;
+  f.scores = scores_out ? scores_out : (float*)ws;
+  f.out = out;
+  ws += retrieve_scores_bytes(B, N);
+  f.part = (float*)ws;
+  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax);
+  uint32_t* ctl = (uint32_t*)ws;
+  f.seq_ctr = ctl;
+  f.ready = f.seq_ctr + (size_t)B * sv::kCtrStride;
+  f.vis_done = f.ready + (size_t)B * sv::kCtrStride;
+  f.comb_ctr = f.vis_done + (size_t)B * sv::kCtrStride;
+  return hip_status(sv::launch_fused(f, (hipStream_t)stream), fn);
 }
 
 // ---------------------------------------------------------------- salience

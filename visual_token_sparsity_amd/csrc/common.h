@@ -20,6 +20,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------- buffer loads
+// A raw buffer resource (base, byte extent) lives in scalar registers; a load
+// takes a 32-bit per-lane byte offset plus a wave-uniform byte offset, and
+// any access at or past the extent returns zero without touching memory.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr uint32_t kBufOob = 0x80000000u;  // an offset past every extent in use
+constexpr int kCacheStream = 2;            // non-temporal: data read once
+constexpr int kCacheDefault = 0;
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t extent_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent_bytes,
+                                           0x00020000);
+}
+
 // 16-byte vector of storage elements, widened to fp32.
 template <typename T> struct Vec;
 
@@ -29,6 +43,10 @@ template <> struct Vec<bf16_t> {
   __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void load_stream(const bf16_t* p) {
     raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  template <int Aux>
+  __device__ __forceinline__ void load_buf(BufRsrc r, uint32_t voff, uint32_t soff) {
+    raw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, Aux));
   }
   __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ void to_f32(float* f) const {
@@ -46,6 +64,10 @@ template <> struct Vec<float> {
   __device__ __forceinline__ void load_stream(const float* p) {
     raw = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
   }
+  template <int Aux>
+  __device__ __forceinline__ void load_buf(BufRsrc r, uint32_t voff, uint32_t soff) {
+    raw = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, Aux));
+  }
   __device__ __forceinline__ void zero() { raw = f32x4v{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void to_f32(float* f) const {
     f[0] = raw.x; f[1] = raw.y; f[2] = raw.z; f[3] = raw.w;
@@ -59,6 +81,11 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_key (for keys of finite or infinite values).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -78,6 +105,41 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Whole-wave inclusive prefix sum (all 64 lanes active), DPP only: row
+// shifts build 16-lane scans, then row broadcasts carry the row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Whole-wave min and max (all 64 lanes active), returned wave-uniform:
+// butterflies inside each 16-lane row, then the four row results.
+__device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
+#define SV_DPP_F(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false))
+  mn = fminf(mn, SV_DPP_F(mn, 0xB1));   // quad_perm [1,0,3,2]
+  mx = fmaxf(mx, SV_DPP_F(mx, 0xB1));
+  mn = fminf(mn, SV_DPP_F(mn, 0x4E));   // quad_perm [2,3,0,1]
+  mx = fmaxf(mx, SV_DPP_F(mx, 0x4E));
+  mn = fminf(mn, SV_DPP_F(mn, 0x141));  // row_half_mirror
+  mx = fmaxf(mx, SV_DPP_F(mx, 0x141));
+  mn = fminf(mn, SV_DPP_F(mn, 0x140));  // row_mirror
+  mx = fmaxf(mx, SV_DPP_F(mx, 0x140));
+#undef SV_DPP_F
+  float a = mn, b = mx;
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    a = fminf(a, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), r)));
+    b = fmaxf(b, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), r)));
+  }
+  mn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a)));
+  mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b)));
+}
+
 // ---------------------------------------------------------------- cross-workgroup hand-off
 // Each XCD has its own L2, and an agent-scope fence would write back or
 // invalidate a whole L2.  Data handed from one workgroup to another inside a
@@ -93,6 +155,15 @@ __device__ __forceinline__ float load_shared_dev(const float* p) {
 __device__ __forceinline__ void wait_stores_complete() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
 }
+__device__ __forceinline__ int32_t load_shared_dev_i32(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_flag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t counter_add(uint32_t* c, uint32_t v) {
   return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -100,22 +171,69 @@ __device__ __forceinline__ void counter_reset(uint32_t* c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Counters and flags touched by many workgroups each sit on their own
+// 128-byte line: same-line atomics from many workgroups serialise.
+constexpr int kCtrStride = 32;  // uint32 words
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
+
+// Compute units of the current device.
+int device_cu_count();
+
+// Scan rows per work item when the caller does not choose (0).
+int scan_rows_per_item(int B, int N, int LPR, int nseg);
+
 hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv, int64_t bstride,
                            int64_t tstride, int N, int Hkv, int D, int dtype, float* scores, int k,
-                           int32_t* idx_out, uint32_t* counters, hipStream_t stream);
+                           int32_t* idx_out, uint32_t* counters, int rows_per_item,
+                           hipStream_t stream);
 
 hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int N, int k,
                             int32_t* out, hipStream_t stream);
 
-int attn_splits(int B, int Hkv, int D, int dtype, int k, int Tmax, int* epl_out);
+// Split plan of the decode attention: EPL entries per lane, SE entries per
+// split, CT text splits then CV visual splits.
+struct AttnPlan {
+  int EPL, SE, CT, CV;
+};
+constexpr long kAttnTargetItems = 1024;
+AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_items);
 
 hipError_t launch_attn(const void* q, int B, int Hq, const void* kv, const void* vv,
                        int64_t vbs, int64_t vts, int N, int Hkv, int D, const int32_t* idx,
                        int k, const void* kt, const void* vt, int64_t tbs, int64_t tts,
                        const int32_t* txt_len, int Tmax, int dtype, float scale, float* out,
-                       float* partials, uint32_t* counters, hipStream_t stream);
+                       float* partials, uint32_t* counters, int epl, hipStream_t stream);
+
+// Retrieval + sparse attention of one layer in one launch (Tq = 1).
+struct FusedLaunch {
+  const void* q;
+  int B, Hq, Hkv, D, dtype;
+  const void* k_vis;
+  const void* v_vis;
+  int64_t vbs, vts;
+  int N, k;
+  const void* k_txt;
+  const void* v_txt;
+  int64_t tbs, tts;
+  const int32_t* txt_len;
+  int Tmax;
+  float scale;
+  int32_t* idx;        // [B][k]
+  float* scores;       // [B][N]
+  float* out;          // [B][Hq][D]
+  float* part;         // partials
+  // Control words, each on its own 128-byte line (stride 32 words), zero
+  // before the launch and zero again after it.
+  uint32_t* seq_ctr;   // [B]
+  uint32_t* ready;     // [B]
+  uint32_t* vis_done;  // [B]
+  uint32_t* comb_ctr;  // [B][Hkv]
+  int rows_per_item;   // 0: default
+  int epl;             // 0: default
+};
+hipError_t launch_fused(const FusedLaunch& f, hipStream_t stream);
 
 bool salience_supported(int N, int D);
 

@@ -1,0 +1,522 @@
+// Work items of the decode hot path (internal header), shared by the
+// standalone retrieval kernel, the standalone attention kernel and the fused
+// per-layer kernel.
+//
+// Scan item (SparseVILA velog summary, Sec. 3.2, Query-Aware Token Selection;
+// xllm-io review, core formulas): scores s[b,t] = sum_g qhat[b,g,:] . K[b,t,g,:]
+// for a contiguous run of cache rows of sequence b, where qhat[b,g] is the sum
+// of the query over its Tq tokens and the G query heads of KV head g.  The
+// score is linear in the query, so summing first equals summing per-head
+// logits.  qhat lives in LDS (two planes of four floats per 16-byte chunk, so
+// a wave's reads are conflict-free); registers hold only two rows of keys in
+// flight per lane.  A row of C 16-byte chunks is split into segments of at
+// most 512 chunks; LPR lanes (a power of two) cover one segment with up to 8
+// chunks each.  Chunks past the row end read a clamped in-row address and
+// meet a zero in qhat, so every load is unconditional.
+//
+// Select (same passage): when the last scan item of a sequence finishes, its
+// workgroup takes the exact top-k of the score row (select.h).
+//
+// Attention item (velog summary, Sec. 3.2 and Sec. 4.5): split c of KV head g
+// of sequence b.  Splits [0, CT) cover the text entries, splits [CT, CT+CV)
+// the selected visual entries, SE entries each.  A lane group of LPE lanes
+// owns EPL entries and reads their K and V head rows as 16-byte vectors (a
+// gather: no packed copy is made), all loads in flight before any math; the
+// softmax runs in base 2 on a query pre-scaled by scale*log2(e).  Partials
+// (m, l, acc) go out with device-coherent stores; the last split of (b, g) to
+// arrive merges them by max-rescaling and writes the output.
+#pragma once
+
+#include "common.h"
+#include "select.h"
+
+namespace sv {
+
+constexpr int kItemWaves = 4;
+constexpr int kItemThreads = kItemWaves * kWave;
+constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment
+constexpr int kScanSegChunks = 512;
+constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
+
+// ---------------------------------------------------------------- scan
+struct ScanArgs {
+  const void* q;
+  int Tq, Hq, G;
+  const void* kv;
+  int64_t bstride, tstride;  // elements
+  int N, D;
+  int C;                     // 16-byte chunks per row
+  int nseg, LPR;             // segments per row, lanes per segment
+  int rows_per_item, items_per_seq;
+  float* scores;             // [B][N]
+  int k;
+  int32_t* idx;              // [B][k]
+  uint32_t* seq_ctr;         // [B] (stride kCtrStride) finished scan items, self-resetting
+  uint32_t* ready;           // [B] (stride kCtrStride) selection published (fused kernel only)
+};
+
+// Chunks of qhat kept in LDS (zero past C).
+__host__ __device__ inline int scan_padded_chunks(int nseg, int LPR) {
+  return nseg > 1 ? nseg * kScanSegChunks : LPR * kScanCpl;
+}
+
+__host__ inline void scan_geometry(int C, int* nseg, int* LPR) {
+  if (C > kScanSegChunks) {
+    *nseg = (C + kScanSegChunks - 1) / kScanSegChunks;
+    *LPR = kWave;
+    return;
+  }
+  *nseg = 1;
+  const int need = (C + kScanCpl - 1) / kScanCpl;
+  int l = 1;
+  while (l < need) l <<= 1;
+  *LPR = l;
+}
+
+__device__ __forceinline__ float sum_lanes_rt(float v, int width) {
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// One scan item: rows [item*rows_per_item, ...) of sequence b.  Returns true
+// in every thread of the workgroup that must run the select for b.  q_of is
+// the sequence whose qhat LDS holds (-1: none); it is reused when it matches.
+template <typename T>
+__device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, char* smem,
+                                          int& q_of) {
+  constexpr int VE = Vec<T>::kElems;
+  constexpr int NP = VE / 4;  // float4 planes of qhat
+  constexpr int ES = (int)sizeof(T);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int LPR = a.LPR, nseg = a.nseg;
+  const int RPS = kWave / LPR;  // units per wave step
+  const int sub = lane & (LPR - 1);
+  const int rsub = lane / LPR;
+  const int CP = scan_padded_chunks(nseg, LPR);
+  float* qh = reinterpret_cast<float*>(smem);  // [NP][CP][4]
+
+  const int r0 = item * a.rows_per_item;
+  int r1 = r0 + a.rows_per_item;
+  r1 = r1 < a.N ? r1 : a.N;
+  const int nrows = r1 - r0;
+  int wrows = (nrows + kItemWaves - 1) / kItemWaves;
+  wrows = ((wrows + RPS - 1) / RPS) * RPS;
+  const int wr0 = wave * wrows;  // relative to r0
+  int wn = nrows - wr0;
+  wn = wn < 0 ? 0 : (wn > wrows ? wrows : wn);
+  const int nunits = wn * nseg;
+
+  // The item's rows as one buffer: row r at byte (r - r0) * row_bytes.
+  const uint32_t row_bytes = (uint32_t)(a.tstride * ES);
+  const BufRsrc rs = make_rsrc(
+      reinterpret_cast<const char*>(a.kv) + ((int64_t)b * a.bstride + (int64_t)r0 * a.tstride) * ES,
+      (uint32_t)(nrows - 1) * row_bytes + (uint32_t)a.C * 16u);
+  // Unit u of this wave: row wr0 + u / nseg, segment u % nseg.  Units past the
+  // wave's run read past the extent (zeros, no memory traffic).
+  auto unit_seg = [&](int u) { return nseg == 1 ? 0 : u % nseg; };
+  auto unit_off = [&](int u) -> uint32_t {
+    if (u >= nunits) return kBufOob;
+    const int row = wr0 + (nseg == 1 ? u : u / nseg);
+    return (uint32_t)row * row_bytes + (uint32_t)(unit_seg(u) * kScanSegChunks + sub) * 16u;
+  };
+  // Chunk j of a unit is chunk sub + j*LPR of its segment; chunks past the
+  // segment are not loaded (uniform) or, where a segment is ragged, zeroed.
+  auto load_unit = [&](int u, Vec<T>* dst) {
+    const int slen = min(kScanSegChunks, a.C - unit_seg(u < nunits ? u : 0) * kScanSegChunks);
+    const uint32_t off = unit_off(u);
+#pragma unroll
+    for (int j = 0; j < kScanCpl; ++j) {
+      if (j * LPR < slen)
+        dst[j].template load_buf<kCacheStream>(rs, off, (uint32_t)(j * LPR * 16));
+      else
+        dst[j].zero();
+    }
+  };
+  auto mask_ragged = [&](int u, Vec<T>* v) {
+    const int slen = min(kScanSegChunks, a.C - unit_seg(u) * kScanSegChunks);
+    if (slen % LPR == 0) return;  // uniform
+#pragma unroll
+    for (int j = 0; j < kScanCpl; ++j)
+      if (sub + j * LPR >= slen) v[j].zero();
+  };
+
+  // First keys in flight before the query is summed.
+  Vec<T> nxt[kScanCpl];
+  load_unit(rsub, nxt);
+
+  // qhat -> LDS (zero past C).
+  if (q_of != b) {
+    const T* qb = reinterpret_cast<const T*>(a.q);
+    for (int c = tid; c < CP; c += kItemThreads) {
+      float acc[VE];
+#pragma unroll
+      for (int v = 0; v < VE; ++v) acc[v] = 0.f;
+      if (c < a.C) {
+        const int e0 = c * VE;
+        const int g = e0 / a.D, d0 = e0 % a.D;
+        for (int tau = 0; tau < a.Tq; ++tau) {
+          for (int i = 0; i < a.G; ++i) {
+            Vec<T> x;
+            x.load(qb + ((int64_t)(b * a.Tq + tau) * a.Hq + g * a.G + i) * a.D + d0);
+            float f[VE];
+            x.to_f32(f);
+#pragma unroll
+            for (int v = 0; v < VE; ++v) acc[v] += f[v];
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        *reinterpret_cast<f32x4v*>(qh + ((int64_t)p * CP + c) * 4) =
+            f32x4v{acc[4 * p], acc[4 * p + 1], acc[4 * p + 2], acc[4 * p + 3]};
+    }
+    __syncthreads();
+    q_of = b;
+  }
+
+  const bool coherent = a.k > 0;
+  float* srow = a.scores + (int64_t)b * a.N + r0;
+  float acc = 0.f;
+  for (int u0 = 0; u0 < nunits; u0 += RPS) {
+    Vec<T> cur[kScanCpl];
+#pragma unroll
+    for (int j = 0; j < kScanCpl; ++j) cur[j] = nxt[j];
+    if (u0 + RPS < nunits) load_unit(u0 + RPS + rsub, nxt);
+    const int u = u0 + rsub;
+    const int seg = unit_seg(u);
+    mask_ragged(u, cur);
+#pragma unroll
+    for (int j = 0; j < kScanCpl; ++j) {
+      const int ch = seg * kScanSegChunks + sub + j * LPR;
+      float f[VE];
+      cur[j].to_f32(f);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const f32x4v w = *reinterpret_cast<const f32x4v*>(qh + ((int64_t)p * CP + ch) * 4);
+        acc = fmaf(w.x, f[4 * p], acc);
+        acc = fmaf(w.y, f[4 * p + 1], acc);
+        acc = fmaf(w.z, f[4 * p + 2], acc);
+        acc = fmaf(w.w, f[4 * p + 3], acc);
+      }
+    }
+    if (seg == nseg - 1) {
+      const float s = sum_lanes_rt(acc, LPR);
+      acc = 0.f;
+      if (sub == 0 && u < nunits) {
+        const int row = wr0 + u / nseg;
+        if (coherent)
+          store_shared_dev(srow + row, s);  // read back by the selecting workgroup
+        else
+          srow[row] = s;
+      }
+    }
+  }
+
+  if (!coherent) return false;
+  __shared__ uint32_t s_last;
+  wait_stores_complete();
+  __syncthreads();
+  if (tid == 0)
+    s_last = counter_add(&a.seq_ctr[b * kCtrStride], 1u) == (uint32_t)a.items_per_seq - 1 ? 1u : 0u;
+  __syncthreads();
+  return s_last != 0;
+}
+
+// Exact top-k of the score row of b into idx[b]; leaves idx visible to other
+// workgroups of the kernel (device-coherent stores, completed) and resets the
+// sequence counter.
+__device__ __forceinline__ void select_item(const ScanArgs& a, int b, char* smem, int& q_of) {
+  q_of = -1;  // the select overwrites qhat
+  // Everything waiting on this sequence waits on this workgroup: let its
+  // waves issue ahead of the streaming waves that share the CU.
+  __builtin_amdgcn_s_setprio(3);
+  SelectSmem<kItemWaves>& sm = *reinterpret_cast<SelectSmem<kItemWaves>*>(smem);
+  block_topk<kItemWaves, kSelKpt, true>(a.scores + (int64_t)b * a.N, a.N, a.k,
+                                        a.idx + (int64_t)b * a.k, sm);
+  wait_stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    counter_reset(&a.seq_ctr[b * kCtrStride]);
+    if (a.ready) store_flag(&a.ready[b * kCtrStride], 1u);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+__host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE) {
+  const size_t q = (size_t)scan_padded_chunks(nseg, LPR) * VE * sizeof(float);
+  const size_t s = sizeof(SelectSmem<kItemWaves>);
+  return q > s ? q : s;
+}
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;
+  int Hq, Hkv;
+  const void* kv;
+  const void* vv;
+  int64_t vbs, vts;
+  int N;
+  const int32_t* idx;
+  int k;
+  const void* kt;
+  const void* vt;
+  int64_t tbs, tts;
+  const int32_t* txt_len;
+  int Tmax;
+  float qscale;          // scale * log2(e)
+  int CT, CV;            // text and visual splits
+  float* part;           // [B][Hq][CT+CV][D+2]
+  uint32_t* comb_ctr;    // [B][Hkv] (stride kCtrStride), self-resetting
+  float* out;            // [B][Hq][D]
+  uint32_t* ready;       // [B] (stride kCtrStride; fused kernel only)
+  uint32_t* vis_done;    // [B] (stride kCtrStride) finished visual items (fused kernel only)
+};
+
+template <typename T, int D>
+struct AttnShape {
+  static constexpr int VE = Vec<T>::kElems;
+  static constexpr int LPE = D / VE;       // lanes per entry row of one head
+  static constexpr int EPW = kWave / LPE;  // entries per wave per step
+};
+
+template <int D, int G>
+__host__ __device__ constexpr size_t attn_smem_bytes() {
+  return (size_t)kItemWaves * G * (D + 2) * sizeof(float);
+}
+
+constexpr uint32_t kSpinLimit = 1u << 24;
+
+// Item (b, g, c).  wait: the visual indices are produced by this kernel;
+// poll ready[b] (bounded) and read them with device-coherent loads.
+template <typename T, int D, int G, int EPL>
+__device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c, bool wait,
+                                          char* smem) {
+  using S = AttnShape<T, D>;
+  constexpr int VE = S::VE, LPE = S::LPE, EPW = S::EPW;
+  constexpr int SE = kItemWaves * EPW * EPL;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int eg = lane / LPE, sub = lane % LPE, d0 = sub * VE;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const int C = a.CT + a.CV;
+
+  const bool text = c < a.CT;
+  int n_ent;  // entries of this split
+  int e0;     // first entry: text row or position in idx[b]
+  if (text) {
+    int tl = a.txt_len ? a.txt_len[b] : 0;
+    tl = tl < 0 ? 0 : (tl > a.Tmax ? a.Tmax : tl);
+    e0 = c * SE;
+    n_ent = tl - e0;
+  } else {
+    e0 = (c - a.CT) * SE;
+    n_ent = a.k - e0;
+  }
+  n_ent = n_ent < 0 ? 0 : (n_ent > SE ? SE : n_ent);
+
+  Vec<T> qx[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) qx[i].load(q + ((int64_t)b * a.Hq + g * G + i) * D + d0);
+
+  // The sequence's text or visual cache as one buffer; entry j of this lane
+  // is the head-g row of one token, at a 32-bit byte offset (kBufOob: none).
+  constexpr int ES = (int)sizeof(T);
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  BufRsrc krs, vrs;
+  int64_t ts;
+  if (text) {
+    ts = a.tts;
+    const uint32_t ext = (uint32_t)(((int64_t)(a.Tmax > 0 ? a.Tmax - 1 : 0) * ts + row_elems) * ES);
+    krs = make_rsrc(reinterpret_cast<const char*>(a.kt) + (int64_t)b * a.tbs * ES, ext);
+    vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + (int64_t)b * a.tbs * ES, ext);
+  } else {
+    ts = a.vts;
+    const uint32_t ext = (uint32_t)(((int64_t)(a.N > 0 ? a.N - 1 : 0) * ts + row_elems) * ES);
+    krs = make_rsrc(reinterpret_cast<const char*>(a.kv) + (int64_t)b * a.vbs * ES, ext);
+    vrs = make_rsrc(reinterpret_cast<const char*>(a.vv) + (int64_t)b * a.vbs * ES, ext);
+  }
+  const uint32_t head_off = (uint32_t)((g * D + d0) * ES);
+  uint32_t off[EPL];
+  if (text) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = (j * kItemWaves + wave) * EPW + eg;
+      off[j] = e < n_ent ? (uint32_t)((e0 + e) * ts * ES) + head_off : kBufOob;
+    }
+  } else {
+    if (wait && n_ent > 0) {
+      if (tid == 0) {
+        uint32_t n = 0;
+        while (load_flag(&a.ready[b * kCtrStride]) == 0u && ++n < kSpinLimit)
+          __builtin_amdgcn_s_sleep(8);
+      }
+      __syncthreads();
+    }
+    const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
+    int tok[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = (j * kItemWaves + wave) * EPW + eg;
+      tok[j] = -1;
+      if (e < n_ent) tok[j] = wait ? load_shared_dev_i32(ib + e) : ib[e];
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int t = tok[j];  // indices outside [0, N) are skipped
+      off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
+    }
+  }
+
+  Vec<T> kx[EPL], vx[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    kx[j].template load_buf<kCacheDefault>(krs, off[j], 0u);
+    vx[j].template load_buf<kCacheDefault>(vrs, off[j], 0u);
+  }
+
+  float qv[G][VE];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    qx[i].to_f32(qv[i]);
+#pragma unroll
+    for (int v = 0; v < VE; ++v) qv[i][v] *= a.qscale;
+  }
+
+  float m[G], l[G], acc[G][VE];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int v = 0; v < VE; ++v) acc[i][v] = 0.f;
+  }
+
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    float kf[VE], vf[VE];
+    kx[j].to_f32(kf);
+    vx[j].to_f32(vf);
+    float z[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
+      z[i] = group_sum<LPE>(s);
+    }
+    if (off[j] != kBufOob) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float mn = fmaxf(m[i], z[i]);
+        const float al = fast_exp2(m[i] - mn);  // m = -inf -> 0
+        const float p = fast_exp2(z[i] - mn);
+        l[i] = l[i] * al + p;
+#pragma unroll
+        for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
+        m[i] = mn;
+      }
+    }
+  }
+
+  // Merge the EPW lane groups of this wave.
+#pragma unroll
+  for (int off = LPE; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float mo = __shfl_xor(m[i], off, kWave);
+      const float lo = __shfl_xor(l[i], off, kWave);
+      const float mn = fmaxf(m[i], mo);
+      const float al = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
+      const float bo = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
+      l[i] = l[i] * al + lo * bo;
+#pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        const float ao = __shfl_xor(acc[i][v], off, kWave);
+        acc[i][v] = acc[i][v] * al + ao * bo;
+      }
+      m[i] = mn;
+    }
+  }
+
+  // Merge the waves through LDS: per wave and head, acc[D] then (m, l).
+  float* s_w = reinterpret_cast<float*>(smem);
+  auto slot = [&](int w, int i) { return s_w + ((int64_t)w * G + i) * (D + 2); };
+  if (eg == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float* sp = slot(wave, i);
+#pragma unroll
+      for (int v = 0; v < VE; ++v) sp[d0 + v] = acc[i][v];
+      if (sub == 0) {
+        sp[D] = m[i];
+        sp[D + 1] = l[i];
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t head0 = (int64_t)b * a.Hq + g * G;
+  for (int t = tid; t < G * D; t += kItemThreads) {
+    const int i = t / D, d = t % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kItemWaves; ++w) mm = fmaxf(mm, slot(w, i)[D]);
+    float ll = 0.f, aa = 0.f;
+#pragma unroll
+    for (int w = 0; w < kItemWaves; ++w) {
+      const float mw = slot(w, i)[D];
+      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mm);
+      ll += slot(w, i)[D + 1] * f;
+      aa += slot(w, i)[d] * f;
+    }
+    if (C == 1) {
+      a.out[(head0 + i) * D + d] = ll > 0.f ? aa / ll : 0.f;
+    } else {
+      float* pp = a.part + ((head0 + i) * C + c) * (D + 2);
+      store_shared_dev(pp + d, aa);
+      if (d == 0) {
+        store_shared_dev(pp + D, mm);
+        store_shared_dev(pp + D + 1, ll);
+      }
+    }
+  }
+  if (C == 1) return;
+
+  __shared__ uint32_t s_comb;
+  wait_stores_complete();
+  __syncthreads();
+  uint32_t* ctr = a.comb_ctr + ((int64_t)b * a.Hkv + g) * kCtrStride;
+  if (tid == 0) s_comb = counter_add(ctr, 1u) == (uint32_t)C - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_comb) return;
+
+  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c
+  for (int t = tid; t < G * D; t += kItemThreads) {
+    const int i = t / D, d = t % D;
+    const float* pp = a.part + (head0 + i) * C * (D + 2);
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, load_shared_dev(pp + cc * (D + 2) + D));
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int cc = 0; cc < C; ++cc) {
+        const float mc = load_shared_dev(pp + cc * (D + 2) + D);
+        const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+        num = fmaf(f, load_shared_dev(pp + cc * (D + 2) + d), num);
+        den = fmaf(f, load_shared_dev(pp + cc * (D + 2) + D + 1), den);
+      }
+    }
+    a.out[(head0 + i) * D + d] = den > 0.f ? num / den : 0.f;
+  }
+  if (tid == 0) counter_reset(ctr);
+}
+
+// Entries per split for (dtype, D, EPL).
+__host__ inline int attn_split_entries(int VE, int D, int EPL) {
+  return kItemWaves * (kWave / (D / VE)) * EPL;
+}
+
+}  // namespace sv

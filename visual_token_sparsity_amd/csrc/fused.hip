@@ -1,0 +1,166 @@
+// One decode layer in one launch: relevance scan, exact top-k, sparse
+// attention over the selected visual entries plus the text entries, and the
+// split combine (SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
+//
+// Work order.  Workgroup i runs item i: every scan item first, then the text
+// attention items (they need no selection), then the visual attention items.
+// The last scan item of a sequence runs its top-k and raises ready[b]; a
+// visual item of sequence b polls ready[b] (bounded) before it reads idx[b].
+// Each XCD dispatches its share of the grid in increasing order, so every
+// scan item a visual item can wait on has been dispatched before it; scan
+// items never wait.  No atomic ticket: same-address atomics from thousands
+// of workgroups serialise in the memory system.
+//
+// Control words (one 128-byte line each): seq_ctr[b] counts finished scan
+// items and is reset by the selecting workgroup; comb_ctr[b,g] counts
+// finished splits and is reset by the combining one; vis_done[b] counts
+// visual items past their wait, and the last one lowers ready[b] again.  The
+// control block is therefore zero after every launch.
+#include "decode_items.h"
+
+namespace sv {
+
+struct FusedCtl {
+  uint32_t scan_items, text_items, total;
+  uint32_t* vis_done;
+};
+
+template <typename T, int D, int G, int EPL>
+__global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnArgs aa,
+                                                             FusedCtl ctl) {
+  extern __shared__ __align__(16) char smem[];
+  const uint32_t t = blockIdx.x;
+  if (t < ctl.scan_items) {
+    int q_of = -1;
+    const int b = t / sa.items_per_seq;
+    if (scan_item<T>(sa, b, t % sa.items_per_seq, smem, q_of)) select_item(sa, b, smem, q_of);
+    return;
+  }
+  uint32_t u = t - ctl.scan_items;
+  const bool text = u < ctl.text_items;
+  int per = aa.CT, c0 = 0;
+  if (!text) {
+    u -= ctl.text_items;
+    per = aa.CV;
+    c0 = aa.CT;
+  }
+  const int b = u / (per * aa.Hkv);
+  const int g = (u / per) % aa.Hkv;
+  attn_item<T, D, G, EPL>(aa, b, g, c0 + u % per, !text, smem);
+  if (!text && threadIdx.x == 0) {
+    uint32_t* vd = ctl.vis_done + b * kCtrStride;
+    if (counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1) {
+      store_flag(aa.ready + b * kCtrStride, 0u);
+      counter_reset(vd);
+    }
+  }
+}
+
+template <typename T, int D, int G, int EPL>
+static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
+                           hipStream_t st) {
+  const int VE = Vec<T>::kElems;
+  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE);
+  if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
+  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
+                     sa, aa, ctl);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+static hipError_t fused_epl(int epl, const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
+                            hipStream_t st) {
+  switch (epl) {
+    case 1: return fused_go<T, D, G, 1>(sa, aa, ctl, st);
+    case 2: return fused_go<T, D, G, 2>(sa, aa, ctl, st);
+    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, st);
+    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
+                          const FusedCtl& ctl, hipStream_t st) {
+  switch (G) {
+    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, st);
+    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, st);
+    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, st);
+    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, st);
+    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, st);
+    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, st);
+    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, st);
+    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
+  const int VE = f.dtype == 1 ? 8 : 4;
+  const int G = f.Hq / f.Hkv;
+  ScanArgs sa{};
+  sa.q = f.q;
+  sa.Tq = 1;
+  sa.Hq = f.Hq;
+  sa.G = G;
+  sa.kv = f.k_vis;
+  sa.bstride = f.vbs;
+  sa.tstride = f.vts;
+  sa.N = f.N;
+  sa.D = f.D;
+  sa.C = f.Hkv * f.D / VE;
+  scan_geometry(sa.C, &sa.nseg, &sa.LPR);
+  sa.rows_per_item = f.rows_per_item > 0 ? f.rows_per_item
+                                         : scan_rows_per_item(f.B, f.N, sa.LPR, sa.nseg);
+  sa.items_per_seq = (f.N + sa.rows_per_item - 1) / sa.rows_per_item;
+  sa.scores = f.scores;
+  sa.k = f.k;
+  sa.idx = f.idx;
+  sa.seq_ctr = f.seq_ctr;
+  sa.ready = f.ready;
+
+  AttnPlan p = attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax, kAttnTargetItems);
+  if (f.epl > 0) {
+    p.EPL = f.epl;
+    p.SE = attn_split_entries(VE, f.D, f.epl);
+    p.CT = (f.Tmax + p.SE - 1) / p.SE;
+    p.CV = (f.k + p.SE - 1) / p.SE;
+  }
+  AttnArgs aa{};
+  aa.q = f.q;
+  aa.Hq = f.Hq;
+  aa.Hkv = f.Hkv;
+  aa.kv = f.k_vis;
+  aa.vv = f.v_vis;
+  aa.vbs = f.vbs;
+  aa.vts = f.vts;
+  aa.N = f.N;
+  aa.idx = f.idx;
+  aa.k = f.k;
+  aa.kt = f.k_txt;
+  aa.vt = f.v_txt;
+  aa.tbs = f.tbs;
+  aa.tts = f.tts;
+  aa.txt_len = f.txt_len;
+  aa.Tmax = f.Tmax;
+  aa.qscale = f.scale * 1.4426950408889634f;
+  aa.CT = p.CT;
+  aa.CV = p.CV;
+  aa.part = f.part;
+  aa.comb_ctr = f.comb_ctr;
+  aa.out = f.out;
+  aa.ready = f.ready;
+
+  FusedCtl ctl{};
+  ctl.vis_done = f.vis_done;
+  ctl.scan_items = (uint32_t)sa.items_per_seq * f.B;
+  ctl.text_items = (uint32_t)p.CT * f.Hkv * f.B;
+  ctl.total = ctl.scan_items + ctl.text_items + (uint32_t)p.CV * f.Hkv * f.B;
+  if (f.dtype == 1)
+    return f.D == 128 ? fused_g<bf16_t, 128>(G, p.EPL, sa, aa, ctl, st)
+                      : fused_g<bf16_t, 64>(G, p.EPL, sa, aa, ctl, st);
+  return f.D == 128 ? fused_g<float, 128>(G, p.EPL, sa, aa, ctl, st)
+                    : fused_g<float, 64>(G, p.EPL, sa, aa, ctl, st);
+}
+
+}  // namespace sv

@@ -1,196 +1,86 @@
-// Query-aware retrieval for the decode stage: relevance scan + exact top-k,
-// in one kernel.
+// Query-aware retrieval for the decode stage: relevance scan + exact top-k in
+// one kernel (SparseVILA velog summary, Sec. 3.2, Query-Aware Token
+// Selection; xllm-io review, core formulas: TopK(Query . KV_Cache, k)).
 //
-// SparseVILA velog summary, Sec. 3.2 (Query-Aware Token Selection): the
-// current query scores every cached vision token and only the top-k are
-// activated.  xllm-io review, core formulas: TopK(Query . KV_Cache, k).
-//
-// Scan.  s[b,t] = sum_g qhat[b,g,:] . K[b,t,g,:] where qhat[b,g] is the sum of
-// the query over the Tq query tokens and the G query heads sharing KV head g.
-// The sum is linear, so summing the queries first gives the same score as
-// summing per-head logits.  Decode is HBM-bound: every retained key row is
-// read exactly once as contiguous 16-byte vectors.  A lane group of LPR lanes
-// covers one token row (Hkv*D elements); each wave walks a contiguous run of
-// rows with the next rows' loads already in flight, and the key loads of the
-// first rows are issued before the query is summed.
-//
-// Select.  Every workgroup of sequence b publishes its scores with
-// device-coherent stores, waits for them to complete and bumps a counter; the
-// last one runs the exact top-k of the whole score row (select.h, reading
-// with device-coherent loads) and resets the counter to zero, so the
-// workspace is ready for the next call.
-#include "common.h"
-#include "select.h"
+// Workgroup (i, b) runs scan item i of sequence b (decode_items.h).  With
+// k > 0 every item publishes its scores with device-coherent stores and bumps
+// a per-sequence counter; the last item of a sequence runs the exact top-k of
+// the whole score row and resets the counter, so the workspace is ready for
+// the next call.  Also: the top-k of independent rows (per-frame pruning).
+#include "decode_items.h"
 
 namespace sv {
 
-constexpr int kScanWaves = 4;
-constexpr int kSelKpt = 8;  // keys per thread kept in registers by the select
-
-template <typename T, int CPL, int LPR>
-__global__ __launch_bounds__(kScanWaves* kWave) void retrieve_kernel(
-    const T* __restrict__ q, int Tq, int Hq, int G, const T* __restrict__ kv, int64_t bstride,
-    int64_t tstride, int N, int D, int rows_per_wave, float* __restrict__ scores, int k,
-    int32_t* __restrict__ idx_out, uint32_t* __restrict__ counters) {
-  constexpr int VE = Vec<T>::kElems;
-  constexpr int RPW = kWave / LPR;  // rows per wave per step
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int b = blockIdx.y;
-  const int sub = lane % LPR;
-  const int rsub = lane / LPR;
-
-  const T* base = kv + (int64_t)b * bstride;
-  float* srow = scores + (int64_t)b * N;
-  const int r_begin = (blockIdx.x * kScanWaves + wave) * rows_per_wave;
-  int r_end = r_begin + rows_per_wave;
-  r_end = r_end < N ? r_end : N;
-
-  // First rows' keys in flight before anything else.
-  Vec<T> nxt[CPL];
-  {
-    const int r = r_begin + rsub;
-    if (r < r_end) {
-      const T* row = base + (int64_t)r * tstride;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) nxt[j].load_stream(row + (sub + j * LPR) * VE);
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) nxt[j].zero();
-    }
-  }
-
-  // qhat for this lane's chunks: chunk j covers row elements [(sub + j*LPR)*VE, +VE).
-  float qh[CPL][VE];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int e0 = (sub + j * LPR) * VE;
-    const int g = e0 / D, d0 = e0 % D;
-#pragma unroll
-    for (int v = 0; v < VE; ++v) qh[j][v] = 0.f;
-    for (int tau = 0; tau < Tq; ++tau) {
-      for (int i = 0; i < G; ++i) {
-        Vec<T> x;
-        x.load(q + ((int64_t)(b * Tq + tau) * Hq + g * G + i) * D + d0);
-        float f[VE];
-        x.to_f32(f);
-#pragma unroll
-        for (int v = 0; v < VE; ++v) qh[j][v] += f[v];
-      }
-    }
-  }
-
-  for (int r0 = r_begin; r0 < r_end; r0 += RPW) {
-    Vec<T> cur[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) cur[j] = nxt[j];
-    // Prefetch the next step's rows.
-    {
-      const int r = r0 + RPW + rsub;
-      if (r < r_end) {
-        const T* row = base + (int64_t)r * tstride;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) nxt[j].load_stream(row + (sub + j * LPR) * VE);
-      }
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      float f[VE];
-      cur[j].to_f32(f);
-#pragma unroll
-      for (int v = 0; v < VE; ++v) acc = fmaf(qh[j][v], f[v], acc);
-    }
-    acc = group_sum<LPR>(acc);
-    const int r = r0 + rsub;
-    if (r < r_end && sub == 0) {
-      if (k > 0)
-        store_shared_dev(srow + r, acc);  // read back by the selecting workgroup
-      else
-        srow[r] = acc;
-    }
-  }
-
-  if (k <= 0) return;
-  __shared__ SelectSmem<kScanWaves> sm;
-  __shared__ uint32_t s_last;
-  wait_stores_complete();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = counter_add(&counters[b], 1u) == gridDim.x - 1 ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  block_topk<kScanWaves, kSelKpt, true>(srow, N, k, idx_out + (int64_t)b * k, sm);
-  if (threadIdx.x == 0) counter_reset(&counters[b]);
-}
-
-template <typename T, int CPL, int LPR>
-static hipError_t retrieve_go(const void* q, int B, int Tq, int Hq, int G, const void* kv,
-                              int64_t bs, int64_t ts, int N, int D, float* scores, int k,
-                              int32_t* idx, uint32_t* counters, hipStream_t st) {
-  constexpr int RPW = kWave / LPR;
-  // About 16 resident waves per CU on 256 CUs; each wave walks a run of rows.
-  const long target_waves = 4096;
-  long waves_per_seq = (target_waves + B - 1) / B;
-  const long max_waves = (N + RPW - 1) / RPW;
-  if (waves_per_seq > max_waves) waves_per_seq = max_waves;
-  int rows_per_wave = (int)((N + waves_per_seq - 1) / waves_per_seq);
-  rows_per_wave = ((rows_per_wave + RPW - 1) / RPW) * RPW;
-  const int waves = (N + rows_per_wave - 1) / rows_per_wave;
-  const int blocks = (waves + kScanWaves - 1) / kScanWaves;
-  hipLaunchKernelGGL((retrieve_kernel<T, CPL, LPR>), dim3(blocks, B), dim3(kScanWaves * kWave), 0,
-                     st, (const T*)q, Tq, Hq, G, (const T*)kv, bs, ts, N, D, rows_per_wave,
-                     scores, k, idx, counters);
-  return hipGetLastError();
-}
-
 template <typename T>
-static hipError_t retrieve_dispatch(const void* q, int B, int Tq, int Hq, int G, const void* kv,
-                                    int64_t bs, int64_t ts, int N, int R, int D, float* scores,
-                                    int k, int32_t* idx, uint32_t* ctr, hipStream_t st) {
-  constexpr int VE = Vec<T>::kElems;
-  const int C = R / VE;  // 16-byte chunks per token row
-  // Each lane keeps CPL chunks of qhat; a row is covered by LPR = C / CPL lanes.
-  switch (C) {
-    case 8: return retrieve_go<T, 8, 1>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 16: return retrieve_go<T, 8, 2>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 32: return retrieve_go<T, 8, 4>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 64: return retrieve_go<T, 8, 8>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 128: return retrieve_go<T, 8, 16>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 256: return retrieve_go<T, 8, 32>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 512: return retrieve_go<T, 8, 64>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    case 1024: return retrieve_go<T, 16, 64>(q, B, Tq, Hq, G, kv, bs, ts, N, D, scores, k, idx, ctr, st);
-    default: return hipErrorInvalidValue;
-  }
+__global__ __launch_bounds__(kItemThreads) void scan_select_kernel(ScanArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  int q_of = -1;
+  const int b = blockIdx.y;
+  if (scan_item<T>(a, b, blockIdx.x, smem, q_of)) select_item(a, b, smem, q_of);
+}
+
+int scan_rows_per_item(int B, int N, int LPR, int nseg) {
+  // About 16 resident waves per CU on 256 CUs, each wave with a short run of
+  // rows (whole rows per wave when a row has several segments).
+  const long target_items = 1024;
+  long per_seq = (target_items + B - 1) / B;
+  const int rps = kWave / LPR;
+  const long min_rows = (long)kItemWaves * (nseg > 1 ? 1 : rps);
+  long rows = (N + per_seq - 1) / per_seq;
+  if (rows < min_rows) rows = min_rows;
+  rows = ((rows + min_rows - 1) / min_rows) * min_rows;
+  return (int)rows;
 }
 
 hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv, int64_t bstride,
                            int64_t tstride, int N, int Hkv, int D, int dtype, float* scores, int k,
-                           int32_t* idx_out, uint32_t* counters, hipStream_t stream) {
-  const int G = Hq / Hkv;
-  const int R = Hkv * D;
+                           int32_t* idx_out, uint32_t* counters, int rows_per_item,
+                           hipStream_t stream) {
+  const int VE = dtype == 1 ? 8 : 4;
+  ScanArgs a{};
+  a.q = q;
+  a.Tq = Tq;
+  a.Hq = Hq;
+  a.G = Hq / Hkv;
+  a.kv = kv;
+  a.bstride = bstride;
+  a.tstride = tstride;
+  a.N = N;
+  a.D = D;
+  a.C = Hkv * D / VE;
+  scan_geometry(a.C, &a.nseg, &a.LPR);
+  a.rows_per_item = rows_per_item > 0 ? rows_per_item : scan_rows_per_item(B, N, a.LPR, a.nseg);
+  a.items_per_seq = (N + a.rows_per_item - 1) / a.rows_per_item;
+  a.scores = scores;
+  a.k = k;
+  a.idx = idx_out;
+  a.seq_ctr = counters;
+  a.ready = nullptr;
+  const size_t lds = scan_smem_bytes(a.nseg, a.LPR, VE);
+  const dim3 grid(a.items_per_seq, B);
   if (dtype == 1)
-    return retrieve_dispatch<bf16_t>(q, B, Tq, Hq, G, kv, bstride, tstride, N, R, D, scores, k,
-                                     idx_out, counters, stream);
-  return retrieve_dispatch<float>(q, B, Tq, Hq, G, kv, bstride, tstride, N, R, D, scores, k,
-                                  idx_out, counters, stream);
+    hipLaunchKernelGGL(scan_select_kernel<bf16_t>, grid, dim3(kItemThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(scan_select_kernel<float>, grid, dim3(kItemThreads), lds, stream, a);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
 // Top-k of independent rows, one workgroup per row (used for per-frame pruning)
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kScanWaves* kWave) void topk_rows_kernel(const float* __restrict__ vals,
-                                                                    int64_t row_stride, int N,
-                                                                    int k, int32_t* __restrict__ out) {
-  __shared__ SelectSmem<kScanWaves> sm;
+__global__ __launch_bounds__(kItemThreads) void topk_rows_kernel(const float* __restrict__ vals,
+                                                               int64_t row_stride, int N, int k,
+                                                               int32_t* __restrict__ out) {
+  __shared__ SelectSmem<kItemWaves> sm;
   if (k <= 0) return;
-  block_topk<kScanWaves, kSelKpt, false>(vals + (int64_t)blockIdx.x * row_stride, N, k,
-                                  out + (int64_t)blockIdx.x * k, sm);
+  block_topk<kItemWaves, kSelKpt, false>(vals + (int64_t)blockIdx.x * row_stride, N, k,
+                                         out + (int64_t)blockIdx.x * k, sm);
 }
 
 hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int N, int k,
                             int32_t* out, hipStream_t stream) {
   if (k <= 0 || rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kScanWaves * kWave), 0, stream, vals,
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kItemThreads), 0, stream, vals,
                      row_stride, N, k, out);
   return hipGetLastError();
 }

@@ -671,17 +671,6 @@ static size_t colstat_lds_bytes(int tpw, int D) {
          32;
 }
 
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int D, int TPW>
 static hipError_t colstat_go(const void* q, const void* k, int FH, int N, float c2, float* colsum,
                              hipStream_t st) {
@@ -693,7 +682,7 @@ static hipError_t colstat_go(const void* q, const void* k, int FH, int N, float 
     (void)hipGetLastError();
     attr_set = true;
   }
-  int grid = cu_count();
+  int grid = device_cu_count();
   if (grid > FH) grid = FH;
   hipLaunchKernelGGL((salience_colstat_kernel<D, TPW>), dim3(grid), dim3(kColWaves * kWave), lds, st,
                      (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum);
