@@ -3,20 +3,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one decode step of the whole batch through every layer: for each
-layer, query-aware retrieval (relevance scan + top-k select) followed by
-sparse decode attention over the selected visual entries plus the text
-entries (split-K partials + combine).  The default workload is LLaVA-NeXT-7B
-shaped: 8 sequences, 32 layers x 32 heads, head dim 128, bf16, 1440 retained
-visual tokens, k = 360, 256 text entries.  All caches are resident in HBM
-before timing starts (7.1 GB, far above the 256 MB Infinity Cache, so every
-step streams from HBM).  The step's launches are captured once in a HIP
-graph and replayed.
+layer, query-aware retrieval (relevance scan + top-k select) and sparse
+decode attention over the selected visual entries plus the text entries
+(split-K partials + combine), all in one launch per layer
+(sv_retrieve_attend).  The default workload is LLaVA-NeXT-7B shaped: 8
+sequences, 32 layers x 32 heads, head dim 128, bf16, 1440 retained visual
+tokens, k = 360, 256 text entries.  All caches are resident in HBM before
+timing starts (7.1 GB, far above the 256 MB Infinity Cache, so every step
+streams from HBM).  The step's launches are captured once in a HIP graph and
+replayed.
 
 Printed: one JSON line with steps/s (whole job), algorithmic HBM GB/s, the
-roofline of the dominant kernel (the relevance scan, timed live with HIP
-events on the stream it runs on), the prefill salience workload (256 frames
-x 729 tokens, 16 heads, D = 72: tokens/s and MFMA utilisation), and the CPU
-oracle timed on a bounded sample of the same decode workload.
+roofline of the dominant kernel (the one-launch decode layer, timed live
+with HIP events over the timed region on the stream it runs on), the same
+step through the two-call path (sv_retrieve + sv_sparse_decode_attn) for
+comparison, the prefill salience workload (256 frames x 729 tokens, 16
+heads, D = 72: tokens/s and MFMA utilisation), and the CPU oracle timed on a
+bounded sample of the same decode workload.
 """
 from __future__ import annotations
 
@@ -50,7 +53,7 @@ def parse():
 
 
 def decode_bytes(w):
-    """Algorithmic HBM bytes of one step, and of one relevance-scan launch (one layer)."""
+    """Algorithmic HBM bytes of one step, and of one layer of the whole batch."""
     e = 2 if w.dtype.itemsize == 2 else 4
     row = w.Hkv * w.D * e
     q = w.Hq * w.D * e
@@ -58,7 +61,7 @@ def decode_bytes(w):
     select = w.N * 4 + w.k * 4                            # scores in, indices out
     attn = (w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4   # K,V of the attended rows
     per_seq_layer = scan + select + attn
-    return per_seq_layer * w.B * w.L, scan * w.B
+    return per_seq_layer * w.B * w.L, per_seq_layer * w.B
 
 
 def source_hash(*names):
@@ -149,35 +152,32 @@ def main():
               for l in range(w.L)]
     idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in range(w.L)]
     out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(w.L)]
-    scores = [torch.empty((w.B, w.N), dtype=torch.float32, device=dev) for _ in range(w.L)]
+    ws_f = sv.new_workspace(sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax), dev)
     ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
     ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
     torch.cuda.synchronize()
 
     def step():
         for l, d in enumerate(layers):
+            sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
+                               d["txt_len"], workspace=ws_f, out=out[l], idx_out=idx[l])
+
+    def step_two_call():
+        for l, d in enumerate(layers):
             sv.retrieve(d["q"], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
             sv.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
                                   d["txt_len"], workspace=ws_a, out=out[l])
-
-    def scan_only():
-        for l, d in enumerate(layers):
-            # k = 0: the scan kernel alone, scores written to scores[l]
-            sv.load().sv_retrieve(d["q"].data_ptr(), w.B, 1, w.Hq, d["k_vis"].data_ptr(),
-                                  d["k_vis"].stride(0), d["k_vis"].stride(1), w.N, w.Hkv, w.D,
-                                  sv.SV_BF16 if w.dtype == torch.bfloat16 else sv.SV_F32, 0, None,
-                                  scores[l].data_ptr(), ws_r.data_ptr(), ws_r.numel(),
-                                  torch.cuda.current_stream().cuda_stream)
 
     stream = torch.cuda.Stream(device=dev)      # default priority
     with torch.cuda.stream(stream):
         for _ in range(max(1, a.warmup)):
             step()
+            step_two_call()
         torch.cuda.synchronize()
         g_step = None if a.no_graph else capture(step, stream)
-        g_scan = None if a.no_graph else capture(scan_only, stream)
+        g_two = None if a.no_graph else capture(step_two_call, stream)
         run_step = g_step.replay if g_step is not None else step
-        run_scan = g_scan.replay if g_scan is not None else scan_only
+        run_two = g_two.replay if g_two is not None else step_two_call
         for _ in range(a.warmup):
             run_step()
         # ---------------------------------------------------- timed region: exactly K steps
@@ -185,19 +185,20 @@ def main():
         t0 = time.perf_counter()
         secs = gpu_time(run_step, a.steps, stream)
         wall = time.perf_counter() - t0
-        # ---------------------------------------------------- dominant kernel: relevance scan
+        # ---------------------------------------------------- the two-call path, for comparison
         for _ in range(3):
-            run_scan()
-        scan_reps = max(5, a.steps // 2)
-        scan_secs = gpu_time(run_scan, scan_reps, stream)
-    scan_avg = scan_secs / (scan_reps * w.L)
+            run_two()
+        two_reps = max(5, a.steps // 2)
+        two_secs = gpu_time(run_two, two_reps, stream) / two_reps
 
-    step_bytes, scan_launch_bytes = decode_bytes(w)
+    step_bytes, layer_bytes = decode_bytes(w)
     steps_per_s = a.steps / secs
     gbs = step_bytes * steps_per_s / 1e9
-    scan_gbs = scan_launch_bytes / scan_avg / 1e9
-    traffic = committed_traffic(f"scan_{w.name}", source_hash("retrieve.hip", "common.h"))
-
+    # One launch per layer: the average launch duration over the timed region.
+    layer_avg = secs / (a.steps * w.L)
+    layer_gbs = layer_bytes / layer_avg / 1e9
+    traffic = committed_traffic(f"fused_{w.name}",
+                                source_hash("fused.hip", "decode_items.h", "select.h", "common.h"))
     dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     res = {
         "metric": "decode steps/s (retrieval + sparse attention, all layers, whole batch)",
@@ -219,11 +220,15 @@ def main():
         "hbm_gbs_algorithmic": round(gbs, 1),
         "hbm_frac_algorithmic": round(gbs / HBM_PEAK_GBS, 4),
         "step_bytes_algorithmic": step_bytes,
-        "roofline": {"kernel": "scan_kernel (relevance scan, one layer x batch per launch)",
-                     "bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": scan_launch_bytes,
-                     "avg_launch_us": round(scan_avg * 1e6, 3)},
+        "roofline": {"kernel": "fused_kernel (one decode layer of the whole batch per launch: "
+                               "scan + select + sparse attention + combine)",
+                     "bound": "hbm", "achieved": round(layer_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": layer_bytes,
+                     "avg_launch_us": round(layer_avg * 1e6, 3)},
+        "two_call_path": {"ms_per_step": round(two_secs * 1e3, 4),
+                          "value": round(1.0 / two_secs, 2), "unit": "steps/s",
+                          "launches_per_layer": 2},
         "wall_s_timed": round(wall, 4),
     }
 

@@ -168,10 +168,12 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq,
  *  workspace  at least sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax)
  *             bytes, 256-byte aligned, ZERO-FILLED before its first use.  It
  *             holds the scores, the split partials and a control block
- *             (work ticket, completion counters, per-sequence ready flags);
- *             every call leaves the control block zero again, so the
- *             workspace can be reused and the call captured in a HIP graph.
- *             Two calls that share a workspace must not run concurrently.
+ *             (completion counters, per-sequence ready flags); every call
+ *             leaves it ready for the next call with the same B, N, Hq, Hkv,
+ *             D, k and Tmax, so it can be reused as is and the call captured
+ *             in a HIP graph.  For other sizes, zero it again (or use
+ *             another).  Two calls that share a workspace must not run
+ *             concurrently.
  * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hq/Hkv in 1..8;
  * Hkv*D <= 8192 (bf16) or <= 4096 (fp32); B <= 65535.
  * Errors: SV_EINVAL (k < 1, k > N, Hq % Hkv != 0, NULL required pointer,

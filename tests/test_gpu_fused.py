@@ -3,8 +3,9 @@
 Against the fp64 oracle: the selected set (index-set rule of tests/accept.py)
 and the attention output over the GPU's own selection (2e-3 max-abs-relative
 per (b, h)).  Against the two-call path (sv_retrieve then
-sv_sparse_decode_attn): identical indices and bit-identical outputs, since
-both run the same work items with the same split plan.
+sv_sparse_decode_attn): identical scores and indices (the same scan and
+select arithmetic) and outputs equal up to the summation order of the
+attention splits (the fused launch uses finer splits).
 """
 import numpy as np
 import pytest
@@ -78,7 +79,8 @@ def test_retrieve_attend_parity(name, wl, ov):
         for b in range(w.B):
             assert set(d["planted"][b].tolist()) <= set(idx[b].cpu().tolist())
 
-    # The two-call path runs the same items with the same plan: identical results.
+    # The two-call path: the same scores and selection, the same attention up
+    # to the order of the split merge.
     idx2, sc2 = sv.retrieve(g["q"], g["k_vis"], w.k, scores=True)
     out2 = sv.sparse_decode_attn(g["q"], g["k_vis"], g["v_vis"], idx2,
                                  g["k_txt"] if w.Tmax else None, g["v_txt"] if w.Tmax else None,
@@ -86,7 +88,8 @@ def test_retrieve_attend_parity(name, wl, ov):
     torch.cuda.synchronize()
     assert torch.equal(sc, sc2)
     assert torch.equal(idx, idx2)
-    assert torch.equal(out, out2)
+    scale = out2.abs().amax(dim=-1, keepdim=True) + 1e-30
+    assert ((out - out2).abs() / scale).max().item() < 1e-5
 
 
 def test_retrieve_attend_strided_caches():

@@ -123,10 +123,11 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
 
 // ---------------------------------------------------------------- attention
 // Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+2) fp32][counters B*Hkv uint32].
-static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax) {
+static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax,
+                                 long target = sv::kAttnTargetItems) {
   size_t best = 0;
   for (int ve = 4; ve <= 8; ve += 4) {
-    const sv::AttnPlan p = sv::attn_plan(B, Hkv, D, ve, k, Tmax, sv::kAttnTargetItems);
+    const sv::AttnPlan p = sv::attn_plan(B, Hkv, D, ve, k, Tmax, target);
     const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * (D + 2) * sizeof(float);
     if (bytes > best) best = bytes;
   }
@@ -184,13 +185,16 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
 
 // ---------------------------------------------------------------- fused layer
 // Workspace of sv_retrieve_attend:
-//   [scores B*N fp32][partials][control: seq B | ready B | vis_done B | comb B*Hkv],
-// every control word on its own 128-byte line.
+//   [scores B*N][partials][control: seq B | ready B | vis_done B | comb B*Hkv],
+// every control word on its own 128-byte line.  The score words are zero
+// between launches (short rows: the kernel stores them complemented and
+// zeroes them once read).
 static size_t fused_ctl_bytes(int B, int Hkv) { return ctr_bytes((size_t)B * (3 + Hkv)); }
 
 size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return 256;
-  return retrieve_scores_bytes(B, N) + attn_partial_bytes(B, Hq, Hkv, D, k, Tmax) +
+  return retrieve_scores_bytes(B, N) +
+         attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, sv::kFusedAttnTargetItems) +
          fused_ctl_bytes(B, Hkv);
 }
 
@@ -251,11 +255,12 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
   f.Tmax = Tmax;
   f.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   f.idx = idx_out;
-  f.scores = scores_out ? scores_out : (float*)ws;
+  f.scores_ws = (float*)ws;
+  f.scores_out = scores_out;
   f.out = out;
   ws += retrieve_scores_bytes(B, N);
   f.part = (float*)ws;
-  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax);
+  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, sv::kFusedAttnTargetItems);
   uint32_t* ctl = (uint32_t*)ws;
   f.seq_ctr = ctl;
   f.ready = f.seq_ctr + (size_t)B * sv::kCtrStride;

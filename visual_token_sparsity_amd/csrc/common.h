@@ -197,7 +197,8 @@ hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int
 struct AttnPlan {
   int EPL, SE, CT, CV;
 };
-constexpr long kAttnTargetItems = 1024;
+constexpr long kAttnTargetItems = 1024;       // standalone attention launch
+constexpr long kFusedAttnTargetItems = 2048;  // fused layer: smaller splits start sooner
 AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_items);
 
 hipError_t launch_attn(const void* q, int B, int Hq, const void* kv, const void* vv,
@@ -221,7 +222,8 @@ struct FusedLaunch {
   int Tmax;
   float scale;
   int32_t* idx;        // [B][k]
-  float* scores;       // [B][N]
+  float* scores_ws;    // [B][N] in the workspace, zero before the launch
+  float* scores_out;   // [B][N] caller's copy of the scores, may be null
   float* out;          // [B][Hq][D]
   float* part;         // partials
   // Control words, each on its own 128-byte line (stride 32 words), zero

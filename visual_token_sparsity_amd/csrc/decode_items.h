@@ -37,6 +37,7 @@ constexpr int kItemThreads = kItemWaves * kWave;
 constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment
 constexpr int kScanSegChunks = 512;
 constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
+constexpr uint32_t kSpinLimit = 1u << 24;  // bound of every in-kernel wait
 
 // ---------------------------------------------------------------- scan
 struct ScanArgs {
@@ -53,6 +54,10 @@ struct ScanArgs {
   int32_t* idx;              // [B][k]
   uint32_t* seq_ctr;         // [B] (stride kCtrStride) finished scan items, self-resetting
   uint32_t* ready;           // [B] (stride kCtrStride) selection published (fused kernel only)
+  // Fused kernel, rows that fit the select's registers: scores are stored as
+  // the complement of their bits (a zero word: not written yet) and a select
+  // item polls the row; no counters.
+  bool encode;
 };
 
 // Chunks of qhat kept in LDS (zero past C).
@@ -206,7 +211,10 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
       acc = 0.f;
       if (sub == 0 && u < nunits) {
         const int row = wr0 + u / nseg;
-        if (coherent)
+        if (a.encode)
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + row, ~__float_as_uint(s),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else if (coherent)
           store_shared_dev(srow + row, s);  // read back by the selecting workgroup
         else
           srow[row] = s;
@@ -214,7 +222,7 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
     }
   }
 
-  if (!coherent) return false;
+  if (!coherent || a.encode) return false;
   __shared__ uint32_t s_last;
   wait_stores_complete();
   __syncthreads();
@@ -233,8 +241,11 @@ __device__ __forceinline__ void select_item(const ScanArgs& a, int b, char* smem
   // waves issue ahead of the streaming waves that share the CU.
   __builtin_amdgcn_s_setprio(3);
   SelectSmem<kItemWaves>& sm = *reinterpret_cast<SelectSmem<kItemWaves>*>(smem);
-  block_topk<kItemWaves, kSelKpt, true>(a.scores + (int64_t)b * a.N, a.N, a.k,
-                                        a.idx + (int64_t)b * a.k, sm);
+  const float* srow = a.scores + (int64_t)b * a.N;
+  if (a.N <= kItemThreads * kSelKpt)
+    block_topk<kItemWaves, kSelKpt, true, true>(srow, a.N, a.k, a.idx + (int64_t)b * a.k, sm);
+  else
+    block_topk<kItemWaves, kSelKpt, true, false>(srow, a.N, a.k, a.idx + (int64_t)b * a.k, sm);
   wait_stores_complete();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -242,6 +253,56 @@ __device__ __forceinline__ void select_item(const ScanArgs& a, int b, char* smem
     if (a.ready) store_flag(&a.ready[b * kCtrStride], 1u);
   }
   __builtin_amdgcn_s_setprio(0);
+}
+
+// Select item of the fused kernel (rows of at most kItemThreads*kSelKpt
+// scores, stored complemented by the scan items): polls the score row of b
+// until every word is written (completion detection and loading the keys
+// are one and the same read), selects the top-k into idx[b], raises
+// ready[b], then restores the words to zero for the next launch and
+// optionally writes the decoded scores.
+__device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float* scores_out,
+                                                 char* smem) {
+  constexpr int NW = kItemWaves, KPT = kSelKpt;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int N = a.N;
+  const int seg = ((N + NW * kWave - 1) / (NW * kWave)) * kWave;
+  const int chunks = seg / kWave;
+  const int base = wave * seg + lane;
+  uint32_t* words = reinterpret_cast<uint32_t*>(a.scores) + (int64_t)b * N;
+  uint32_t w[KPT];
+  for (uint32_t n = 0;; ++n) {
+    bool missing = false;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = base + i * kWave;
+      w[i] = (i < chunks && e < N)
+                 ? __hip_atomic_load(words + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 1u;
+      missing |= w[i] == 0u;
+    }
+    if (!__syncthreads_or(missing) || n + 1 >= kSpinLimit) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) w[i] = float_key(__uint_as_float(~w[i]));
+  SelectSmem<NW>& sm = *reinterpret_cast<SelectSmem<NW>*>(smem);
+  block_topk<NW, KPT, true, true>(nullptr, N, a.k, a.idx + (int64_t)b * a.k, sm, w);
+  wait_stores_complete();
+  __syncthreads();
+  if (tid == 0) store_flag(&a.ready[b * kCtrStride], 1u);
+  __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = base + i * kWave;
+    if (i < chunks && e < N) {
+      words[e] = 0u;  // ready for the next launch
+      if (scores_out) scores_out[(int64_t)b * N + e] = key_to_float(w[i]);
+    }
+  }
 }
 
 __host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE) {
@@ -285,8 +346,6 @@ template <int D, int G>
 __host__ __device__ constexpr size_t attn_smem_bytes() {
   return (size_t)kItemWaves * G * (D + 2) * sizeof(float);
 }
-
-constexpr uint32_t kSpinLimit = 1u << 24;
 
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
 // poll ready[b] (bounded) and read them with device-coherent loads.

@@ -2,27 +2,39 @@
 // attention over the selected visual entries plus the text entries, and the
 // split combine (SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
 //
-// Work order.  Workgroup i runs item i: every scan item first, then the text
-// attention items (they need no selection), then the visual attention items.
-// The last scan item of a sequence runs its top-k and raises ready[b]; a
-// visual item of sequence b polls ready[b] (bounded) before it reads idx[b].
-// Each XCD dispatches its share of the grid in increasing order, so every
-// scan item a visual item can wait on has been dispatched before it; scan
-// items never wait.  No atomic ticket: same-address atomics from thousands
-// of workgroups serialise in the memory system.
+// Work order.  Workgroup i runs item i, in this order:
+//   for each sequence b: its scan items, then (rows that fit the select's
+//     registers) its select item;
+//   the text attention items (they need no selection);
+//   the visual attention items, sequence by sequence (each polls ready[b]).
+// There are more scan items than resident workgroups, so the sequences
+// finish their scans one after another and each select overlaps the scans
+// of the sequences behind it.  Scan items store each score complemented (a
+// zero word: not written yet) and never wait; the select item of b polls
+// the score row until it is complete, which also loads its keys.  Longer
+// rows use counters instead: every scan item of b bumps seq_ctr[b] after
+// its stores have completed, and the last one selects.
 //
-// Control words (one 128-byte line each): seq_ctr[b] counts finished scan
-// items and is reset by the selecting workgroup; comb_ctr[b,g] counts
-// finished splits and is reset by the combining one; vis_done[b] counts
-// visual items past their wait, and the last one lowers ready[b] again.  The
-// control block is therefore zero after every launch.
+// Each XCD dispatches its share of the grid in increasing order, so whatever
+// a waiting workgroup waits on has been dispatched before it, and scan items
+// never wait.  All waits are bounded.  No atomic ticket: same-address
+// atomics from thousands of workgroups serialise in the memory system.
+//
+// Control words (one 128-byte line each) are zero after every launch:
+// seq_ctr[b] is reset by the selecting workgroup, comb_ctr[b,g] by the
+// combining one, and vis_done[b] counts visual items past their wait, the
+// last of which lowers ready[b] again.  Complemented scores are zeroed by
+// the select item that read them.
 #include "decode_items.h"
 
 namespace sv {
 
 struct FusedCtl {
-  uint32_t scan_items, text_items, total;
+  uint32_t per_seq;    // items per sequence in the first block: scan items (+1 select item)
+  uint32_t seq_end;    // B * per_seq
+  uint32_t text_end, total;
   uint32_t* vis_done;
+  float* scores_out;   // decoded scores (polling mode), may be null
 };
 
 template <typename T, int D, int G, int EPL>
@@ -30,23 +42,23 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
                                                              FusedCtl ctl) {
   extern __shared__ __align__(16) char smem[];
   const uint32_t t = blockIdx.x;
-  if (t < ctl.scan_items) {
+  if (t < ctl.seq_end) {
+    const int b = t / ctl.per_seq;
+    const int j = t % ctl.per_seq;
     int q_of = -1;
-    const int b = t / sa.items_per_seq;
-    if (scan_item<T>(sa, b, t % sa.items_per_seq, smem, q_of)) select_item(sa, b, smem, q_of);
+    if (j < sa.items_per_seq) {
+      if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+    } else {
+      select_poll_item(sa, b, ctl.scores_out, smem);
+    }
     return;
   }
-  uint32_t u = t - ctl.scan_items;
-  const bool text = u < ctl.text_items;
-  int per = aa.CT, c0 = 0;
-  if (!text) {
-    u -= ctl.text_items;
-    per = aa.CV;
-    c0 = aa.CT;
-  }
+  const bool text = t < ctl.text_end;
+  uint32_t u = text ? t - ctl.seq_end : t - ctl.text_end;
+  const int per = text ? aa.CT : aa.CV;
   const int b = u / (per * aa.Hkv);
   const int g = (u / per) % aa.Hkv;
-  attn_item<T, D, G, EPL>(aa, b, g, c0 + u % per, !text, smem);
+  attn_item<T, D, G, EPL>(aa, b, g, (text ? 0 : aa.CT) + u % per, !text, smem);
   if (!text && threadIdx.x == 0) {
     uint32_t* vd = ctl.vis_done + b * kCtrStride;
     if (counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1) {
@@ -62,6 +74,16 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
   const int VE = Vec<T>::kElems;
   size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE);
   if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
+  if (lds > 48 * 1024) {
+    static bool raised = false;  // per instantiation; the attribute is per function
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<T, D, G, EPL>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               96 * 1024);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
   hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
                      sa, aa, ctl);
   return hipGetLastError();
@@ -110,16 +132,22 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.D = f.D;
   sa.C = f.Hkv * f.D / VE;
   scan_geometry(sa.C, &sa.nseg, &sa.LPR);
+  // Rows that fit the select's registers: small scan items (more of them
+  // than resident workgroups, so the sequences finish one after another),
+  // complemented scores and a polling select item per sequence.
+  sa.encode = f.N <= kItemThreads * kSelKpt;
+  const int min_rows = kItemWaves * (sa.nseg > 1 ? 1 : kWave / sa.LPR);
   sa.rows_per_item = f.rows_per_item > 0 ? f.rows_per_item
-                                         : scan_rows_per_item(f.B, f.N, sa.LPR, sa.nseg);
+                     : sa.encode       ? 2 * min_rows
+                                       : scan_rows_per_item(f.B, f.N, sa.LPR, sa.nseg);
   sa.items_per_seq = (f.N + sa.rows_per_item - 1) / sa.rows_per_item;
-  sa.scores = f.scores;
+  sa.scores = sa.encode ? f.scores_ws : (f.scores_out ? f.scores_out : f.scores_ws);
   sa.k = f.k;
   sa.idx = f.idx;
   sa.seq_ctr = f.seq_ctr;
   sa.ready = f.ready;
 
-  AttnPlan p = attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax, kAttnTargetItems);
+  AttnPlan p = attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax, kFusedAttnTargetItems);
   if (f.epl > 0) {
     p.EPL = f.epl;
     p.SE = attn_split_entries(VE, f.D, f.epl);
@@ -153,9 +181,11 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
 
   FusedCtl ctl{};
   ctl.vis_done = f.vis_done;
-  ctl.scan_items = (uint32_t)sa.items_per_seq * f.B;
-  ctl.text_items = (uint32_t)p.CT * f.Hkv * f.B;
-  ctl.total = ctl.scan_items + ctl.text_items + (uint32_t)p.CV * f.Hkv * f.B;
+  ctl.scores_out = sa.encode ? f.scores_out : nullptr;
+  ctl.per_seq = (uint32_t)sa.items_per_seq + (sa.encode ? 1u : 0u);
+  ctl.seq_end = ctl.per_seq * (uint32_t)f.B;
+  ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
+  ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
   if (f.dtype == 1)
     return f.D == 128 ? fused_g<bf16_t, 128>(G, p.EPL, sa, aa, ctl, st)
                       : fused_g<bf16_t, 64>(G, p.EPL, sa, aa, ctl, st);

@@ -20,8 +20,9 @@ __global__ __launch_bounds__(kItemThreads) void scan_select_kernel(ScanArgs a) {
 }
 
 int scan_rows_per_item(int B, int N, int LPR, int nseg) {
-  // About 16 resident waves per CU on 256 CUs, each wave with a short run of
-  // rows (whole rows per wave when a row has several segments).
+  // About 1024 items in all (B of them per row slice when each item scans one
+  // sequence), each wave with a short run of rows (whole rows per wave when a
+  // row has several segments).
   const long target_items = 1024;
   long per_seq = (target_items + B - 1) / B;
   const int rps = kWave / LPR;
@@ -73,8 +74,12 @@ __global__ __launch_bounds__(kItemThreads) void topk_rows_kernel(const float* __
                                                                int32_t* __restrict__ out) {
   __shared__ SelectSmem<kItemWaves> sm;
   if (k <= 0) return;
-  block_topk<kItemWaves, kSelKpt, false>(vals + (int64_t)blockIdx.x * row_stride, N, k,
-                                         out + (int64_t)blockIdx.x * k, sm);
+  const float* row = vals + (int64_t)blockIdx.x * row_stride;
+  if (N <= kItemThreads * kSelKpt) {
+    block_topk<kItemWaves, kSelKpt, false, true>(row, N, k, out + (int64_t)blockIdx.x * k, sm);
+  } else {
+    block_topk<kItemWaves, kSelKpt, false, false>(row, N, k, out + (int64_t)blockIdx.x * k, sm);
+  }
 }
 
 hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int N, int k,

@@ -55,30 +55,35 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // Requires 1 <= k <= N.  Coherent: read vals with device-coherent loads (the
 // values were written by other workgroups of the same kernel) and write out
 // with device-coherent stores (other workgroups of the kernel read it).
-template <int NW, int KPT, bool Coherent>
+// Cached: the row fits in registers (N <= NW*64*KPT); otherwise it is
+// re-read on every pass.  pre: the caller already holds the keys of a cached
+// row, in this layout; vals is then not read.  out == nullptr: compute
+// everything, write nothing (runs the code once, e.g. to warm the
+// instruction cache while waiting for the scores).
+template <int NW, int KPT, bool Coherent, bool Cached>
 __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int32_t* __restrict__ out,
-                           SelectSmem<NW>& sm) {
+                           SelectSmem<NW>& sm, const uint32_t* pre = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int seg = ((N + NW * kWave - 1) / (NW * kWave)) * kWave;  // per-wave segment
   const int chunks = seg / kWave;
   const int base = wave * seg + lane;
-  const bool cached = chunks <= KPT;
+  constexpr bool cached = Cached;
 
   auto ld = [&](int e) -> float { return Coherent ? load_shared_dev(vals + e) : vals[e]; };
   uint32_t key[KPT];
-  if (cached) {
+  if constexpr (cached) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = base + i * kWave;
-      key[i] = (i < chunks && e < N) ? float_key(ld(e)) : 0u;
+      key[i] = pre ? pre[i] : ((i < chunks && e < N) ? float_key(ld(e)) : 0u);
     }
   }
   // Visit this thread's elements in index order: f(e, valid, key).
   // Uniform across the wave (chunks is uniform), so ballots inside f are safe.
   auto for_each = [&](auto&& f) {
-    if (cached) {
+    if constexpr (cached) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         if (i < chunks) {
@@ -272,7 +277,7 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
     const bool sel = selected(e, valid, kk);
     const uint64_t bm = __ballot(sel);
     const uint32_t pos = before + __popcll(bm & lt);
-    if (sel && pos < (uint32_t)k) {
+    if (sel && pos < (uint32_t)k && out != nullptr) {
       if (Coherent)
         __hip_atomic_store(out + pos, (int32_t)e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
