@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--profile-traffic", action="store_true",
+                   help="no timing: run two one-launch decode steps and a 1 GiB device copy "
+                        "(the calibration) for rocprofv3 counter passes")
     return p.parse_args()
 
 
@@ -167,6 +170,21 @@ def main():
             sv.retrieve(d["q"], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
             sv.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
                                   d["txt_len"], workspace=ws_a, out=out[l])
+
+    if a.profile_traffic:
+        # Counter passes: the fused decode layer as timed, and a plain copy of
+        # known size whose counters give the scale factor of the counters.
+        for _ in range(2):
+            step()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_traffic": w.name, "layer_bytes": decode_bytes(w)[1],
+                          "copy_bytes": src.numel()}), flush=True)
+        return
 
     stream = torch.cuda.Stream(device=dev)      # default priority
     with torch.cuda.stream(stream):
