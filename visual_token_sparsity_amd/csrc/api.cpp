@@ -124,10 +124,11 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
 // ---------------------------------------------------------------- attention
 // Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+2) fp32][counters B*Hkv uint32].
 static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax,
-                                 long target = sv::kAttnTargetItems) {
+                                 bool fused = false) {
   size_t best = 0;
   for (int ve = 4; ve <= 8; ve += 4) {
-    const sv::AttnPlan p = sv::attn_plan(B, Hkv, D, ve, k, Tmax, target);
+    const sv::AttnPlan p = fused ? sv::fused_attn_plan(B, Hkv, D, ve, k, Tmax)
+                                 : sv::attn_plan(B, Hkv, D, ve, k, Tmax, sv::kAttnTargetItems);
     const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * (D + 2) * sizeof(float);
     if (bytes > best) best = bytes;
   }
@@ -194,7 +195,7 @@ static size_t fused_ctl_bytes(int B, int Hkv) { return ctr_bytes((size_t)B * (3 
 size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return 256;
   return retrieve_scores_bytes(B, N) +
-         attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, sv::kFusedAttnTargetItems) +
+         attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true) +
          fused_ctl_bytes(B, Hkv);
 }
 
@@ -260,7 +261,7 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
   f.out = out;
   ws += retrieve_scores_bytes(B, N);
   f.part = (float*)ws;
-  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, sv::kFusedAttnTargetItems);
+  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true);
   uint32_t* ctl = (uint32_t*)ws;
   f.seq_ctr = ctl;
   f.ready = f.seq_ctr + (size_t)B * sv::kCtrStride;

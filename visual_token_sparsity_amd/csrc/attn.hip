@@ -18,13 +18,37 @@ __global__ __launch_bounds__(kItemThreads) void attn_items_kernel(AttnArgs a) {
 
 AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_items) {
   // Most entries per lane (fewest partials, deepest load queue) that still
-  // gives about target_items workgroups.
-  AttnPlan p{};
-  for (p.EPL = 8;; p.EPL >>= 1) {
-    p.SE = attn_split_entries(VE, D, p.EPL);
+  // gives about target_items workgroups.  When even one entry per lane does
+  // not (few sequences and KV heads, long lists), keep the split count per
+  // (sequence, KV head) at most kMaxSplits instead: the combine reads every
+  // split, and many tiny splits cost more than they overlap.
+  constexpr int kMaxSplits = 32;
+  auto plan = [&](int epl) {
+    AttnPlan p{};
+    p.EPL = epl;
+    p.SE = attn_split_entries(VE, D, epl);
     p.CT = (Tmax + p.SE - 1) / p.SE;
     p.CV = (k + p.SE - 1) / p.SE;
-    if (p.EPL == 1 || (long)(p.CT + p.CV) * Hkv * B >= target_items) break;
+    return p;
+  };
+  for (int epl = 8; epl >= 1; epl >>= 1) {
+    const AttnPlan p = plan(epl);
+    if ((long)(p.CT + p.CV) * Hkv * B >= target_items) return p;
+  }
+  for (int epl = 1; epl < 8; epl <<= 1) {
+    const AttnPlan p = plan(epl);
+    if (p.CT + p.CV <= kMaxSplits) return p;
+  }
+  return plan(8);
+}
+
+AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax) {
+  AttnPlan p = attn_plan(B, Hkv, D, VE, k, Tmax, kFusedAttnTargetItems);
+  if (p.EPL < 4) {
+    p.EPL = 4;
+    p.SE = attn_split_entries(VE, D, 4);
+    p.CT = (Tmax + p.SE - 1) / p.SE;
+    p.CV = (k + p.SE - 1) / p.SE;
   }
   return p;
 }

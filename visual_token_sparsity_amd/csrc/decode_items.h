@@ -342,9 +342,14 @@ struct AttnShape {
   static constexpr int EPW = kWave / LPE;  // entries per wave per step
 };
 
+// LDS of an attention item: the per-wave (acc, m, l) slots, reused by the
+// combine for the (m, l) pairs of up to kMaxCombineSplits splits per head.
+constexpr int kMaxCombineSplits = 256;
 template <int D, int G>
 __host__ __device__ constexpr size_t attn_smem_bytes() {
-  return (size_t)kItemWaves * G * (D + 2) * sizeof(float);
+  const size_t w = (size_t)kItemWaves * G * (D + 2);
+  const size_t c = (size_t)G * kMaxCombineSplits * 2;
+  return (w > c ? w : c) * sizeof(float);
 }
 
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
@@ -551,21 +556,39 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   __syncthreads();
   if (!s_comb) return;
 
-  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c
+  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.  The (m, l)
+  // pairs of every split go through LDS once (all loads in flight), then each
+  // thread reads its acc column with 16 loads in flight.
+  // Up to kMaxCombineSplits splits: stage the pairs; beyond, read them in place.
+  float* s_ml = reinterpret_cast<float*>(smem);  // [G][C][2] (the wave slots are free)
+  const bool staged = C <= kMaxCombineSplits;  // uniform
+  if (staged) {
+    for (int t = tid; t < G * C; t += kItemThreads) {
+      const int i = t / C, cc = t % C;
+      const float* pp = a.part + ((head0 + i) * C + cc) * (D + 2);
+      s_ml[2 * t] = load_shared_dev(pp + D);
+      s_ml[2 * t + 1] = load_shared_dev(pp + D + 1);
+    }
+    __syncthreads();
+  }
   for (int t = tid; t < G * D; t += kItemThreads) {
     const int i = t / D, d = t % D;
     const float* pp = a.part + (head0 + i) * C * (D + 2);
+    const float* ml = s_ml + 2 * i * C;
+    auto m_of = [&](int cc) { return staged ? ml[2 * cc] : load_shared_dev(pp + cc * (D + 2) + D); };
+    auto l_of = [&](int cc) {
+      return staged ? ml[2 * cc + 1] : load_shared_dev(pp + cc * (D + 2) + D + 1);
+    };
     float M = -INFINITY;
-#pragma unroll 8
-    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, load_shared_dev(pp + cc * (D + 2) + D));
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, m_of(cc));
     float num = 0.f, den = 0.f;
     if (M != -INFINITY) {
 #pragma unroll 8
       for (int cc = 0; cc < C; ++cc) {
-        const float mc = load_shared_dev(pp + cc * (D + 2) + D);
+        const float mc = m_of(cc);
         const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
         num = fmaf(f, load_shared_dev(pp + cc * (D + 2) + d), num);
-        den = fmaf(f, load_shared_dev(pp + cc * (D + 2) + D + 1), den);
+        den = fmaf(f, l_of(cc), den);
       }
     }
     a.out[(head0 + i) * D + d] = den > 0.f ? num / den : 0.f;

@@ -25,97 +25,15 @@
 // combining one, and vis_done[b] counts visual items past their wait, the
 // last of which lowers ready[b] again.  Complemented scores are zeroed by
 // the select item that read them.
-#include "decode_items.h"
+#include "fused_kernel.h"
 
 namespace sv {
 
-struct FusedCtl {
-  uint32_t per_seq;    // items per sequence in the first block: scan items (+1 select item)
-  uint32_t seq_end;    // B * per_seq
-  uint32_t text_end, total;
-  uint32_t* vis_done;
-  float* scores_out;   // decoded scores (polling mode), may be null
-};
-
-template <typename T, int D, int G, int EPL>
-__global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnArgs aa,
-                                                             FusedCtl ctl) {
-  extern __shared__ __align__(16) char smem[];
-  const uint32_t t = blockIdx.x;
-  if (t < ctl.seq_end) {
-    const int b = t / ctl.per_seq;
-    const int j = t % ctl.per_seq;
-    int q_of = -1;
-    if (j < sa.items_per_seq) {
-      if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
-    } else {
-      select_poll_item(sa, b, ctl.scores_out, smem);
-    }
-    return;
-  }
-  const bool text = t < ctl.text_end;
-  uint32_t u = text ? t - ctl.seq_end : t - ctl.text_end;
-  const int per = text ? aa.CT : aa.CV;
-  const int b = u / (per * aa.Hkv);
-  const int g = (u / per) % aa.Hkv;
-  attn_item<T, D, G, EPL>(aa, b, g, (text ? 0 : aa.CT) + u % per, !text, smem);
-  if (!text && threadIdx.x == 0) {
-    uint32_t* vd = ctl.vis_done + b * kCtrStride;
-    if (counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1) {
-      store_flag(aa.ready + b * kCtrStride, 0u);
-      counter_reset(vd);
-    }
-  }
-}
-
-template <typename T, int D, int G, int EPL>
-static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
-                           hipStream_t st) {
-  const int VE = Vec<T>::kElems;
-  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE);
-  if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
-  if (lds > 48 * 1024) {
-    static bool raised = false;  // per instantiation; the attribute is per function
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<T, D, G, EPL>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               96 * 1024);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
-  }
-  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
-                     sa, aa, ctl);
-  return hipGetLastError();
-}
-
-template <typename T, int D, int G>
-static hipError_t fused_epl(int epl, const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
-                            hipStream_t st) {
-  switch (epl) {
-    case 1: return fused_go<T, D, G, 1>(sa, aa, ctl, st);
-    case 2: return fused_go<T, D, G, 2>(sa, aa, ctl, st);
-    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, st);
-    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <typename T, int D>
-static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
-                          const FusedCtl& ctl, hipStream_t st) {
-  switch (G) {
-    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, st);
-    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, st);
-    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, st);
-    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, st);
-    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, st);
-    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, st);
-    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, st);
-    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, st);
-    default: return hipErrorInvalidValue;
-  }
-}
+// Defined in fused_bf16.hip and fused_f32.hip.
+extern template hipError_t launch_fused_typed<bf16_t>(int, int, int, const ScanArgs&,
+                                                      const AttnArgs&, const FusedCtl&, hipStream_t);
+extern template hipError_t launch_fused_typed<float>(int, int, int, const ScanArgs&,
+                                                     const AttnArgs&, const FusedCtl&, hipStream_t);
 
 hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   const int VE = f.dtype == 1 ? 8 : 4;
@@ -147,7 +65,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.seq_ctr = f.seq_ctr;
   sa.ready = f.ready;
 
-  AttnPlan p = attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax, kFusedAttnTargetItems);
+  AttnPlan p = fused_attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax);
   if (f.epl > 0) {
     p.EPL = f.epl;
     p.SE = attn_split_entries(VE, f.D, f.epl);
@@ -186,11 +104,8 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   ctl.seq_end = ctl.per_seq * (uint32_t)f.B;
   ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
   ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
-  if (f.dtype == 1)
-    return f.D == 128 ? fused_g<bf16_t, 128>(G, p.EPL, sa, aa, ctl, st)
-                      : fused_g<bf16_t, 64>(G, p.EPL, sa, aa, ctl, st);
-  return f.D == 128 ? fused_g<float, 128>(G, p.EPL, sa, aa, ctl, st)
-                    : fused_g<float, 64>(G, p.EPL, sa, aa, ctl, st);
+  if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, st);
+  return launch_fused_typed<float>(f.D, G, p.EPL, sa, aa, ctl, st);
 }
 
 }  // namespace sv

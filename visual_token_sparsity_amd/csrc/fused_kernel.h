@@ -1,0 +1,127 @@
+// One decode layer in one launch: relevance scan, exact top-k, sparse
+// attention over the selected visual entries plus the text entries, and the
+// split combine (SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
+//
+// Work order.  Workgroup i runs item i, in this order:
+//   for each sequence b: its scan items, then (rows that fit the select's
+//     registers) its select item;
+//   the text attention items (they need no selection);
+//   the visual attention items, sequence by sequence (each polls ready[b]).
+// There are more scan items than resident workgroups, so the sequences
+// finish their scans one after another and each select overlaps the scans
+// of the sequences behind it.  Scan items store each score complemented (a
+// zero word: not written yet) and never wait; the select item of b polls
+// the score row until it is complete, which also loads its keys.  Longer
+// rows use counters instead: every scan item of b bumps seq_ctr[b] after
+// its stores have completed, and the last one selects.
+//
+// Each XCD dispatches its share of the grid in increasing order, so whatever
+// a waiting workgroup waits on has been dispatched before it, and scan items
+// never wait.  All waits are bounded.  No atomic ticket: same-address
+// atomics from thousands of workgroups serialise in the memory system.
+//
+// Control words (one 128-byte line each) are zero after every launch:
+// seq_ctr[b] is reset by the selecting workgroup, comb_ctr[b,g] by the
+// combining one, and vis_done[b] counts visual items past their wait, the
+// last of which lowers ready[b] again.  Complemented scores are zeroed by
+// the select item that read them.
+#pragma once
+
+#include "decode_items.h"
+
+namespace sv {
+
+struct FusedCtl {
+  uint32_t per_seq;    // items per sequence in the first block: scan items (+1 select item)
+  uint32_t seq_end;    // B * per_seq
+  uint32_t text_end, total;
+  uint32_t* vis_done;
+  float* scores_out;   // decoded scores (polling mode), may be null
+};
+
+template <typename T, int D, int G, int EPL>
+__global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnArgs aa,
+                                                             FusedCtl ctl) {
+  extern __shared__ __align__(16) char smem[];
+  const uint32_t t = blockIdx.x;
+  if (t < ctl.seq_end) {
+    const int b = t / ctl.per_seq;
+    const int j = t % ctl.per_seq;
+    int q_of = -1;
+    if (j < sa.items_per_seq) {
+      if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+    } else {
+      select_poll_item(sa, b, ctl.scores_out, smem);
+    }
+    return;
+  }
+  const bool text = t < ctl.text_end;
+  uint32_t u = text ? t - ctl.seq_end : t - ctl.text_end;
+  const int per = text ? aa.CT : aa.CV;
+  const int b = u / (per * aa.Hkv);
+  const int g = (u / per) % aa.Hkv;
+  attn_item<T, D, G, EPL>(aa, b, g, (text ? 0 : aa.CT) + u % per, !text, smem);
+  if (!text && threadIdx.x == 0) {
+    uint32_t* vd = ctl.vis_done + b * kCtrStride;
+    if (counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1) {
+      store_flag(aa.ready + b * kCtrStride, 0u);
+      counter_reset(vd);
+    }
+  }
+}
+
+template <typename T, int D, int G, int EPL>
+static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
+                           hipStream_t st) {
+  const int VE = Vec<T>::kElems;
+  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE);
+  if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
+  if (lds > 48 * 1024) {
+    static bool raised = false;  // per instantiation; the attribute is per function
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<T, D, G, EPL>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               96 * 1024);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
+                     sa, aa, ctl);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+static hipError_t fused_epl(int epl, const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
+                            hipStream_t st) {
+  switch (epl) {  // the fused launch plans 4 or 8 entries per lane
+    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, st);
+    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
+                          const FusedCtl& ctl, hipStream_t st) {
+  switch (G) {
+    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, st);
+    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, st);
+    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, st);
+    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, st);
+    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, st);
+    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, st);
+    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, st);
+    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One dtype's instantiations (compiled in their own translation unit).
+template <typename T>
+hipError_t launch_fused_typed(int D, int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
+                              const FusedCtl& ctl, hipStream_t st) {
+  return D == 128 ? fused_g<T, 128>(G, epl, sa, aa, ctl, st) : fused_g<T, 64>(G, epl, sa, aa, ctl, st);
+}
+
+}  // namespace sv

@@ -51,6 +51,37 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// One wave: the digit of an nb-bin histogram h (LDS, padded layout
+// sel_bin; highest digit first) that holds the `remaining`-th key.  The one
+// lane that finds it writes (digit, keys in higher bins, keys in the
+// digit's bin) to the three outputs (LDS).  Each lane sums its run of nb/64
+// bins (independent reads), a DPP scan finds the run holding the crossing,
+// and the wave scans that run one bin per lane.
+__device__ __forceinline__ void wave_find_digit(const uint32_t* h, int nb, uint32_t remaining,
+                                                uint32_t* digit, uint32_t* above,
+                                                uint32_t* count) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = nb / kWave;
+  const int hi = nb - 1 - lane * per;
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < kSelBins / kWave; ++j)
+    if (j < per) tot += h[sel_bin((uint32_t)(hi - j))];
+  const uint32_t incl = wave_incl_scan(tot);
+  const uint32_t excl = incl - tot;
+  const uint64_t hit = __ballot(excl < remaining && incl >= remaining);  // one lane
+  const int hl = hit ? (int)__builtin_ctzll(hit) : 0;
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, hl);
+  const int top = nb - 1 - hl * per;
+  const uint32_t c = lane < per ? h[sel_bin((uint32_t)(top - lane))] : 0u;
+  const uint32_t ci = wave_incl_scan(c);
+  if (lane < per && base + ci >= remaining && base + ci - c < remaining) {  // one lane
+    *digit = (uint32_t)(top - lane);
+    *above = base + ci - c;
+    *count = c;
+  }
+}
+
 // Top-k of vals[0..N) -> out[0..k), ascending.  Called by all NW*64 threads.
 // Requires 1 <= k <= N.  Coherent: read vals with device-coherent loads (the
 // values were written by other workgroups of the same kernel) and write out
@@ -120,25 +151,7 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
   // (independent reads), a lane scan finds the run that holds the crossing,
   // and the wave then scans that run one bin per lane.
   auto find_digit = [&](const uint32_t* h, int nb, uint32_t remaining) {
-    const int per = nb / kWave;
-    const int hi = nb - 1 - lane * per;
-    uint32_t tot = 0;
-#pragma unroll
-    for (int j = 0; j < kSelBins / kWave; ++j)
-      if (j < per) tot += h[sel_bin((uint32_t)(hi - j))];
-    const uint32_t incl = wave_incl_scan(tot);
-    const uint32_t excl = incl - tot;
-    const uint64_t hit = __ballot(excl < remaining && incl >= remaining);  // one lane
-    const int hl = hit ? (int)__builtin_ctzll(hit) : 0;
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, hl);
-    const int top = nb - 1 - hl * per;
-    const uint32_t c = lane < per ? h[sel_bin((uint32_t)(top - lane))] : 0u;
-    const uint32_t ci = wave_incl_scan(c);
-    if (lane < per && base + ci >= remaining && base + ci - c < remaining) {  // one lane
-      sm.digit = (uint32_t)(top - lane);
-      sm.above = base + ci - c;
-      sm.count = c;
-    }
+    wave_find_digit(h, nb, remaining, &sm.digit, &sm.above, &sm.count);
   };
 
   // ---- value range (and a cleared histogram)
