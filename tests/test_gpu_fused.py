@@ -41,6 +41,11 @@ FUSED_CASES = [
     ("qwen2_gqa7_n4096", "qwen2_7b_video", dict(N=4096, k=512, T=100, Tmax=128)),
     ("qwen2_gqa7_ragged", "qwen2_7b_video", dict(N=3001, k=333, T=37, Tmax=40)),
     ("multiturn_n8192", "multiturn_128k", dict(B=2, N=8192, k=1024, T=130, Tmax=256)),
+    # Long rows at full length: the parallel select over 13 and 64 chunks.
+    ("qwen2_full_layer", "qwen2_7b_video", {}),
+    ("multiturn_b1_n131072_h8", "multiturn_128k", dict(B=1, Hq=8, Hkv=8, T=130, Tmax=256)),
+    ("long_k_equals_n", "qwen2_7b_video", dict(N=4100, k=4100, T=16, Tmax=16)),
+    ("long_k_one", "multiturn_128k", dict(B=3, N=2049, k=1, Hq=4, Hkv=4, T=8, Tmax=8)),
     ("visual_only", "llava_next_7b", dict(B=2, N=300, k=40, T=0, Tmax=0, planted=0)),
     ("k_one", "llava_next_7b", dict(B=3, N=77, k=1, T=5, Tmax=8, planted=0)),
     ("n_one", "llava_next_7b", dict(B=2, N=1, k=1, T=4, Tmax=4, planted=0)),
@@ -171,6 +176,133 @@ def test_retrieve_attend_workspace_reuse_and_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.count_nonzero(ws[-ctl_bytes:]) == 0, rep
+        for l in range(w.L):
+            assert torch.equal(idx[l], ref_idx[l]), (rep, l)
+            assert torch.equal(out[l], ref_out[l]), (rep, l)
+    for l, d in enumerate(layers):
+        host = {k: v.cpu() for k, v in d.items()}
+        s_ref = oracle.retrieval_scores(host["q"], host["k_vis"])
+        ok, _, msgs = accept.check_index_sets(ref_idx[l].cpu().numpy(), s_ref, w.k)
+        assert ok, msgs[:3]
+        ref = oracle.sparse_decode_attn(host["q"], host["k_vis"], host["v_vis"],
+                                        ref_idx[l].cpu().numpy(), host["k_txt"], host["v_txt"],
+                                        host["txt_len"])
+        ok, err = accept.check_attention(ref_out[l].cpu().numpy(), ref)
+        assert ok, err
+
+
+# ---------------------------------------------------------------- long rows
+LONG_EDGE = [
+    # mode, N, ks.  all_equal at N > 16384 overflows the candidate list and
+    # two_values the final bin: both take the whole-row fallback.  tied_top_100
+    # puts the k-th key inside a block of 100 equal top scores (ranked by index
+    # in the threshold item); tied_block_3000 spans chunk boundaries.
+    ("gaussian", 20000, (1, 2047, 2048, 9999, 20000)),
+    ("all_equal", 20000, (1, 5000, 20000)),
+    ("two_values", 6000, (1, 2999, 3000, 3001, 6000)),
+    ("tied_top_100", 9000, (1, 50, 99, 100, 101)),
+    ("tied_block_3000", 9000, (100, 4000, 8000)),
+    ("outlier", 9000, (1, 2, 4500)),
+]
+
+
+@pytest.mark.parametrize("mode,N,ks", LONG_EDGE, ids=[c[0] for c in LONG_EDGE])
+def test_retrieve_attend_long_row_edges(mode, N, ks):
+    """Exact selection on long rows whatever the score distribution: ties go to
+    the lower index, both fallbacks agree with the single-workgroup select."""
+    B, H, D = 2, 4, 64
+    g = torch.Generator().manual_seed(41)
+    q = torch.randn(B, 1, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, H, D, generator=g).to(torch.bfloat16)
+    vv = torch.randn(B, N, H, D, generator=g).to(torch.bfloat16)
+    if mode == "all_equal":
+        kv[:] = kv[:, :1].clone()
+    elif mode == "two_values":
+        kv[:, ::2] = kv[:, :1].clone()
+        kv[:, 1::2] = kv[:, 1:2].clone()
+    elif mode == "tied_top_100":
+        kv[:, 4000:4100] = (q[:, 0] * 4).unsqueeze(1).to(torch.bfloat16)
+    elif mode == "tied_block_3000":
+        kv[:, 1500:4500] = kv[:, 1500:1501].clone()
+    elif mode == "outlier":
+        kv[:, 7777] = (q[:, 0] * 1000).to(torch.bfloat16)
+    s_ref = oracle.retrieval_scores(q, kv)
+    gq, gk, gv = q.to(DEV), kv.to(DEV), vv.to(DEV)
+    for k in ks:
+        _say("retrieve_attend long edge", mode, "N", N, "k", k)
+        out, idx = sv.retrieve_attend(gq, gk, gv, k, None, None, None)
+        idx2 = sv.retrieve(gq, gk, k)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2), (mode, k)
+        h = idx.cpu().numpy()
+        ok, _, msgs = accept.check_index_sets(h, s_ref, k)
+        assert ok, (mode, k, msgs[:2])
+        if mode != "outlier" and mode != "gaussian":   # exact ties: the lowest indices win
+            for b in range(B):
+                order = np.lexsort((np.arange(N), -s_ref[b]))
+                assert h[b].tolist() == np.sort(order[:k]).tolist(), (mode, k, b)
+        kt0 = torch.zeros(B, 0, H, D, dtype=torch.bfloat16)
+        ref = oracle.sparse_decode_attn(q, kv, vv, h, kt0, kt0, np.zeros(B, np.int64))
+        ok, err = accept.check_attention(out.cpu().numpy(), ref)
+        assert ok, (mode, k, err)
+
+
+def _al256(n):
+    return (n + 255) // 256 * 256
+
+
+def _long_zero_span(B, N, total):
+    """Byte range of the long-row control lines and histograms (zero between
+    launches): the tail of the workspace is [control lines 6 per sequence]
+    [hist1 8 x 2048 words][hist2 2048 words][candidates 16384 x 8 bytes]
+    [two arrays of ceil(N / 2048) words], each part 256-byte aligned."""
+    P = (N + 2047) // 2048
+    zero = _al256(B * 6 * 128) + _al256(B * 8 * 2048 * 4) + _al256(B * 2048 * 4)
+    long_total = zero + _al256(B * 16384 * 8) + 2 * _al256(B * P * 4)
+    start = total - long_total
+    return start, start + zero
+
+
+def test_retrieve_attend_long_rows_reuse_and_graph_replay():
+    """Long rows: the control lines, counters and histograms are zero after every
+    launch, and graph replays reproduce the eager results."""
+    w = synthetic.scaled_decode(synthetic.DECODE["qwen2_7b_video"], B=2, L=2, N=6000, k=700,
+                                T=40, Tmax=64)
+    _say("retrieve_attend long reuse + graph", w)
+    layers = [_to(synthetic.make_decode_layer(w, seed=15, layer=l)) for l in range(w.L)]
+    nbytes = sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax)
+    ws = sv.new_workspace(nbytes, DEV)
+    z0, z1 = _long_zero_span(w.B, w.N, nbytes)
+    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=DEV) for _ in layers]
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV) for _ in layers]
+
+    def step():
+        for l, d in enumerate(layers):
+            sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
+                               d["txt_len"], workspace=ws, out=out[l], idx_out=idx[l])
+
+    def zero_ok():
+        return (torch.count_nonzero(ws[z0:z1]) == 0 and
+                torch.count_nonzero(ws[z0 - ctl_bytes:z0]) == 0)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    assert zero_ok()
+    ref_idx = [t.clone() for t in idx]
+    ref_out = [t.clone() for t in out]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    for rep in range(4):
+        for t in idx + out:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert zero_ok(), rep
         for l in range(w.L):
             assert torch.equal(idx[l], ref_idx[l]), (rep, l)
             assert torch.equal(out[l], ref_out[l]), (rep, l)

@@ -234,10 +234,16 @@ struct FusedLaunch {
   uint32_t* ready;     // [B]
   uint32_t* vis_done;  // [B]
   uint32_t* comb_ctr;  // [B][Hkv]
+  // Rows longer than the single-workgroup select: long_select_bytes(B, N)
+  // bytes whose first long_select_zero_bytes(B) are zero before the launch
+  // and zero again after it.
+  void* long_ws;
   int rows_per_item;   // 0: default
   int epl;             // 0: default
 };
 hipError_t launch_fused(const FusedLaunch& f, hipStream_t stream);
+size_t long_select_bytes(int B, int N);  // 0 when rows take the single-workgroup select
+size_t long_select_zero_bytes(int B, int N);
 
 bool salience_supported(int N, int D);
 

@@ -38,6 +38,8 @@ constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment
 constexpr int kScanSegChunks = 512;
 constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
 constexpr uint32_t kSpinLimit = 1u << 24;  // bound of every in-kernel wait
+constexpr int kLsReps = 8;         // replicas of a long row's first-level key histogram
+constexpr int kLsBins = 2048;      // 11-bit key digits
 
 // ---------------------------------------------------------------- scan
 struct ScanArgs {
@@ -58,6 +60,10 @@ struct ScanArgs {
   // the complement of their bits (a zero word: not written yet) and a select
   // item polls the row; no counters.
   bool encode;
+  // Fused kernel, longer rows: [B][kLsReps][kLsBins] histogram of the
+  // scores' top 11 key bits, which every scan item adds to (long_select.h).
+  // Null otherwise.
+  uint32_t* hist1;
 };
 
 // Chunks of qhat kept in LDS (zero past C).
@@ -151,6 +157,13 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   Vec<T> nxt[kScanCpl];
   load_unit(rsub, nxt);
 
+  // Long rows: a local histogram of the item's score digits, past qhat.
+  uint32_t* lh = reinterpret_cast<uint32_t*>(smem + (size_t)CP * VE * sizeof(float));
+  if (a.hist1) {
+    for (int i = tid; i < kLsBins; i += kItemThreads) lh[i] = 0u;
+    if (q_of == b) __syncthreads();  // otherwise the qhat barrier orders it
+  }
+
   // qhat -> LDS (zero past C).
   if (q_of != b) {
     const T* qb = reinterpret_cast<const T*>(a.q);
@@ -214,9 +227,10 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
         if (a.encode)
           __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + row, ~__float_as_uint(s),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else if (coherent)
+        else if (coherent) {
           store_shared_dev(srow + row, s);  // read back by the selecting workgroup
-        else
+          if (a.hist1) atomicAdd(&lh[float_key(s) >> 21], 1u);
+        } else
           srow[row] = s;
       }
     }
@@ -224,6 +238,18 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
 
   if (!coherent || a.encode) return false;
   __shared__ uint32_t s_last;
+  if (a.hist1) {
+    __syncthreads();
+    uint32_t* g = a.hist1 + ((int64_t)b * kLsReps + (item & (kLsReps - 1))) * kLsBins;
+    for (int i = tid; i < kLsBins; i += kItemThreads) {
+      const uint32_t v = lh[i];
+      if (v) __hip_atomic_fetch_add(g + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_stores_complete();
+    __syncthreads();
+    if (tid == 0) counter_add(&a.seq_ctr[b * kCtrStride], 1u);
+    return false;
+  }
   wait_stores_complete();
   __syncthreads();
   if (tid == 0)
@@ -305,8 +331,9 @@ __device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float
   }
 }
 
-__host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE) {
-  const size_t q = (size_t)scan_padded_chunks(nseg, LPR) * VE * sizeof(float);
+__host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE, bool hist = false) {
+  const size_t q = (size_t)scan_padded_chunks(nseg, LPR) * VE * sizeof(float) +
+                   (hist ? (size_t)kLsBins * sizeof(uint32_t) : 0);
   const size_t s = sizeof(SelectSmem<kItemWaves>);
   return q > s ? q : s;
 }

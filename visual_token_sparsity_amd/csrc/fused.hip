@@ -1,39 +1,37 @@
-// One decode layer in one launch: relevance scan, exact top-k, sparse
-// attention over the selected visual entries plus the text entries, and the
-// split combine (SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
-//
-// Work order.  Workgroup i runs item i, in this order:
-//   for each sequence b: its scan items, then (rows that fit the select's
-//     registers) its select item;
-//   the text attention items (they need no selection);
-//   the visual attention items, sequence by sequence (each polls ready[b]).
-// There are more scan items than resident workgroups, so the sequences
-// finish their scans one after another and each select overlaps the scans
-// of the sequences behind it.  Scan items store each score complemented (a
-// zero word: not written yet) and never wait; the select item of b polls
-// the score row until it is complete, which also loads its keys.  Longer
-// rows use counters instead: every scan item of b bumps seq_ctr[b] after
-// its stores have completed, and the last one selects.
-//
-// Each XCD dispatches its share of the grid in increasing order, so whatever
-// a waiting workgroup waits on has been dispatched before it, and scan items
-// never wait.  All waits are bounded.  No atomic ticket: same-address
-// atomics from thousands of workgroups serialise in the memory system.
-//
-// Control words (one 128-byte line each) are zero after every launch:
-// seq_ctr[b] is reset by the selecting workgroup, comb_ctr[b,g] by the
-// combining one, and vis_done[b] counts visual items past their wait, the
-// last of which lowers ready[b] again.  Complemented scores are zeroed by
-// the select item that read them.
+// Host side of the one-launch decode layer: the work plan of one launch and
+// the long-row select workspace (the kernel and its work order are in
+// fused_kernel.h; SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
 #include "fused_kernel.h"
 
 namespace sv {
 
 // Defined in fused_bf16.hip and fused_f32.hip.
 extern template hipError_t launch_fused_typed<bf16_t>(int, int, int, const ScanArgs&,
-                                                      const AttnArgs&, const FusedCtl&, hipStream_t);
+                                                      const AttnArgs&, const FusedCtl&,
+                                                      const LongSelArgs&, hipStream_t);
 extern template hipError_t launch_fused_typed<float>(int, int, int, const ScanArgs&,
-                                                     const AttnArgs&, const FusedCtl&, hipStream_t);
+                                                     const AttnArgs&, const FusedCtl&,
+                                                     const LongSelArgs&, hipStream_t);
+
+// Long-row select workspace, per launch:
+//   [ctl B*kLsCtlLines lines][hist1 B*kLsReps*kLsBins][hist2 B*kLsBins]  (zero between launches)
+//   [cand B*kLsCandCap][chunk_hi B*P][offs B*P]
+static size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
+static bool long_rows(int N) { return N > kItemThreads * kSelKpt; }
+static int long_chunks(int N) { return (N + kLsChunk - 1) / kLsChunk; }
+
+size_t long_select_zero_bytes(int B, int N) {
+  if (!long_rows(N)) return 0;
+  return al256((size_t)B * kLsCtlLines * kCtrStride * 4) +
+         al256((size_t)B * kLsReps * kLsBins * 4) + al256((size_t)B * kLsBins * 4);
+}
+
+size_t long_select_bytes(int B, int N) {
+  if (!long_rows(N)) return 0;
+  const size_t P = (size_t)long_chunks(N);
+  return long_select_zero_bytes(B, N) + al256((size_t)B * kLsCandCap * 8) +
+         2 * al256((size_t)B * P * 4);
+}
 
 hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   const int VE = f.dtype == 1 ? 8 : 4;
@@ -52,8 +50,9 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   scan_geometry(sa.C, &sa.nseg, &sa.LPR);
   // Rows that fit the select's registers: small scan items (more of them
   // than resident workgroups, so the sequences finish one after another),
-  // complemented scores and a polling select item per sequence.
-  sa.encode = f.N <= kItemThreads * kSelKpt;
+  // complemented scores and a polling select item per sequence.  Longer
+  // rows: the parallel select of long_select.h.
+  sa.encode = !long_rows(f.N);
   const int min_rows = kItemWaves * (sa.nseg > 1 ? 1 : kWave / sa.LPR);
   sa.rows_per_item = f.rows_per_item > 0 ? f.rows_per_item
                      : sa.encode       ? 2 * min_rows
@@ -64,6 +63,25 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.idx = f.idx;
   sa.seq_ctr = f.seq_ctr;
   sa.ready = f.ready;
+  LongSelArgs ls{};
+  if (!sa.encode) {
+    if (!f.long_ws) return hipErrorInvalidValue;
+    const size_t P = (size_t)long_chunks(f.N);
+    char* w = static_cast<char*>(f.long_ws);
+    ls.P = (int)P;
+    ls.ctl = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)f.B * kLsCtlLines * kCtrStride * 4);
+    ls.hist1 = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)f.B * kLsReps * kLsBins * 4);
+    ls.hist2 = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)f.B * kLsBins * 4);
+    ls.cand = reinterpret_cast<uint64_t*>(w);
+    w += al256((size_t)f.B * kLsCandCap * 8);
+    ls.chunk_hi = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)f.B * P * 4);
+    ls.offs = reinterpret_cast<uint32_t*>(w);
+    sa.hist1 = ls.hist1;
+  }
 
   AttnPlan p = fused_attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax);
   if (f.epl > 0) {
@@ -100,12 +118,12 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   FusedCtl ctl{};
   ctl.vis_done = f.vis_done;
   ctl.scores_out = sa.encode ? f.scores_out : nullptr;
-  ctl.per_seq = (uint32_t)sa.items_per_seq + (sa.encode ? 1u : 0u);
+  ctl.per_seq = (uint32_t)sa.items_per_seq + (sa.encode ? 1u : 2u * (uint32_t)ls.P + 1u);
   ctl.seq_end = ctl.per_seq * (uint32_t)f.B;
   ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
   ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
-  if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, st);
-  return launch_fused_typed<float>(f.D, G, p.EPL, sa, aa, ctl, st);
+  if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
+  return launch_fused_typed<float>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
 }
 
 }  // namespace sv

@@ -5,6 +5,7 @@
 namespace sv {
 
 template hipError_t launch_fused_typed<float>(int, int, int, const ScanArgs&, const AttnArgs&,
-                                           const FusedCtl&, hipStream_t);
+                                           const FusedCtl&, const LongSelArgs&,
+                                           hipStream_t);
 
 }  // namespace sv

@@ -12,8 +12,9 @@
 // of the sequences behind it.  Scan items store each score complemented (a
 // zero word: not written yet) and never wait; the select item of b polls
 // the score row until it is complete, which also loads its keys.  Longer
-// rows use counters instead: every scan item of b bumps seq_ctr[b] after
-// its stores have completed, and the last one selects.
+// rows select in parallel (long_select.h): per sequence, the scan items are
+// followed by P candidate items, one threshold item and P compaction items,
+// P = ceil(N / 2048).
 //
 // Each XCD dispatches its share of the grid in increasing order, so whatever
 // a waiting workgroup waits on has been dispatched before it, and scan items
@@ -21,18 +22,19 @@
 // atomics from thousands of workgroups serialise in the memory system.
 //
 // Control words (one 128-byte line each) are zero after every launch:
-// seq_ctr[b] is reset by the selecting workgroup, comb_ctr[b,g] by the
-// combining one, and vis_done[b] counts visual items past their wait, the
-// last of which lowers ready[b] again.  Complemented scores are zeroed by
-// the select item that read them.
+// seq_ctr[b] is reset by the selecting workgroup (long rows: the threshold
+// item), comb_ctr[b,g] by the combining one, and vis_done[b] counts visual
+// items past their wait, the last of which lowers ready[b] again.
+// Complemented scores are zeroed by the select item that read them; the
+// long-row histograms and counters by the threshold and compaction items.
 #pragma once
 
-#include "decode_items.h"
+#include "long_select.h"
 
 namespace sv {
 
 struct FusedCtl {
-  uint32_t per_seq;    // items per sequence in the first block: scan items (+1 select item)
+  uint32_t per_seq;    // items per sequence in the first block: scan items, then the select's
   uint32_t seq_end;    // B * per_seq
   uint32_t text_end, total;
   uint32_t* vis_done;
@@ -41,7 +43,7 @@ struct FusedCtl {
 
 template <typename T, int D, int G, int EPL>
 __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnArgs aa,
-                                                             FusedCtl ctl) {
+                                                             FusedCtl ctl, LongSelArgs ls) {
   extern __shared__ __align__(16) char smem[];
   const uint32_t t = blockIdx.x;
   if (t < ctl.seq_end) {
@@ -50,8 +52,16 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
     int q_of = -1;
     if (j < sa.items_per_seq) {
       if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
-    } else {
+    } else if (!sa.hist1) {
       select_poll_item(sa, b, ctl.scores_out, smem);
+    } else {
+      const int r = j - sa.items_per_seq;
+      if (r < ls.P)
+        cand_item(sa, ls, b, r, smem);
+      else if (r == ls.P)
+        thr_item(sa, ls, b, smem);
+      else
+        compact_item(sa, ls, b, r - ls.P - 1, smem);
     }
     return;
   }
@@ -72,10 +82,14 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
 
 template <typename T, int D, int G, int EPL>
 static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
-                           hipStream_t st) {
+                           const LongSelArgs& ls, hipStream_t st) {
   const int VE = Vec<T>::kElems;
-  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE);
+  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE, sa.hist1 != nullptr);
   if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
+  if (sa.hist1) {
+    if (cand_smem_bytes() > lds) lds = cand_smem_bytes();
+    if (thr_smem_bytes(ls.P) > lds) lds = thr_smem_bytes(ls.P);
+  }
   if (lds > 48 * 1024) {
     static bool raised = false;  // per instantiation; the attribute is per function
     if (!raised) {
@@ -86,33 +100,34 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
       raised = true;
     }
   }
+  if (lds > 96 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
-                     sa, aa, ctl);
+                     sa, aa, ctl, ls);
   return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 static hipError_t fused_epl(int epl, const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
-                            hipStream_t st) {
+                            const LongSelArgs& ls, hipStream_t st) {
   switch (epl) {  // the fused launch plans 4 or 8 entries per lane
-    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, st);
-    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, st);
+    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, ls, st);
+    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, ls, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int D>
 static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
-                          const FusedCtl& ctl, hipStream_t st) {
+                          const FusedCtl& ctl, const LongSelArgs& ls, hipStream_t st) {
   switch (G) {
-    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, st);
-    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, st);
-    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, st);
-    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, st);
-    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, st);
-    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, st);
-    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, st);
-    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, st);
+    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, ls, st);
+    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, ls, st);
+    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, ls, st);
+    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, ls, st);
+    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, ls, st);
+    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, ls, st);
+    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, ls, st);
+    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, ls, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -120,8 +135,9 @@ static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa
 // One dtype's instantiations (compiled in their own translation unit).
 template <typename T>
 hipError_t launch_fused_typed(int D, int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
-                              const FusedCtl& ctl, hipStream_t st) {
-  return D == 128 ? fused_g<T, 128>(G, epl, sa, aa, ctl, st) : fused_g<T, 64>(G, epl, sa, aa, ctl, st);
+                              const FusedCtl& ctl, const LongSelArgs& ls, hipStream_t st) {
+  return D == 128 ? fused_g<T, 128>(G, epl, sa, aa, ctl, ls, st)
+                  : fused_g<T, 64>(G, epl, sa, aa, ctl, ls, st);
 }
 
 }  // namespace sv
