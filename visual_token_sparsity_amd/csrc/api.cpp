@@ -122,14 +122,14 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
 }
 
 // ---------------------------------------------------------------- attention
-// Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+2) fp32][counters B*Hkv uint32].
+// Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+4) fp32][counters B*Hkv uint32].
 static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax,
                                  bool fused = false) {
   size_t best = 0;
   for (int ve = 4; ve <= 8; ve += 4) {
     const sv::AttnPlan p = fused ? sv::fused_attn_plan(B, Hkv, D, ve, k, Tmax)
                                  : sv::attn_plan(B, Hkv, D, ve, k, Tmax, sv::kAttnTargetItems);
-    const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * (D + 2) * sizeof(float);
+    const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * sv::attn_part_stride(D) * sizeof(float);
     if (bytes > best) best = bytes;
   }
   return align256(best);

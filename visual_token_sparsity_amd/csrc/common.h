@@ -171,6 +171,19 @@ __device__ __forceinline__ void counter_reset(uint32_t* c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Agent-coherent 4- and 16-byte buffer accesses (sc1: served past the
+// XCD-local L2, like the agent-scope atomic loads and stores above).
+constexpr int kCacheCoherent = 16;
+__device__ __forceinline__ uint32_t load1_dev(BufRsrc r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kCacheCoherent);
+}
+__device__ __forceinline__ u32x4 load4_dev(BufRsrc r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCacheCoherent));
+}
+__device__ __forceinline__ void store4_dev(BufRsrc r, uint32_t voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kCacheCoherent);
+}
+
 // Counters and flags touched by many workgroups each sit on their own
 // 128-byte line: same-line atomics from many workgroups serialise.
 constexpr int kCtrStride = 32;  // uint32 words
@@ -183,6 +196,8 @@ int device_cu_count();
 
 // Scan rows per work item when the caller does not choose (0).
 int scan_rows_per_item(int B, int N, int LPR, int nseg);
+// Rows per item for at most about target_items items in all.
+int scan_rows_for_items(int B, int N, int LPR, int nseg, long target_items);
 
 hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv, int64_t bstride,
                            int64_t tstride, int N, int Hkv, int D, int dtype, float* scores, int k,
@@ -191,6 +206,10 @@ hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv,
 
 hipError_t launch_topk_rows(const float* vals, int rows, int64_t row_stride, int N, int k,
                             int32_t* out, hipStream_t stream);
+
+// One split's partial result of one query head: acc[D], m, l, two pad
+// words (rows stay 16-byte aligned for the combine's vector loads).
+__host__ __device__ constexpr int attn_part_stride(int D) { return D + 4; }
 
 // Split plan of the decode attention: EPL entries per lane, SE entries per
 // split, CT text splits then CV visual splits.

@@ -355,7 +355,7 @@ struct AttnArgs {
   int Tmax;
   float qscale;          // scale * log2(e)
   int CT, CV;            // text and visual splits
-  float* part;           // [B][Hq][CT+CV][D+2]
+  float* part;           // [B][Hq][CT+CV][attn_part_stride(D)]
   uint32_t* comb_ctr;    // [B][Hkv] (stride kCtrStride), self-resetting
   float* out;            // [B][Hq][D]
   uint32_t* ready;       // [B] (stride kCtrStride; fused kernel only)
@@ -370,13 +370,24 @@ struct AttnShape {
 };
 
 // LDS of an attention item: the per-wave (acc, m, l) slots, reused by the
-// combine for the (m, l) pairs of up to kMaxCombineSplits splits per head.
+// combine for the weights and l of up to kMaxCombineSplits splits per head,
+// G denominators and one float4 per thread.
 constexpr int kMaxCombineSplits = 256;
 template <int D, int G>
 __host__ __device__ constexpr size_t attn_smem_bytes() {
   const size_t w = (size_t)kItemWaves * G * (D + 2);
-  const size_t c = (size_t)G * kMaxCombineSplits * 2;
+  const size_t c = (size_t)G * kMaxCombineSplits * 2 + 8 + (size_t)kItemThreads * 4;
   return (w > c ? w : c) * sizeof(float);
+}
+
+// Float4 columns of the combine and the number of thread groups that split
+// the splits among them (a power of two, at most 16).
+template <int D, int G>
+__host__ __device__ constexpr int combine_groups() {
+  constexpr int V = G * D / 4;
+  int s = 1;
+  while (s < 16 && 2 * s * V <= kItemThreads) s *= 2;
+  return s;
 }
 
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
@@ -549,6 +560,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   }
   __syncthreads();
   const int64_t head0 = (int64_t)b * a.Hq + g * G;
+  constexpr int PS = attn_part_stride(D);
   for (int t = tid; t < G * D; t += kItemThreads) {
     const int i = t / D, d = t % D;
     float mm = -INFINITY;
@@ -565,7 +577,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     if (C == 1) {
       a.out[(head0 + i) * D + d] = ll > 0.f ? aa / ll : 0.f;
     } else {
-      float* pp = a.part + ((head0 + i) * C + c) * (D + 2);
+      float* pp = a.part + ((head0 + i) * C + c) * PS;
       store_shared_dev(pp + d, aa);
       if (d == 0) {
         store_shared_dev(pp + D, mm);
@@ -583,42 +595,93 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   __syncthreads();
   if (!s_comb) return;
 
-  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.  The (m, l)
-  // pairs of every split go through LDS once (all loads in flight), then each
-  // thread reads its acc column with 16 loads in flight.
-  // Up to kMaxCombineSplits splits: stage the pairs; beyond, read them in place.
-  float* s_ml = reinterpret_cast<float*>(smem);  // [G][C][2] (the wave slots are free)
-  const bool staged = C <= kMaxCombineSplits;  // uniform
-  if (staged) {
+  // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
+  const float* pb = a.part + head0 * C * PS;  // this (b, g): [G][C][PS]
+  if (C <= kMaxCombineSplits) {
+    // (m, l) of every split into LDS (all loads in flight); one wave per
+    // head turns m into the weight 2^(m - M) and sums the denominator.
+    float* s_f = reinterpret_cast<float*>(smem);  // [G][C]
+    float* s_l = s_f + G * kMaxCombineSplits;    // [G][C]
+    float* s_den = s_l + G * kMaxCombineSplits;  // [G]
+    f32x4v* s_red = reinterpret_cast<f32x4v*>(s_den + 8);
     for (int t = tid; t < G * C; t += kItemThreads) {
-      const int i = t / C, cc = t % C;
-      const float* pp = a.part + ((head0 + i) * C + cc) * (D + 2);
-      s_ml[2 * t] = load_shared_dev(pp + D);
-      s_ml[2 * t + 1] = load_shared_dev(pp + D + 1);
+      s_f[t] = load_shared_dev(pb + (int64_t)t * PS + D);
+      s_l[t] = load_shared_dev(pb + (int64_t)t * PS + D + 1);
     }
     __syncthreads();
-  }
-  for (int t = tid; t < G * D; t += kItemThreads) {
-    const int i = t / D, d = t % D;
-    const float* pp = a.part + (head0 + i) * C * (D + 2);
-    const float* ml = s_ml + 2 * i * C;
-    auto m_of = [&](int cc) { return staged ? ml[2 * cc] : load_shared_dev(pp + cc * (D + 2) + D); };
-    auto l_of = [&](int cc) {
-      return staged ? ml[2 * cc + 1] : load_shared_dev(pp + cc * (D + 2) + D + 1);
-    };
-    float M = -INFINITY;
-    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, m_of(cc));
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int cc = 0; cc < C; ++cc) {
-        const float mc = m_of(cc);
+    for (int i = wave; i < G; i += kItemWaves) {
+      float M = -INFINITY;
+      for (int cc = lane; cc < C; cc += kWave) M = fmaxf(M, s_f[i * C + cc]);
+      M = group_max<kWave>(M);
+      float den = 0.f;
+      for (int cc = lane; cc < C; cc += kWave) {
+        const float mc = s_f[i * C + cc];
         const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
-        num = fmaf(f, load_shared_dev(pp + cc * (D + 2) + d), num);
-        den = fmaf(f, l_of(cc), den);
+        s_f[i * C + cc] = f;
+        den = fmaf(f, s_l[i * C + cc], den);
+      }
+      den = group_sum<kWave>(den);
+      if (lane == 0) s_den[i] = den;
+    }
+    __syncthreads();
+    // Numerators: thread (v, s) sums float4 column v over splits s, s+S, ...
+    // with 16 vector loads in flight; the S groups meet in LDS.
+    constexpr int V = G * D / 4, S = combine_groups<D, G>();
+    const int v = tid % V, s = tid / V;
+    const int i = v / (D / 4), d4 = v % (D / 4);
+    f32x4v num = {0.f, 0.f, 0.f, 0.f};
+    if (s < S) {
+      const BufRsrc pr = make_rsrc(pb, (uint32_t)(G * C * PS * 4));
+      const uint32_t col = (uint32_t)(i * C * PS + 4 * d4) * 4u;
+      const float* fw = s_f + i * C;
+      for (int c0 = s; c0 < C; c0 += 16 * S) {
+        f32x4v x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int cc = c0 + j * S;
+          x[j] = __builtin_bit_cast(f32x4v, load4_dev(pr, cc < C ? col + (uint32_t)(cc * PS * 4) : kBufOob));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int cc = c0 + j * S;
+          const float f = cc < C ? fw[cc] : 0.f;
+          num += f * x[j];
+        }
       }
     }
-    a.out[(head0 + i) * D + d] = den > 0.f ? num / den : 0.f;
+    if constexpr (S > 1) {
+      s_red[tid] = num;
+      __syncthreads();
+      if (s == 0) {
+#pragma unroll
+        for (int r = 1; r < S; ++r) num += s_red[r * V + v];
+      }
+    }
+    if (s == 0 && v < V && tid < V) {
+      const float den = s_den[i];
+      float* o = a.out + (head0 + i) * D + 4 * d4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = den > 0.f ? num[j] / den : 0.f;
+    }
+  } else {
+    // More splits than LDS holds: read (m, l) in place.
+    for (int t = tid; t < G * D; t += kItemThreads) {
+      const int i = t / D, d = t % D;
+      const float* pp = pb + (int64_t)i * C * PS;
+      float M = -INFINITY;
+      for (int cc = 0; cc < C; ++cc) M = fmaxf(M, load_shared_dev(pp + cc * PS + D));
+      float num = 0.f, den = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll 8
+        for (int cc = 0; cc < C; ++cc) {
+          const float mc = load_shared_dev(pp + cc * PS + D);
+          const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+          num = fmaf(f, load_shared_dev(pp + cc * PS + d), num);
+          den = fmaf(f, load_shared_dev(pp + cc * PS + D + 1), den);
+        }
+      }
+      a.out[(head0 + i) * D + d] = den > 0.f ? num / den : 0.f;
+    }
   }
   if (tid == 0) counter_reset(ctr);
 }

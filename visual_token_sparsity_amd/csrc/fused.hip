@@ -118,8 +118,10 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   FusedCtl ctl{};
   ctl.vis_done = f.vis_done;
   ctl.scores_out = sa.encode ? f.scores_out : nullptr;
+  ctl.B = (uint32_t)f.B;
+  ctl.auto_rows = !sa.encode && f.rows_per_item <= 0;
   ctl.per_seq = (uint32_t)sa.items_per_seq + (sa.encode ? 1u : 2u * (uint32_t)ls.P + 1u);
-  ctl.seq_end = ctl.per_seq * (uint32_t)f.B;
+  ctl.seq_end = ctl.per_seq * (uint32_t)f.B;  // long rows: the same count, in phase order
   ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
   ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
   if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, ls, st);

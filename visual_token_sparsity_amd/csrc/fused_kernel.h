@@ -3,18 +3,21 @@
 // split combine (SparseVILA velog summary, Sec. 3.2 and Sec. 4.5).
 //
 // Work order.  Workgroup i runs item i, in this order:
-//   for each sequence b: its scan items, then (rows that fit the select's
-//     registers) its select item;
+//   rows that fit the select's registers: for each sequence b, its scan
+//     items, then its select item;
+//   longer rows (the parallel select of long_select.h, P = ceil(N / 2048)
+//     chunks per row): every scan item of every sequence, then the P
+//     candidate items of each sequence, the threshold items, and the P
+//     compaction items of each sequence;
 //   the text attention items (they need no selection);
 //   the visual attention items, sequence by sequence (each polls ready[b]).
-// There are more scan items than resident workgroups, so the sequences
-// finish their scans one after another and each select overlaps the scans
-// of the sequences behind it.  Scan items store each score complemented (a
-// zero word: not written yet) and never wait; the select item of b polls
-// the score row until it is complete, which also loads its keys.  Longer
-// rows select in parallel (long_select.h): per sequence, the scan items are
-// followed by P candidate items, one threshold item and P compaction items,
-// P = ceil(N / 2048).
+// Short rows: there are more scan items than resident workgroups, so the
+// sequences finish their scans one after another and each select overlaps
+// the scans of the sequences behind it.  Scan items store each score
+// complemented (a zero word: not written yet) and never wait; the select
+// item of b polls the score row until it is complete, which also loads its
+// keys.  Long rows: the select items come after all scan items, so none of
+// them holds a workgroup slot while scans still wait for one.
 //
 // Each XCD dispatches its share of the grid in increasing order, so whatever
 // a waiting workgroup waits on has been dispatched before it, and scan items
@@ -34,9 +37,11 @@
 namespace sv {
 
 struct FusedCtl {
-  uint32_t per_seq;    // items per sequence in the first block: scan items, then the select's
-  uint32_t seq_end;    // B * per_seq
+  uint32_t B;
+  uint32_t per_seq;    // short rows: scan items + 1 select item per sequence
+  uint32_t seq_end;    // items before the attention items
   uint32_t text_end, total;
+  bool auto_rows;      // long rows: size the scan items from the kernel's occupancy
   uint32_t* vis_done;
   float* scores_out;   // decoded scores (polling mode), may be null
 };
@@ -47,21 +52,28 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   extern __shared__ __align__(16) char smem[];
   const uint32_t t = blockIdx.x;
   if (t < ctl.seq_end) {
-    const int b = t / ctl.per_seq;
-    const int j = t % ctl.per_seq;
     int q_of = -1;
-    if (j < sa.items_per_seq) {
-      if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
-    } else if (!sa.hist1) {
-      select_poll_item(sa, b, ctl.scores_out, smem);
+    if (!sa.hist1) {
+      const int b = t / ctl.per_seq;
+      const int j = t % ctl.per_seq;
+      if (j < sa.items_per_seq) {
+        if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+      } else {
+        select_poll_item(sa, b, ctl.scores_out, smem);
+      }
+      return;
+    }
+    const uint32_t S = (uint32_t)sa.items_per_seq, P = (uint32_t)ls.P;
+    uint32_t u = t;
+    if (u < ctl.B * S) {
+      scan_item<T>(sa, u / S, u % S, smem, q_of);
+    } else if ((u -= ctl.B * S) < ctl.B * P) {
+      cand_item(sa, ls, u / P, u % P, smem);
+    } else if ((u -= ctl.B * P) < ctl.B) {
+      thr_item(sa, ls, u, smem);
     } else {
-      const int r = j - sa.items_per_seq;
-      if (r < ls.P)
-        cand_item(sa, ls, b, r, smem);
-      else if (r == ls.P)
-        thr_item(sa, ls, b, smem);
-      else
-        compact_item(sa, ls, b, r - ls.P - 1, smem);
+      u -= ctl.B;
+      compact_item(sa, ls, u / P, u % P, smem);
     }
     return;
   }
@@ -101,8 +113,29 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
     }
   }
   if (lds > 96 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(ctl.total), dim3(kItemThreads), lds, st,
-                     sa, aa, ctl, ls);
+  ScanArgs s = sa;
+  FusedCtl c = ctl;
+  if (ctl.auto_rows) {
+    // Long rows: one round of scan items, as many as fit on the device at
+    // once (a second, partly filled round would leave the memory system
+    // idle at its end).
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<T, D, G, EPL>,
+                                                     kItemThreads, lds) == hipSuccess &&
+        per_cu > 0) {
+      const uint32_t attn_items = ctl.total - ctl.seq_end, text_items = ctl.text_end - ctl.seq_end;
+      const uint32_t sel_items = ctl.per_seq - (uint32_t)sa.items_per_seq;
+      s.rows_per_item = scan_rows_for_items((int)ctl.B, sa.N, sa.LPR, sa.nseg,
+                                            (long)per_cu * device_cu_count());
+      s.items_per_seq = (sa.N + s.rows_per_item - 1) / s.rows_per_item;
+      c.per_seq = (uint32_t)s.items_per_seq + sel_items;
+      c.seq_end = c.per_seq * ctl.B;
+      c.text_end = c.seq_end + text_items;
+      c.total = c.seq_end + attn_items;
+    }
+  }
+  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(c.total), dim3(kItemThreads), lds, st,
+                     s, aa, c, ls);
   return hipGetLastError();
 }
 

@@ -66,19 +66,6 @@ enum { kLsCandN = 0, kLsCandDone = 1, kLsThrReady = 2, kLsCompDone = 3, kLsInfo1
 __device__ __forceinline__ uint32_t digit1(uint32_t key) { return key >> 21; }
 __device__ __forceinline__ uint32_t digit2(uint32_t key) { return (key >> 10) & (kLsBins - 1); }
 
-// Agent-coherent 4- and 16-byte buffer accesses (sc1: served past the
-// XCD-local L2, like the agent-scope atomic loads and stores).
-constexpr int kCacheCoherent = 16;
-__device__ __forceinline__ uint32_t load1_dev(BufRsrc r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kCacheCoherent);
-}
-__device__ __forceinline__ u32x4 load4_dev(BufRsrc r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCacheCoherent));
-}
-__device__ __forceinline__ void store4_dev(BufRsrc r, uint32_t voff, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kCacheCoherent);
-}
-
 // Poll a counter line until it reaches `target` (thread 0 of the
 // workgroup; bounded).
 __device__ __forceinline__ uint32_t poll_until(const uint32_t* p, uint32_t target) {

@@ -23,7 +23,11 @@ int scan_rows_per_item(int B, int N, int LPR, int nseg) {
   // About 1024 items in all (B of them per row slice when each item scans one
   // sequence), each wave with a short run of rows (whole rows per wave when a
   // row has several segments).
-  const long target_items = 1024;
+  return scan_rows_for_items(B, N, LPR, nseg, 1024);
+}
+
+int scan_rows_for_items(int B, int N, int LPR, int nseg, long target_items) {
+  if (target_items < 1) target_items = 1;
   long per_seq = (target_items + B - 1) / B;
   const int rps = kWave / LPR;
   const long min_rows = (long)kItemWaves * (nseg > 1 ? 1 : rps);
