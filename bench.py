@@ -67,6 +67,12 @@ def decode_bytes(w):
     return per_seq_layer * w.B * w.L, per_seq_layer * w.B
 
 
+# Sources of the one-launch decode layer's kernel (their hash keys the
+# committed counter summaries).
+FUSED_SOURCES = ("fused.hip", "fused_kernel.h", "fused_bf16.hip", "fused_f32.hip",
+                 "decode_items.h", "long_select.h", "select.h", "common.h")
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -215,8 +221,7 @@ def main():
     # One launch per layer: the average launch duration over the timed region.
     layer_avg = secs / (a.steps * w.L)
     layer_gbs = layer_bytes / layer_avg / 1e9
-    traffic = committed_traffic(f"fused_{w.name}",
-                                source_hash("fused.hip", "decode_items.h", "select.h", "common.h"))
+    traffic = committed_traffic(f"fused_{w.name}", source_hash(*FUSED_SOURCES))
     dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     res = {
         "metric": "decode steps/s (retrieval + sparse attention, all layers, whole batch)",

@@ -153,7 +153,9 @@ def test_retrieve_attend_workspace_reuse_and_graph_replay():
             sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
                                d["txt_len"], workspace=ws, out=out[l], idx_out=idx[l])
 
-    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256   # one 128-byte line per word
+    # The tail of the workspace: control words (one 128-byte line each), then
+    # the encoded index copy (B*k words), both zero between launches.
+    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256 + _al256(w.B * w.k * 4)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         step()
@@ -273,7 +275,7 @@ def test_retrieve_attend_long_rows_reuse_and_graph_replay():
     nbytes = sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax)
     ws = sv.new_workspace(nbytes, DEV)
     z0, z1 = _long_zero_span(w.B, w.N, nbytes)
-    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256
+    ctl_bytes = (w.B * (3 + w.Hkv) * 128 + 255) // 256 * 256 + _al256(w.B * w.k * 4)
     idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=DEV) for _ in layers]
     out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV) for _ in layers]
 

@@ -187,18 +187,20 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
 // ---------------------------------------------------------------- fused layer
 // Workspace of sv_retrieve_attend:
 //   [scores B*N][partials][control: seq B | ready B | vis_done B | comb B*Hkv]
+//   [encoded index copy B*k]
 //   [long-row select: control lines and histograms | candidates, chunk offsets],
 // every control word on its own 128-byte line.  The score words, control
-// words, and the long-row control lines and histograms are zero between
-// launches (short rows: the kernel stores scores complemented and zeroes
-// them once read).
+// words, index copy, and the long-row control lines and histograms are zero
+// between launches (short rows: the kernel stores scores complemented and
+// zeroes them once read).
 static size_t fused_ctl_bytes(int B, int Hkv) { return ctr_bytes((size_t)B * (3 + Hkv)); }
+static size_t fused_enc_bytes(int B, int k) { return align256((size_t)B * k * sizeof(uint32_t)); }
 
 size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return 256;
   return retrieve_scores_bytes(B, N) +
          attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true) +
-         fused_ctl_bytes(B, Hkv) + sv::long_select_bytes(B, N);
+         fused_ctl_bytes(B, Hkv) + fused_enc_bytes(B, k) + sv::long_select_bytes(B, N);
 }
 
 sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
@@ -270,6 +272,8 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
   f.vis_done = f.ready + (size_t)B * sv::kCtrStride;
   f.comb_ctr = f.vis_done + (size_t)B * sv::kCtrStride;
   ws += fused_ctl_bytes(B, Hkv);
+  f.idx_enc = (uint32_t*)ws;
+  ws += fused_enc_bytes(B, k);
   f.long_ws = sv::long_select_bytes(B, N) ? ws : nullptr;
   return hip_status(sv::launch_fused(f, (hipStream_t)stream), fn);
 }

@@ -253,6 +253,7 @@ struct FusedLaunch {
   uint32_t* ready;     // [B]
   uint32_t* vis_done;  // [B]
   uint32_t* comb_ctr;  // [B][Hkv]
+  uint32_t* idx_enc;   // [B][k] zero before the launch and after it
   // Rows longer than the single-workgroup select: long_select_bytes(B, N)
   // bytes whose first long_select_zero_bytes(B) are zero before the launch
   // and zero again after it.

@@ -64,6 +64,9 @@ struct ScanArgs {
   // scores' top 11 key bits, which every scan item adds to (long_select.h).
   // Null otherwise.
   uint32_t* hist1;
+  // Fused kernel: [B][k] the selected indices plus one (zero: not written
+  // yet), which the attention items poll; zero again after the launch.
+  uint32_t* idx_enc;
 };
 
 // Chunks of qhat kept in LDS (zero past C).
@@ -316,7 +319,8 @@ __device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float
 #pragma unroll
   for (int i = 0; i < KPT; ++i) w[i] = float_key(__uint_as_float(~w[i]));
   SelectSmem<NW>& sm = *reinterpret_cast<SelectSmem<NW>*>(smem);
-  block_topk<NW, KPT, true, true>(nullptr, N, a.k, a.idx + (int64_t)b * a.k, sm, w);
+  block_topk<NW, KPT, true, true>(nullptr, N, a.k, a.idx + (int64_t)b * a.k, sm, w,
+                                  a.idx_enc ? a.idx_enc + (int64_t)b * a.k : nullptr);
   wait_stores_complete();
   __syncthreads();
   if (tid == 0) store_flag(&a.ready[b * kCtrStride], 1u);
@@ -360,6 +364,7 @@ struct AttnArgs {
   float* out;            // [B][Hq][D]
   uint32_t* ready;       // [B] (stride kCtrStride; fused kernel only)
   uint32_t* vis_done;    // [B] (stride kCtrStride) finished visual items (fused kernel only)
+  const uint32_t* idx_enc;  // [B][k] selected indices plus one, polled (fused kernel only)
 };
 
 template <typename T, int D>
@@ -391,7 +396,7 @@ __host__ __device__ constexpr int combine_groups() {
 }
 
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
-// poll ready[b] (bounded) and read them with device-coherent loads.
+// poll their encoded copy idx_enc (bounded).
 template <typename T, int D, int G, int EPL>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c, bool wait,
                                           char* smem) {
@@ -449,21 +454,31 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
       off[j] = e < n_ent ? (uint32_t)((e0 + e) * ts * ES) + head_off : kBufOob;
     }
   } else {
-    if (wait && n_ent > 0) {
-      if (tid == 0) {
-        uint32_t n = 0;
-        while (load_flag(&a.ready[b * kCtrStride]) == 0u && ++n < kSpinLimit)
-          __builtin_amdgcn_s_sleep(8);
-      }
-      __syncthreads();
-    }
-    const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
     int tok[EPL];
+    if (wait) {
+      // The indices are produced by this kernel: poll this split's words of
+      // the encoded copy until every one is written (bounded); the read that
+      // finds them complete is the one that loads them.
+      const uint32_t* ib = a.idx_enc + (int64_t)b * a.k + e0;
+      for (uint32_t n = 0;; ++n) {
+        bool missing = false;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = (j * kItemWaves + wave) * EPW + eg;
-      tok[j] = -1;
-      if (e < n_ent) tok[j] = wait ? load_shared_dev_i32(ib + e) : ib[e];
+        for (int j = 0; j < EPL; ++j) {
+          const int e = (j * kItemWaves + wave) * EPW + eg;
+          const uint32_t w = e < n_ent ? load_flag(ib + e) : 0u;
+          tok[j] = e < n_ent ? (int)w - 1 : -1;  // -1: no entry
+          missing |= e < n_ent && w == 0u;
+        }
+        if (!__syncthreads_or(missing) || n + 1 >= kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+    } else {
+      const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = (j * kItemWaves + wave) * EPW + eg;
+        tok[j] = e < n_ent ? ib[e] : -1;
+      }
     }
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
@@ -598,56 +613,58 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
   const float* pb = a.part + head0 * C * PS;  // this (b, g): [G][C][PS]
   if (C <= kMaxCombineSplits) {
-    // (m, l) of every split into LDS (all loads in flight); one wave per
-    // head turns m into the weight 2^(m - M) and sums the denominator.
+    // Thread (v, s) sums float4 column v over splits s, s+S, ...; its first
+    // 16 loads go out together with the (m, l) loads of every split (to
+    // LDS), so the merge costs one round trip.  Then one wave per head turns
+    // m into the weight 2^(m - M) and sums the denominator, and the S groups
+    // of a column meet in LDS.
     float* s_f = reinterpret_cast<float*>(smem);  // [G][C]
     float* s_l = s_f + G * kMaxCombineSplits;    // [G][C]
     float* s_den = s_l + G * kMaxCombineSplits;  // [G]
     f32x4v* s_red = reinterpret_cast<f32x4v*>(s_den + 8);
+    constexpr int V = G * D / 4, S = combine_groups<D, G>();
+    const int v = tid % V, s = tid / V;
+    const int i = v / (D / 4), d4 = v % (D / 4);
+    const BufRsrc pr = make_rsrc(pb, (uint32_t)(G * C * PS * 4));
+    const uint32_t col = (uint32_t)(i * C * PS + 4 * d4) * 4u;
+    auto col_load = [&](int cc) {
+      return __builtin_bit_cast(
+          f32x4v, load4_dev(pr, (s < S && cc < C) ? col + (uint32_t)(cc * PS * 4) : kBufOob));
+    };
+    f32x4v x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = col_load(s + j * S);
     for (int t = tid; t < G * C; t += kItemThreads) {
       s_f[t] = load_shared_dev(pb + (int64_t)t * PS + D);
       s_l[t] = load_shared_dev(pb + (int64_t)t * PS + D + 1);
     }
     __syncthreads();
-    for (int i = wave; i < G; i += kItemWaves) {
+    for (int h = wave; h < G; h += kItemWaves) {
       float M = -INFINITY;
-      for (int cc = lane; cc < C; cc += kWave) M = fmaxf(M, s_f[i * C + cc]);
+      for (int cc = lane; cc < C; cc += kWave) M = fmaxf(M, s_f[h * C + cc]);
       M = group_max<kWave>(M);
       float den = 0.f;
       for (int cc = lane; cc < C; cc += kWave) {
-        const float mc = s_f[i * C + cc];
+        const float mc = s_f[h * C + cc];
         const float f = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
-        s_f[i * C + cc] = f;
-        den = fmaf(f, s_l[i * C + cc], den);
+        s_f[h * C + cc] = f;
+        den = fmaf(f, s_l[h * C + cc], den);
       }
       den = group_sum<kWave>(den);
-      if (lane == 0) s_den[i] = den;
+      if (lane == 0) s_den[h] = den;
     }
     __syncthreads();
-    // Numerators: thread (v, s) sums float4 column v over splits s, s+S, ...
-    // with 16 vector loads in flight; the S groups meet in LDS.
-    constexpr int V = G * D / 4, S = combine_groups<D, G>();
-    const int v = tid % V, s = tid / V;
-    const int i = v / (D / 4), d4 = v % (D / 4);
     f32x4v num = {0.f, 0.f, 0.f, 0.f};
-    if (s < S) {
-      const BufRsrc pr = make_rsrc(pb, (uint32_t)(G * C * PS * 4));
-      const uint32_t col = (uint32_t)(i * C * PS + 4 * d4) * 4u;
-      const float* fw = s_f + i * C;
-      for (int c0 = s; c0 < C; c0 += 16 * S) {
-        f32x4v x[16];
+    const float* fw = s_f + i * C;
+    for (int c0 = s;; c0 += 16 * S) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int cc = c0 + j * S;
-          x[j] = __builtin_bit_cast(f32x4v, load4_dev(pr, cc < C ? col + (uint32_t)(cc * PS * 4) : kBufOob));
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int cc = c0 + j * S;
-          const float f = cc < C ? fw[cc] : 0.f;
-          num += f * x[j];
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int cc = c0 + j * S;
+        num += (s < S && cc < C ? fw[cc] : 0.f) * x[j];
       }
+      if (c0 + 16 * S >= C) break;  // no barrier inside: per-thread exit is fine
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = col_load(c0 + 16 * S + j * S);
     }
     if constexpr (S > 1) {
       s_red[tid] = num;
@@ -657,7 +674,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         for (int r = 1; r < S; ++r) num += s_red[r * V + v];
       }
     }
-    if (s == 0 && v < V && tid < V) {
+    if (s == 0 && tid < V) {
       const float den = s_den[i];
       float* o = a.out + (head0 + i) * D + 4 * d4;
 #pragma unroll

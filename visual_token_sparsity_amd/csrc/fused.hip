@@ -63,6 +63,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.idx = f.idx;
   sa.seq_ctr = f.seq_ctr;
   sa.ready = f.ready;
+  sa.idx_enc = f.idx_enc;
   LongSelArgs ls{};
   if (!sa.encode) {
     if (!f.long_ws) return hipErrorInvalidValue;
@@ -114,6 +115,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   aa.comb_ctr = f.comb_ctr;
   aa.out = f.out;
   aa.ready = f.ready;
+  aa.idx_enc = f.idx_enc;
 
   FusedCtl ctl{};
   ctl.vis_done = f.vis_done;

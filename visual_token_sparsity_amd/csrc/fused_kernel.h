@@ -10,7 +10,8 @@
 //     candidate items of each sequence, the threshold items, and the P
 //     compaction items of each sequence;
 //   the text attention items (they need no selection);
-//   the visual attention items, sequence by sequence (each polls ready[b]).
+//   the visual attention items, sequence by sequence (each polls the words
+//     of the encoded index copy it needs).
 // Short rows: there are more scan items than resident workgroups, so the
 // sequences finish their scans one after another and each select overlaps
 // the scans of the sequences behind it.  Scan items store each score
@@ -27,7 +28,8 @@
 // Control words (one 128-byte line each) are zero after every launch:
 // seq_ctr[b] is reset by the selecting workgroup (long rows: the threshold
 // item), comb_ctr[b,g] by the combining one, and vis_done[b] counts visual
-// items past their wait, the last of which lowers ready[b] again.
+// items past their wait, the last of which lowers ready[b] again and clears
+// the encoded index copy the visual items poll.
 // Complemented scores are zeroed by the select item that read them; the
 // long-row histograms and counters by the threshold and compaction items.
 #pragma once
@@ -83,12 +85,19 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   const int b = u / (per * aa.Hkv);
   const int g = (u / per) % aa.Hkv;
   attn_item<T, D, G, EPL>(aa, b, g, (text ? 0 : aa.CT) + u % per, !text, smem);
-  if (!text && threadIdx.x == 0) {
-    uint32_t* vd = ctl.vis_done + b * kCtrStride;
-    if (counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1) {
-      store_flag(aa.ready + b * kCtrStride, 0u);
-      counter_reset(vd);
-    }
+  if (text) return;
+  // The last visual item of b (every other one has read its indices) clears
+  // the encoded index copy, ready[b] and the count for the next launch.
+  __shared__ uint32_t s_last;
+  uint32_t* vd = ctl.vis_done + b * kCtrStride;
+  if (threadIdx.x == 0) s_last = counter_add(vd, 1u) == (uint32_t)(aa.CV * aa.Hkv) - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  uint32_t* enc = const_cast<uint32_t*>(aa.idx_enc) + (int64_t)b * aa.k;
+  for (int i = threadIdx.x; i < aa.k; i += kItemThreads) store_flag(enc + i, 0u);
+  if (threadIdx.x == 0) {
+    store_flag(aa.ready + b * kCtrStride, 0u);
+    counter_reset(vd);
   }
 }
 

@@ -325,7 +325,8 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
     __syncthreads();  // the select reuses the LDS
     SelectSmem<kItemWaves>& ss = *reinterpret_cast<SelectSmem<kItemWaves>*>(smem);
     block_topk<kItemWaves, kSelKpt, true, false>(a.scores + (int64_t)b * a.N, a.N, a.k,
-                                                 a.idx + (int64_t)b * a.k, ss);
+                                                 a.idx + (int64_t)b * a.k, ss, nullptr,
+                                                 a.idx_enc ? a.idx_enc + (int64_t)b * a.k : nullptr);
   }
   wait_stores_complete();
   __syncthreads();
@@ -389,9 +390,13 @@ __device__ __forceinline__ void compact_item(const ScanArgs& a, const LongSelArg
     for (int i = 0; i < kSelKpt; ++i) {
       const uint64_t bm = __ballot(sel[i]);
       const uint32_t o = pos + (uint32_t)__popcll(bm & lt);
-      if (sel[i] && o < (uint32_t)a.k)
+      if (sel[i] && o < (uint32_t)a.k) {
         __hip_atomic_store(out + o, (int32_t)(e0 + i * kWave), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+        if (a.idx_enc)
+          __hip_atomic_store(a.idx_enc + (int64_t)b * a.k + o, (uint32_t)(e0 + i * kWave) + 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       pos += (uint32_t)__popcll(bm);
     }
   }

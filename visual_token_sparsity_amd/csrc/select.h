@@ -90,10 +90,12 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* h, int nb, uint3
 // re-read on every pass.  pre: the caller already holds the keys of a cached
 // row, in this layout; vals is then not read.  out == nullptr: compute
 // everything, write nothing (runs the code once, e.g. to warm the
-// instruction cache while waiting for the scores).
+// instruction cache while waiting for the scores).  out_enc: also write
+// each index plus one there (device-coherent; zero means not written).
 template <int NW, int KPT, bool Coherent, bool Cached>
 __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int32_t* __restrict__ out,
-                           SelectSmem<NW>& sm, const uint32_t* pre = nullptr) {
+                           SelectSmem<NW>& sm, const uint32_t* pre = nullptr,
+                           uint32_t* __restrict__ out_enc = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -295,6 +297,8 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
         __hip_atomic_store(out + pos, (int32_t)e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
         out[pos] = e;
+      if (out_enc)
+        __hip_atomic_store(out_enc + pos, (uint32_t)e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     before += __popcll(bm);
   });
