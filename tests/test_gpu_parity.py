@@ -366,10 +366,31 @@ def test_salience_large_logits_use_exact_row_max(mode):
     assert ok, msgs[:3]
 
 
+def test_salience_mixed_items_split_between_kernels():
+    """One (frame, head) item with large logits among ordinary ones: the fp16
+    row kernel computes the ordinary items and flags the large one for the fp32
+    kernel; both write the same column-sum buffer."""
+    w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=3, H=2)
+    Q, K = synthetic.make_salience(w, seed=12)
+    Q = Q.float()
+    Q[1, 0] *= 12.0
+    Q = Q.to(torch.bfloat16)
+    _say("salience mixed items")
+    s_ref = oracle.salience(Q, K)
+    for _ in range(2):  # the flags are rewritten by every call
+        sal, idx = sv.salience_prune(Q.to(DEV), K.to(DEV), w.keep)
+        torch.cuda.synchronize()
+        ok, rel, sm = accept.check_salience(sal.cpu().numpy(), s_ref)
+        assert ok, (rel, sm)
+        ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.keep)
+        assert ok, msgs[:3]
+
+
 @pytest.mark.parametrize("D", [64, 72, 80, 96])
-@pytest.mark.parametrize("N", [32, 129, 729])
+@pytest.mark.parametrize("N", [32, 129, 250, 256, 729])
 def test_salience_head_dim_grid(D, N):
-    """Every head dim of the column-stationary kernel, with and without ragged tiles."""
+    """Every head dim of both on-chip kernels (the row kernel takes N = 241..256 and
+    721..736), with and without a ragged last tile."""
     w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=1, H=2, N=N, D=D, keep=N // 2)
     _say("salience grid", N, D)
     Q, K = synthetic.make_salience(w, seed=3)

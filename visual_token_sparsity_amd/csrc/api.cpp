@@ -281,7 +281,8 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
 // ---------------------------------------------------------------- salience
 size_t sv_salience_prune_workspace(int F, int H, int N) {
   if (F < 1 || H < 1 || N < 1) return 256;
-  return align256((size_t)F * H * N * sizeof(float)) + align256((size_t)F * N * sizeof(float));
+  return align256((size_t)F * H * N * sizeof(float)) + align256((size_t)F * N * sizeof(float)) +
+         align256((size_t)F * H * sizeof(int32_t));
 }
 
 sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, int N, int D,
@@ -303,11 +304,12 @@ sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, 
   if (workspace_bytes < need)
     return fail(SV_EWORKSPACE, "sv_salience_prune: workspace %zu < %zu bytes", workspace_bytes, need);
   float* colsum = (float*)workspace;
-  float* sal = salience_out ? salience_out
-                            : (float*)((char*)workspace + align256((size_t)F * H * N * sizeof(float)));
+  char* sal_ws = (char*)workspace + align256((size_t)F * H * N * sizeof(float));
+  float* sal = salience_out ? salience_out : (float*)sal_ws;
+  int32_t* redo = (int32_t*)(sal_ws + align256((size_t)F * N * sizeof(float)));
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   hipStream_t st = (hipStream_t)stream;
-  sv_status s = hip_status(sv::launch_salience(vis_q, vis_k, F, H, N, D, sc, colsum, sal, st),
+  sv_status s = hip_status(sv::launch_salience(vis_q, vis_k, F, H, N, D, sc, colsum, redo, sal, st),
                            "sv_salience_prune salience");
   if (s != SV_OK) return s;
   return hip_status(sv::launch_topk_rows(sal, F, N, N, keep, idx_out, st), "sv_salience_prune select");

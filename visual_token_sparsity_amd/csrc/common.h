@@ -268,6 +268,7 @@ size_t long_select_zero_bytes(int B, int N);
 bool salience_supported(int N, int D);
 
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D,
-                           float scale, float* colsum_ws, float* sal, hipStream_t stream);
+                           float scale, float* colsum_ws, int32_t* redo_ws, float* sal,
+                           hipStream_t stream);
 
 }  // namespace sv

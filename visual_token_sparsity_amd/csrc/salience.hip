@@ -208,6 +208,11 @@ __global__ __launch_bounds__(kSalWaves* kWave, 1) void salience_colsum_kernel(
 // ----------------------------------------------------------------------------
 constexpr int kColWaves = 8;  // waves per workgroup, each owning a column slice
 constexpr int kRowBlocks = 1;  // 16-row blocks per iteration
+#ifndef SV_SAL_PREFETCH
+#define SV_SAL_PREFETCH 2
+#endif
+constexpr int kPrefetch = SV_SAL_PREFETCH;  // iterations of query fragments in flight
+static_assert(kPrefetch == 1 || kPrefetch == 2 || kPrefetch == 4, "ring slots must divide the unroll");
 
 __device__ __forceinline__ float sumsq8(const bf16x8& v) {
   float s = 0.f;
@@ -240,7 +245,7 @@ __device__ __forceinline__ float row16_max(float v) {
 template <int D, int TPW>
 __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
-    float* __restrict__ colsum) {
+    float* __restrict__ colsum, const int32_t* __restrict__ only) {
   // 32-wide k-steps; lanes whose 8-element chunk lies beyond D feed zeros.
   constexpr int KS = (D + 31) / 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -313,10 +318,16 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
     return acc;
   };
 
-  int item = blockIdx.x;
+  // With `only`, items whose flag is 0 are skipped (another kernel computed them).
+  auto next_item = [&](int i) {
+    if (only)
+      while (i < FH && only[i] == 0) i += gridDim.x;
+    return i;
+  };
+  int item = next_item(blockIdx.x);
   if (item < FH) stage_keys(item);
   int buf = 0, par = 0;
-  for (; item < FH; item += gridDim.x, par ^= 1) {
+  for (int nxt; item < FH; item = nxt, par ^= 1) {
     wait_stores_complete();  // this wave's direct loads have landed (vmcnt = 0)
     __syncthreads();
     const bf16_t* q = Qg + (int64_t)item * N * D;
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
     const float kc = __builtin_amdgcn_sqrtf(__uint_as_float(maxu[2 * par])) * c2 * 1.0009765625f;
     const float cmax = __builtin_amdgcn_sqrtf(__uint_as_float(maxu[2 * par + 1])) * kc;
     if (tid < 2) maxu[2 * (par ^ 1) + tid] = 0u;
-    const int nxt = item + gridDim.x;
+    nxt = next_item(item + gridDim.x);
     if (nxt < FH) stage_keys(nxt);
 
     float colacc[TPW];
@@ -386,11 +397,16 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
       for (int t = 0; t < TPW; ++t) npad += (c0 + 16 * t + li >= N) ? 1 : 0;
       const float fpad = (float)npad;
       const bool padw = __any(npad > 0);  // only the wave(s) owning columns >= N
-      bf16x8 af[kRowBlocks][KS];
+      // Query fragments are prefetched kPrefetch iterations ahead into a ring
+      // of register slots (slot = iteration mod kPrefetch): a row block that
+      // misses in L2 has several iterations to arrive.
+      bf16x8 afr[kPrefetch][kRowBlocks][KS];
 #pragma unroll
-      for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, h, af[h]);
+      for (int sl = 0; sl < kPrefetch; ++sl)
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * sl + h, afr[sl][h]);
 
-      auto mfma_phase = [&](f32x4 (&S)[kRowBlocks][TPW], int it) {
+      auto mfma_phase = [&](f32x4 (&S)[kRowBlocks][TPW], bf16x8 (&af)[kRowBlocks][KS], int it) {
 #pragma unroll
         for (int h = 0; h < kRowBlocks; ++h) {
 #pragma unroll
@@ -402,9 +418,9 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
             S[h][t] = acc;
           }
         }
-        // The A fragments are consumed: the next row blocks load into the same registers.
+        // The slot is consumed: the row blocks kPrefetch iterations ahead load into it.
 #pragma unroll
-        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * (it + 1) + h, af[h]);
+        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * (it + kPrefetch) + h, af[h]);
       };
       auto update_phase = [&](const f32x4 (&S)[kRowBlocks][TPW], const float (&f)[kRowBlocks][4]) {
 #pragma unroll
@@ -483,32 +499,23 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
         }
       };
 
-      f32x4 SA[kRowBlocks][TPW], SB[kRowBlocks][TPW];
-      float fA[kRowBlocks][4], fB[kRowBlocks][4];
-      // MFMA(it) | wait for it-1's partials, weights, column update of it-1 | publish(it)
-      mfma_phase(SA, 0);
-      publish(SA, 0);
-      int it = 1;
-      for (; it + 1 < iters; it += 2) {
-        mfma_phase(SB, it);
-        collect(it - 1, fA);
-        update_phase(SA, fA);
-        publish(SB, it);
-        mfma_phase(SA, it + 1);
-        collect(it, fB);
-        update_phase(SB, fB);
-        publish(SA, it + 1);
-      }
-      if (it < iters) {
-        mfma_phase(SB, it);
-        collect(it - 1, fA);
-        update_phase(SA, fA);
-        publish(SB, it);
-        collect(it, fB);
-        update_phase(SB, fB);
-      } else {
-        collect(it - 1, fA);
-        update_phase(SA, fA);
+      f32x4 S2[2][kRowBlocks][TPW];
+      float f2[2][kRowBlocks][4];
+      // Iteration it: MFMA(it) | wait for it-1's partials, weights, column
+      // update of it-1 | publish(it).  Unrolled by kUnroll so the ring slot
+      // (it mod kPrefetch) and the score buffer (it mod 2) are static.
+      constexpr int kUnroll = kPrefetch > 2 ? kPrefetch : 2;
+      for (int base = 0; base <= iters; base += kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int it = base + u;
+          if (it < iters) mfma_phase(S2[u & 1], afr[u % kPrefetch], it);
+          if (it >= 1 && it <= iters) {
+            collect(it - 1, f2[(u + 1) & 1]);
+            update_phase(S2[(u + 1) & 1], f2[(u + 1) & 1]);
+          }
+          if (it < iters) publish(S2[u & 1], it);
+        }
       }
       __syncthreads();  // every wave is done with the partials and the counter
       if (tid == 0) *arrived = 0u;  // ordered before the next publish by the item-start barrier
@@ -596,6 +603,228 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------
+// Row-stationary variant with MFMA column sums (D in {64, 72, 80, 96}).
+//
+// One workgroup of 8 waves per CU loops over (frame, head) items.  The item's
+// keys sit in LDS.  A wave owns a 16-row block of queries at a time and sweeps
+// every key column itself, so a row's softmax denominator is complete inside
+// the wave: no exchange between waves, no barrier per row block.
+//
+// Per 16x16 tile of S = Q K^T (bf16 MFMA, fp32 accumulate):
+//     p = 2^(S * scale * log2(e) - b_i)          (one exp per element)
+//     P tile kept in registers as fp16 (round to nearest even)
+//     l_i += p, summed in fp32 over the rounded fp16 values
+// After the sweep the row weights w_i = 1/l_i are known, and the column sums
+// c_j += sum_i w_i p_ij are one fp16 MFMA per tile: the P tile, as it comes
+// out of the score MFMA, is already the B operand of v_mfma_f32_16x16x16_f16
+// with the 16 rows of the block as the reduction index; the A operand holds
+// w split into an fp16 high part (row 0) and the fp16 residual (row 1).
+//
+// Shift b_i.  Softmax is shift-invariant.  b_i = |q_i| * max_j |k_j| * scale
+// (log2 units, times 1 + 2^-10 for rounding) bounds |S_ij * scale| by
+// Cauchy-Schwarz, so every exponent lies in [-2 b_i, 0].  With b_i <= 7 every
+// p is a normal fp16 number, whose rounding (relative 2^-11) averages out
+// over the rows of a column.  An item with a row above that bound is flagged
+// and left to the fp32 column-stationary kernel, launched right after.
+//
+// The kernel is compiled for an exact tile count (ceil(N/16)), so only the
+// last tile can hold columns >= N; their probabilities are set to zero there.
+// ----------------------------------------------------------------------------
+constexpr int kRowWaves = 8;
+constexpr float kHalfBound = 7.f;  // b_i limit: p >= 2^-14, a normal fp16
+
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+__device__ __forceinline__ f16x4 pack_f16x4(float a, float b, float c, float d) {
+  const f16x2 lo = __builtin_convertvector((f32x2){a, b}, f16x2);  // v_cvt_pk_f16_f32
+  const f16x2 hi = __builtin_convertvector((f32x2){c, d}, f16x2);
+  return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int D, int NTILE>
+__global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
+    const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
+    float* __restrict__ colsum, int32_t* __restrict__ redo) {
+  constexpr int KS = (D + 31) / 32;
+  constexpr int NT = kRowWaves * kWave;
+  constexpr int NC = NTILE * 16;  // key columns rounded up to whole tiles
+  static_assert(D % 8 == 0, "D must be a multiple of 8");
+  extern __shared__ uint4 smem_u4[];
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem_u4);                      // [NC][D] keys
+  float* cacc = reinterpret_cast<float*>(sK + NC * D);                   // [kRowWaves][NC] wave sums
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(cacc + kRowWaves * NC);    // max|k|^2, redo
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const int RB = (N + 15) / 16;
+  const int kbytes = N * D * 2;
+  float* myacc = cacc + wave * NC;
+
+  // Key rows N..NC-1 stay zero for every item.
+  for (int c = N * D / 8 + tid; c < NC * D / 8; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
+
+  // A fragments of row block rb: lane (li, lg) holds row 16 rb + li, dims
+  // 32 s + 8 lg .. +7.  Rows >= N and dims >= D read as zeros.
+  auto load_a = [&](const bf16_t* q, int rb, bf16x8 (&af)[KS]) {
+    const int row = rb * 16 + li;
+    const bool ok = row < N;
+    const int64_t rowc = ok ? row : 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int dd = 32 * s + 8 * lg;
+      const bool in = ok && dd < D;
+      const uint4 u = *reinterpret_cast<const uint4*>(q + rowc * D + (dd < D ? dd : 0));
+      af[s] = __builtin_bit_cast(bf16x8, in ? u : make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  for (int item = blockIdx.x; item < FH; item += gridDim.x) {
+    const bf16_t* q = Qg + (int64_t)item * N * D;
+    bf16x8 af[KS];
+    load_a(q, wave, af);  // in flight during the key staging
+    float colacc[NTILE];  // this wave's column sums (lanes 0-15: column 16 t + li)
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) colacc[t] = 0.f;
+    __syncthreads();      // the previous item is done with sK, cacc and ctl
+    if (tid < 2) ctl[tid] = 0u;
+    {
+      const char* src = reinterpret_cast<const char*>(Kg + (int64_t)item * N * D);
+      char* dst = reinterpret_cast<char*>(sK);
+      for (int chunk = wave; chunk * 1024 < kbytes; chunk += kRowWaves) {
+        const int off = chunk * 1024 + lane * 16;
+        if (off < kbytes) __builtin_amdgcn_global_load_lds(src + off, dst + chunk * 1024, 16, 0, 0);
+      }
+    }
+    wait_stores_complete();  // this wave's direct loads have landed (vmcnt = 0)
+    __syncthreads();
+    float kn2 = 0.f;
+    for (int r = tid; r < N; r += NT) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) n2 += sumsq8(load_bf16x8(sK + r * D + 8 * c));
+      kn2 = fmaxf(kn2, n2);
+    }
+    kn2 = group_max<kWave>(kn2);
+    if (lane == 0) atomicMax(&ctl[0], __float_as_uint(kn2));  // non-negative: uint order
+    __syncthreads();
+    const float kc = __builtin_amdgcn_sqrtf(__uint_as_float(ctl[0])) * c2 * 1.0009765625f;
+
+    for (int rb = wave; rb < RB; rb += kRowWaves) {
+      // |q|^2 of row li: the 4 lanes li + 16 lg hold its chunks.
+      float n2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) n2 += sumsq8(af[s]);
+      n2 += __shfl_xor(n2, 16, kWave);
+      n2 += __shfl_xor(n2, 32, kWave);
+      // Output rows of this lane are 4 lg + r.
+      float b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[r] = __builtin_amdgcn_sqrtf(__shfl(n2, 4 * lg + r, kWave)) * kc;
+      if (__any(fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])) > kHalfBound)) {
+        if (lane == 0) ctl[1] = 1u;
+      }
+      bf16x8 an[KS];
+      load_a(q, rb + kRowWaves, an);  // next row block (zeros past the end)
+
+      // Software pipeline over column tiles: step t issues the LDS reads of
+      // tile t+2 and the MFMAs of tile t+1, then the exps of tile t, so the
+      // matrix core and the LDS work under the VALU.  A scheduling barrier
+      // closes each step (it keeps the compiler from hoisting every tile's
+      // reads, which would run out of registers).
+      f16x4 P[NTILE];
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      // An opaque 1.0 keeps fma(f16 -> f32, 1, acc) as one v_fma_mix_f32
+      // instead of a conversion plus an add.
+      float one = 1.0f;
+      asm volatile("" : "+v"(one));
+      bf16x8 bkb[3][KS];
+      // Lanes whose dims lie beyond D read any finite key data: their query
+      // partners in A are zero, so the products vanish.
+      // The lane's row offset is made opaque once per row block so the
+      // compiler does not keep one address register per tile live.
+      int lrow = li * D;
+      asm volatile("" : "+v"(lrow));
+      auto lds_b = [&](int t, bf16x8 (&bk)[KS]) {
+        const bf16_t* kr = sK + lrow + 16 * t * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int dd = 32 * s + 8 * lg;
+          bk[s] = load_bf16x8(kr + (dd < D ? dd : 0));
+        }
+      };
+      auto mm = [&](const bf16x8 (&bk)[KS]) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bk[s], a, 0, 0, 0);
+        return a;
+      };
+      lds_b(0, bkb[0]);
+      if (NTILE > 1) lds_b(1, bkb[1]);
+      f32x4 acc = mm(bkb[0]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        if (t + 2 < NTILE) lds_b(t + 2, bkb[(t + 2) % 3]);
+        f32x4 accn = acc;
+        if (t + 1 < NTILE) accn = mm(bkb[(t + 1) % 3]);
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(acc[r], c2, -b[r]));
+        if (t == NTILE - 1) {  // the last tile may hold columns >= N
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[r] = 16 * t + li < N ? p[r] : 0.f;
+        }
+        P[t] = pack_f16x4(p[0], p[1], p[2], p[3]);
+        // Row sums of the rounded values the column MFMA will see, so every
+        // normalised row sums to 1 up to fp32 rounding (v_fma_mix_f32).
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rs[r] = fmaf((float)P[t][r], one, rs[r]);
+        acc = accn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Row weights.
+      f16x4 wa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l = row16_sum(rs[r]);
+        const int row = rb * 16 + 4 * lg + r;
+        const float w = row < N ? __builtin_amdgcn_rcpf(l) : 0.f;
+        const _Float16 hi = (_Float16)w;
+        const _Float16 lo = (_Float16)(w - (float)hi);
+        wa[r] = li == 0 ? hi : (li == 1 ? lo : (_Float16)0.f);
+      }
+      // Column sums: C[0][j] + C[1][j] sit in lanes 0-15 (registers 0 and 1);
+      // lanes 16-63 hold rows 4..15 of C, exactly zero (A rows >= 2 are zero).
+      // They accumulate in registers across the wave's row blocks (LDS float
+      // atomics serialise per lane and would stall the whole CU).
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, P[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        colacc[t] += c[0] + c[1];
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) af[s] = an[s];
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) myacc[16 * t + li] = colacc[t];
+    }
+    __syncthreads();
+    const bool bad = ctl[1] != 0u;
+    for (int j = tid; j < N; j += NT) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) sum += cacc[w * NC + j];
+      if (!bad) colsum[(int64_t)item * N + j] = sum;
+    }
+    if (tid == 0) redo[item] = bad ? 1 : 0;
+  }
+}
+
 // sal[f][j] = (1 / (H*N)) * sum_h colsum[f][h][j]
 __global__ __launch_bounds__(256) void salience_mean_kernel(const float* __restrict__ colsum,
                                                            int H, int N, float inv,
@@ -673,7 +902,7 @@ static size_t colstat_lds_bytes(int tpw, int D) {
 
 template <int D, int TPW>
 static hipError_t colstat_go(const void* q, const void* k, int FH, int N, float c2, float* colsum,
-                             hipStream_t st) {
+                             const int32_t* only, hipStream_t st) {
   const size_t lds = colstat_lds_bytes(TPW, D);
   static bool attr_set = false;
   if (!attr_set) {
@@ -685,19 +914,19 @@ static hipError_t colstat_go(const void* q, const void* k, int FH, int N, float 
   int grid = device_cu_count();
   if (grid > FH) grid = FH;
   hipLaunchKernelGGL((salience_colstat_kernel<D, TPW>), dim3(grid), dim3(kColWaves * kWave), lds, st,
-                     (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum);
+                     (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum, only);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t colstat_tpw(int tpw, const void* q, const void* k, int FH, int N, float c2,
-                              float* colsum, hipStream_t st) {
+                              float* colsum, const int32_t* only, hipStream_t st) {
   switch (tpw) {
-    case 1: return colstat_go<D, 1>(q, k, FH, N, c2, colsum, st);
-    case 2: return colstat_go<D, 2>(q, k, FH, N, c2, colsum, st);
-    case 3: return colstat_go<D, 3>(q, k, FH, N, c2, colsum, st);
-    case 4: return colstat_go<D, 4>(q, k, FH, N, c2, colsum, st);
-    case 6: return colstat_go<D, 6>(q, k, FH, N, c2, colsum, st);
+    case 1: return colstat_go<D, 1>(q, k, FH, N, c2, colsum, only, st);
+    case 2: return colstat_go<D, 2>(q, k, FH, N, c2, colsum, only, st);
+    case 3: return colstat_go<D, 3>(q, k, FH, N, c2, colsum, only, st);
+    case 4: return colstat_go<D, 4>(q, k, FH, N, c2, colsum, only, st);
+    case 6: return colstat_go<D, 6>(q, k, FH, N, c2, colsum, only, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -709,33 +938,86 @@ static bool colstat_ok(int N, int D) {
   return tpw > 0 && colstat_lds_bytes(tpw, D) <= (size_t)kSalMaxLds;
 }
 
+static hipError_t colstat_any(const void* q, const void* k, int FH, int N, int D, float c2,
+                              float* colsum, const int32_t* only, hipStream_t st) {
+  const int tpw = pick_tpw_colstat(N);
+  switch (D) {
+    case 64: return colstat_tpw<64>(tpw, q, k, FH, N, c2, colsum, only, st);
+    case 72: return colstat_tpw<72>(tpw, q, k, FH, N, c2, colsum, only, st);
+    case 80: return colstat_tpw<80>(tpw, q, k, FH, N, c2, colsum, only, st);
+    default: return colstat_tpw<96>(tpw, q, k, FH, N, c2, colsum, only, st);
+  }
+}
+
+// Row-stationary kernel: compiled for an exact number of 16-key column tiles,
+// 16 (N in 241..256) or 46 (N in 721..736, e.g. 27 x 27 = 729 patches).
+static int pick_ntm_rows(int N) {
+  const int nt = (N + 15) / 16;
+  return (nt == 16 || nt == 46) ? nt : -1;
+}
+
+static size_t rows_lds_bytes(int ntm, int D) {
+  return (size_t)ntm * 16 * D * 2 + (size_t)kRowWaves * ntm * 16 * 4 + 16;
+}
+
+static bool rows_ok(int N, int D) {
+  if (D != 64 && D != 72 && D != 80 && D != 96) return false;
+  const int ntm = pick_ntm_rows(N);
+  return ntm > 0 && rows_lds_bytes(ntm, D) <= (size_t)kSalMaxLds && colstat_ok(N, D);
+}
+
+template <int D, int NTM>
+static hipError_t rows_go(const void* q, const void* k, int FH, int N, float c2, float* colsum,
+                          int32_t* redo, hipStream_t st) {
+  const size_t lds = rows_lds_bytes(NTM, D);
+  if (lds > (size_t)kSalMaxLds) return hipErrorInvalidValue;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)salience_rows_kernel<D, NTM>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSalMaxLds);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  int grid = device_cu_count();
+  if (grid > FH) grid = FH;
+  hipLaunchKernelGGL((salience_rows_kernel<D, NTM>), dim3(grid), dim3(kRowWaves * kWave), lds, st,
+                     (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum, redo);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t rows_ntm(const void* q, const void* k, int FH, int N, float c2, float* colsum,
+                           int32_t* redo, hipStream_t st) {
+  return pick_ntm_rows(N) == 16 ? rows_go<D, 16>(q, k, FH, N, c2, colsum, redo, st)
+                                : rows_go<D, 46>(q, k, FH, N, c2, colsum, redo, st);
+}
+
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D, float scale,
-                           float* colsum_ws, float* sal, hipStream_t st) {
+                           float* colsum_ws, int32_t* redo_ws, float* sal, hipStream_t st) {
   const float c2 = scale * 1.4426950408889634f;
   const int FH = F * H;
   hipError_t e;
-  if (colstat_ok(N, D)) {
-    const int tpw = pick_tpw_colstat(N);
+  if (rows_ok(N, D)) {
+    // fp16-probability row kernel, then the fp32 kernel on the items it flagged.
     switch (D) {
-      case 64: e = colstat_tpw<64>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
-      case 72: e = colstat_tpw<72>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
-      case 80: e = colstat_tpw<80>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
-      default: e = colstat_tpw<96>(tpw, q, k, FH, N, c2, colsum_ws, st); break;
+      case 64: e = rows_ntm<64>(q, k, FH, N, c2, colsum_ws, redo_ws, st); break;
+      case 72: e = rows_ntm<72>(q, k, FH, N, c2, colsum_ws, redo_ws, st); break;
+      case 80: e = rows_ntm<80>(q, k, FH, N, c2, colsum_ws, redo_ws, st); break;
+      default: e = rows_ntm<96>(q, k, FH, N, c2, colsum_ws, redo_ws, st); break;
     }
-    if (e != hipSuccess) return e;
-    dim3 grid((N + 255) / 256, F);
-    hipLaunchKernelGGL(salience_mean_kernel, grid, dim3(256), 0, st, colsum_ws, H, N,
-                       1.0f / ((float)H * (float)N), sal);
-    return hipGetLastError();
-  }
-  switch (pick_tpw(N)) {
-    case 4: e = sal_ks<4>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    case 8: e = sal_ks<8>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    case 12: e = sal_ks<12>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    case 16: e = sal_ks<16>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    case 23: e = sal_ks<23>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    case 24: e = sal_ks<24>(q, k, FH, N, D, c2, colsum_ws, st); break;
-    default: return hipErrorInvalidValue;
+    if (e == hipSuccess) e = colstat_any(q, k, FH, N, D, c2, colsum_ws, redo_ws, st);
+  } else if (colstat_ok(N, D)) {
+    e = colstat_any(q, k, FH, N, D, c2, colsum_ws, nullptr, st);
+  } else {
+    switch (pick_tpw(N)) {
+      case 4: e = sal_ks<4>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      case 8: e = sal_ks<8>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      case 12: e = sal_ks<12>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      case 16: e = sal_ks<16>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      case 23: e = sal_ks<23>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      case 24: e = sal_ks<24>(q, k, FH, N, D, c2, colsum_ws, st); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   if (e != hipSuccess) return e;
   dim3 grid((N + 255) / 256, F);
