@@ -292,7 +292,7 @@ def bench_salience(a, dev, stream):
     return {"workload": sw.name, "frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
             "head_dim": sw.D, "keep": sw.keep, "ms_per_call": round(secs * 1e3, 4),
             "tokens_per_s": round(sw.F * sw.N / secs, 1),
-            "roofline": {"kernel": "salience_colsum_kernel + mean + top-k (whole call)",
+            "roofline": {"kernel": "salience_rows_kernel (+ flagged-item fp32 pass, head mean, per-frame top-k): whole call",
                          "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "flops_algorithmic": flops}}

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kSalWaves* kWave, 1) void salience_colsum_kernel(
 constexpr int kColWaves = 8;  // waves per workgroup, each owning a column slice
 constexpr int kRowBlocks = 1;  // 16-row blocks per iteration
 #ifndef SV_SAL_PREFETCH
-#define SV_SAL_PREFETCH 2
+#define SV_SAL_PREFETCH 1
 #endif
 constexpr int kPrefetch = SV_SAL_PREFETCH;  // iterations of query fragments in flight
 static_assert(kPrefetch == 1 || kPrefetch == 2 || kPrefetch == 4, "ring slots must divide the unroll");
@@ -633,7 +633,6 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
 // ----------------------------------------------------------------------------
 constexpr int kRowWaves = 8;
 constexpr float kHalfBound = 7.f;  // b_i limit: p >= 2^-14, a normal fp16
-
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -648,14 +647,15 @@ template <int D, int NTILE>
 __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
     float* __restrict__ colsum, int32_t* __restrict__ redo) {
+  // 32-wide k-steps; lanes whose 8 dims lie beyond D get zero query data.
   constexpr int KS = (D + 31) / 32;
   constexpr int NT = kRowWaves * kWave;
   constexpr int NC = NTILE * 16;  // key columns rounded up to whole tiles
   static_assert(D % 8 == 0, "D must be a multiple of 8");
   extern __shared__ uint4 smem_u4[];
-  bf16_t* sK = reinterpret_cast<bf16_t*>(smem_u4);                      // [NC][D] keys
-  float* cacc = reinterpret_cast<float*>(sK + NC * D);                   // [kRowWaves][NC] wave sums
-  uint32_t* ctl = reinterpret_cast<uint32_t*>(cacc + kRowWaves * NC);    // max|k|^2, redo
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem_u4);                    // [NC][D] keys
+  float* cacc = reinterpret_cast<float*>(sK + NC * D);                 // [kRowWaves][NC] wave sums
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(cacc + kRowWaves * NC);  // max|k|^2, redo
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       for (int s = 0; s < KS; ++s) n2 += sumsq8(af[s]);
       n2 += __shfl_xor(n2, 16, kWave);
       n2 += __shfl_xor(n2, 32, kWave);
-      // Output rows of this lane are 4 lg + r.
+      // Output rows of this lane are 16 rb + 4 lg + r.
       float b[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) b[r] = __builtin_amdgcn_sqrtf(__shfl(n2, 4 * lg + r, kWave)) * kc;
@@ -743,12 +743,12 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       float one = 1.0f;
       asm volatile("" : "+v"(one));
       bf16x8 bkb[3][KS];
-      // Lanes whose dims lie beyond D read any finite key data: their query
-      // partners in A are zero, so the products vanish.
       // The lane's row offset is made opaque once per row block so the
       // compiler does not keep one address register per tile live.
       int lrow = li * D;
       asm volatile("" : "+v"(lrow));
+      // Lanes whose dims lie beyond D read any finite key data: their query
+      // partners in A are zero, so the products vanish.
       auto lds_b = [&](int t, bf16x8 (&bk)[KS]) {
         const bf16_t* kr = sK + lrow + 16 * t * D;
 #pragma unroll
@@ -786,7 +786,8 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
         acc = accn;
         __builtin_amdgcn_sched_barrier(0);
       }
-      // Row weights.
+      // Row weights w = 1/l, split into an fp16 high part (A row 0) and the
+      // fp16 residual (A row 1) over the 16 rows of the block.
       f16x4 wa;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -969,6 +970,8 @@ static bool rows_ok(int N, int D) {
 template <int D, int NTM>
 static hipError_t rows_go(const void* q, const void* k, int FH, int N, float c2, float* colsum,
                           int32_t* redo, hipStream_t st) {
+  int grid = device_cu_count();
+  if (grid > FH) grid = FH;
   const size_t lds = rows_lds_bytes(NTM, D);
   if (lds > (size_t)kSalMaxLds) return hipErrorInvalidValue;
   static bool attr_set = false;
@@ -978,8 +981,6 @@ static hipError_t rows_go(const void* q, const void* k, int FH, int N, float c2,
     (void)hipGetLastError();
     attr_set = true;
   }
-  int grid = device_cu_count();
-  if (grid > FH) grid = FH;
   hipLaunchKernelGGL((salience_rows_kernel<D, NTM>), dim3(grid), dim3(kRowWaves * kWave), lds, st,
                      (const bf16_t*)q, (const bf16_t*)k, FH, N, c2, colsum, redo);
   return hipGetLastError();
