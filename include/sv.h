@@ -82,10 +82,15 @@ const char* sv_last_error(void);
  *  scores_out optional [B][N] fp32 scores s (NULL to skip).
  *  workspace  at least sv_retrieve_workspace(B, N, k) bytes, 256-byte
  *             aligned, ZERO-FILLED before its first use.  It holds the
- *             scores and one completion counter per sequence; every call
- *             returns the counters to zero, so the same workspace can be
- *             reused (and a call can be captured in a HIP graph) without
- *             clearing it again.
+ *             scores and one completion counter per sequence and, for rows
+ *             of more than 2048 tokens, the histograms, counters and
+ *             candidate lists of the parallel select; every call returns
+ *             the counters and histograms to zero, so the same workspace can
+ *             be reused for calls of the same B and N (and a call can be
+ *             captured in a HIP graph) without clearing it again.
+ * Rows of more than 2048 tokens with Hq/Hkv <= 8 and k > 0 are selected by
+ * many workgroups (each pass over a row split into 2048-score chunks);
+ * other rows by the last scan workgroup of each sequence.
  * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hkv*D <= 8192 (bf16)
  * or <= 4096 (fp32); Hq % Hkv == 0; Hq/Hkv <= 64; B <= 65535.
  * Errors: SV_EINVAL (k > N, k < 0, N < 1, B < 1, Tq < 1, Hq % Hkv != 0,

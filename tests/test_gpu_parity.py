@@ -156,6 +156,52 @@ def test_retrieve_select_edge_distributions(mode):
                 assert idx[b].tolist() == np.sort(order[:k]).tolist(), (mode, k, b)
 
 
+def test_retrieve_long_rows_multi_token_query():
+    """Rows over 2048 tokens take the parallel select; a 3-token query (GQA 28/4)."""
+    w = synthetic.scaled_decode(synthetic.DECODE["qwen2_7b_video"], N=4100, k=333)
+    _say("retrieve long rows Tq=3", w)
+    d = synthetic.make_decode_layer(w, seed=5)
+    q = torch.randn(1, 3, 28, 128, generator=torch.Generator().manual_seed(19)).to(torch.bfloat16)
+    s_ref = oracle.retrieval_scores(q, d["k_vis"])
+    idx, sc = sv.retrieve(q.to(DEV), d["k_vis"].to(DEV), w.k, scores=True)
+    torch.cuda.synchronize()
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.k)
+    assert ok, msgs[:3]
+    _self_consistent(idx, sc, w.k)
+
+
+@pytest.mark.parametrize("mode", ["all_equal", "outlier", "tied_block_300", "two_values"])
+def test_retrieve_long_rows_edge_distributions(mode):
+    """The parallel select (rows over 2048 tokens) on rows that send it to its
+    fallbacks: one value everywhere, a tied block wider than the ranked bin,
+    two values; and one outlier.  One workspace serves every k in turn."""
+    B, N, H, D = 2, 5000, 4, 64
+    g = torch.Generator().manual_seed(41)
+    q = torch.randn(B, 1, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, H, D, generator=g).to(torch.bfloat16)
+    if mode == "all_equal":
+        kv[:] = kv[:, :1].clone()
+    elif mode == "outlier":
+        kv[:, 3777] = (q[:, 0] * 1000).to(torch.bfloat16)
+    elif mode == "tied_block_300":
+        kv[:, 2400:2700] = kv[:, 2400:2401].clone()
+    elif mode == "two_values":
+        kv[:, ::2] = kv[:, :1].clone()
+        kv[:, 1::2] = kv[:, 1:2].clone()
+    s_ref = oracle.retrieval_scores(q, kv)
+    _say("retrieve long-row select edge", mode)
+    qd, kd = q.to(DEV), kv.to(DEV)
+    ws = sv.new_workspace(sv.retrieve_workspace_bytes(B, N, N), DEV)
+    for k in (1, 777, 2500, N):
+        idx = sv.retrieve(qd, kd, k, workspace=ws).cpu().numpy()
+        for b in range(B):
+            order = np.lexsort((np.arange(N), -s_ref[b]))
+            ok, _, msgs = accept.check_index_sets(idx[b:b + 1], s_ref[b:b + 1], k)
+            assert ok, (mode, k, b, msgs[:2])
+            if mode != "outlier":          # exact ties: the lowest indices must win
+                assert idx[b].tolist() == np.sort(order[:k]).tolist(), (mode, k, b)
+
+
 # ---------------------------------------------------------------- attention
 ATTN_CASES = [
     ("image576_fp32", "image576_fp32", {}),
@@ -291,10 +337,12 @@ def test_workspace_reuse_leaves_counters_zero():
     torch.cuda.synchronize()
     for idx, out in outs[1:]:
         assert torch.equal(idx, outs[0][0]) and torch.equal(out, outs[0][1])
-    # counters (one 128-byte line each) live after the scores / partials, 256-byte aligned
+    # counters (one 128-byte line each) live after the scores / partials, 256-byte aligned;
+    # for these long rows the parallel select's histograms and lists follow them
     n_scores = ((w.B * w.N * 4 + 255) // 256) * 256
-    assert ws_r.numel() - n_scores >= 128 * w.B
-    assert torch.count_nonzero(ws_r[n_scores:]) == 0
+    n_ctr = ((w.B * 128 + 255) // 256) * 256
+    assert ws_r.numel() - n_scores >= n_ctr
+    assert torch.count_nonzero(ws_r[n_scores:n_scores + n_ctr]) == 0
     tail = ws_a[-((w.B * w.Hkv * 128 + 255) // 256) * 256:]
     assert torch.count_nonzero(tail) == 0
     s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])

@@ -74,7 +74,8 @@ int sv_version(void) { return 110; }
 const char* sv_last_error(void) { return g_err.c_str(); }
 
 // ---------------------------------------------------------------- retrieval
-// Workspace of sv_retrieve: [scores B*N fp32][counters B uint32].
+// Workspace of sv_retrieve: [scores B*N fp32][counters B lines] and, for rows
+// longer than the single-workgroup select, the long-row select workspace.
 static size_t retrieve_scores_bytes(int B, int N) { return align256((size_t)B * (size_t)N * sizeof(float)); }
 
 // Control words: one 128-byte line each.
@@ -83,7 +84,7 @@ static size_t ctr_bytes(size_t n) { return align256(n * sv::kCtrStride * sizeof(
 size_t sv_retrieve_workspace(int B, int N, int k) {
   (void)k;
   if (B < 1 || N < 1) return 256;
-  return retrieve_scores_bytes(B, N) + ctr_bytes((size_t)B);
+  return retrieve_scores_bytes(B, N) + ctr_bytes((size_t)B) + sv::long_select_bytes(B, N);
 }
 
 sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, int64_t k_bstride,
@@ -115,6 +116,32 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
                 sv_retrieve_workspace(B, N, k));
   float* scores = scores_out ? scores_out : (float*)workspace;
   uint32_t* counters = (uint32_t*)((char*)workspace + retrieve_scores_bytes(B, N));
+  if (k > 0 && sv::long_select_bytes(B, N) > 0 && Hq / Hkv <= 8) {
+    // Long rows: the scan and the parallel select of the one-launch layer
+    // (every pass over a row split into 2048-score chunks), no attention.
+    sv::FusedLaunch f{};
+    f.q = q;
+    f.B = B;
+    f.Tq = Tq;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.D = D;
+    f.dtype = (int)dtype;
+    f.k_vis = k_vis;
+    f.v_vis = k_vis;
+    f.vbs = k_bstride;
+    f.vts = k_tstride;
+    f.N = N;
+    f.k = k;
+    f.scale = 1.0f;
+    f.idx = idx_out;
+    f.scores_ws = (float*)workspace;
+    f.scores_out = scores_out;
+    f.seq_ctr = counters;
+    f.long_ws = (char*)counters + ctr_bytes((size_t)B);
+    f.retrieve_only = true;
+    return hip_status(sv::launch_fused(f, (hipStream_t)stream), "sv_retrieve");
+  }
   return hip_status(sv::launch_retrieve(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D,
                                         (int)dtype, scores, k, idx_out, counters, 0,
                                         (hipStream_t)stream),

@@ -258,6 +258,10 @@ struct FusedLaunch {
   // bytes whose first long_select_zero_bytes(B) are zero before the launch
   // and zero again after it.
   void* long_ws;
+  int Tq;              // query tokens summed by the scan (0: 1)
+  // Scan and select only (sv_retrieve on rows longer than the single-
+  // workgroup select): no attention items; ready and idx_enc are unused.
+  bool retrieve_only;
   int rows_per_item;   // 0: default
   int epl;             // 0: default
 };

@@ -36,9 +36,10 @@ size_t long_select_bytes(int B, int N) {
 hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   const int VE = f.dtype == 1 ? 8 : 4;
   const int G = f.Hq / f.Hkv;
+  if (f.retrieve_only && !long_rows(f.N)) return hipErrorInvalidValue;
   ScanArgs sa{};
   sa.q = f.q;
-  sa.Tq = 1;
+  sa.Tq = f.Tq > 0 ? f.Tq : 1;
   sa.Hq = f.Hq;
   sa.G = G;
   sa.kv = f.k_vis;
@@ -62,8 +63,8 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.k = f.k;
   sa.idx = f.idx;
   sa.seq_ctr = f.seq_ctr;
-  sa.ready = f.ready;
-  sa.idx_enc = f.idx_enc;
+  sa.ready = f.retrieve_only ? nullptr : f.ready;
+  sa.idx_enc = f.retrieve_only ? nullptr : f.idx_enc;
   LongSelArgs ls{};
   if (!sa.encode) {
     if (!f.long_ws) return hipErrorInvalidValue;
@@ -126,6 +127,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   ctl.seq_end = ctl.per_seq * (uint32_t)f.B;  // long rows: the same count, in phase order
   ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
   ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
+  if (f.retrieve_only) ctl.text_end = ctl.total = ctl.seq_end;
   if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
   return launch_fused_typed<float>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
 }

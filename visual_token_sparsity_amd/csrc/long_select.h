@@ -407,7 +407,7 @@ __device__ __forceinline__ void compact_item(const ScanArgs& a, const LongSelArg
     counter_reset(ls_line(l, b, kLsThrReady));
     counter_reset(ls_line(l, b, kLsInfo2));
     counter_reset(ls_line(l, b, kLsInfo2) + 1);
-    store_flag(&a.ready[b * kCtrStride], 1u);
+    if (a.ready) store_flag(&a.ready[b * kCtrStride], 1u);
   }
 }
 
