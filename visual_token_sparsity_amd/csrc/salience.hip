@@ -732,7 +732,7 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       load_a(q, rb + kRowWaves, an);  // next row block (zeros past the end)
 
       // Software pipeline over column tiles: step t issues the LDS reads of
-      // tile t+2 and the MFMAs of tile t+1, then the exps of tile t, so the
+      // tile t+3 and the MFMAs of tile t+1, then the exps of tile t, so the
       // matrix core and the LDS work under the VALU.  A scheduling barrier
       // closes each step (it keeps the compiler from hoisting every tile's
       // reads, which would run out of registers).
@@ -742,7 +742,8 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       // instead of a conversion plus an add.
       float one = 1.0f;
       asm volatile("" : "+v"(one));
-      bf16x8 bkb[3][KS];
+      constexpr int NB = 4;  // key-fragment buffers: reads run two steps ahead of use
+      bf16x8 bkb[NB][KS];
       // The lane's row offset is made opaque once per row block so the
       // compiler does not keep one address register per tile live.
       int lrow = li * D;
@@ -763,14 +764,15 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
         for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bk[s], a, 0, 0, 0);
         return a;
       };
-      lds_b(0, bkb[0]);
-      if (NTILE > 1) lds_b(1, bkb[1]);
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t)
+        if (t < NTILE) lds_b(t, bkb[t]);
       f32x4 acc = mm(bkb[0]);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) {
-        if (t + 2 < NTILE) lds_b(t + 2, bkb[(t + 2) % 3]);
+        if (t + NB - 1 < NTILE) lds_b(t + NB - 1, bkb[(t + NB - 1) % NB]);
         f32x4 accn = acc;
-        if (t + 1 < NTILE) accn = mm(bkb[(t + 1) % 3]);
+        if (t + 1 < NTILE) accn = mm(bkb[(t + 1) % NB]);
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(acc[r], c2, -b[r]));
