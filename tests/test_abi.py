@@ -50,6 +50,14 @@ def test_workspace_sizes():
     f = sv.retrieve_attend_workspace_bytes(8, 32, 32, 128, 1440, 360, 256)
     assert f % 256 == 0
     assert f >= sv.retrieve_workspace_bytes(8, 1440, 360) + w
+    # rows over 2048 tokens: retrieval also holds the parallel select's
+    # histograms and candidate lists (at least 16384 candidates of 8 bytes each)
+    short = sv.retrieve_workspace_bytes(1, 2048, 100)
+    long_ = sv.retrieve_workspace_bytes(1, 2049, 100)
+    assert long_ % 256 == 0 and long_ - short >= 16384 * 8
+    # the salience workspace ends with one 32-bit flag per (frame, head)
+    assert (sv.salience_prune_workspace_bytes(256, 16, 729)
+            >= 256 * 16 * 729 * 4 + 256 * 729 * 4 + 256 * 16 * 4)
 
 
 def test_retrieve_rejects_slices_of_2gib():
