@@ -392,6 +392,47 @@ def test_decode_step_graph_replays_match_eager():
         assert ok, err
 
 
+def test_salience_graph_replays_match_eager():
+    """A captured salience prune (row kernel, flagged-item pass, mean, top-keep), replayed
+    with eager work in between, matches the eager call bit for bit; one item is flagged so
+    both kernels write the column sums."""
+    w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=3, H=2)
+    Q, K = synthetic.make_salience(w, seed=13)
+    Q = Q.float()
+    Q[2, 1] *= 12.0
+    Q = Q.to(torch.bfloat16)
+    _say("salience graph replay")
+    Qd, Kd = Q.to(DEV), K.to(DEV)
+    ws = sv.new_workspace(sv.salience_prune_workspace_bytes(w.F, w.H, w.N), DEV)
+    sal = torch.empty((w.F, w.N), dtype=torch.float32, device=DEV)
+    keep = torch.empty((w.F, w.keep), dtype=torch.int32, device=DEV)
+
+    def call():
+        sv.salience_prune(Qd, Kd, w.keep, workspace=ws, salience_out=sal, idx_out=keep)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref_sal, ref_keep = sal.clone(), keep.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        call()
+    for rep in range(4):
+        sal.fill_(-7.0)                       # eager work between replays
+        keep.fill_(-7)
+        if rep == 2:
+            ws.zero_()                        # a cleared workspace replays the same
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sal, ref_sal), rep
+        assert torch.equal(keep, ref_keep), rep
+    s_ref = oracle.salience(Q, K)
+    ok, rel, sm = accept.check_salience(ref_sal.cpu().numpy(), s_ref)
+    assert ok, (rel, sm)
+
+
 @pytest.mark.parametrize("mode", ["all_rows", "some_rows"])
 def test_salience_large_logits_use_exact_row_max(mode):
     """Rows whose Cauchy-Schwarz shift could underflow take the exact-max path."""
