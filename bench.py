@@ -55,14 +55,16 @@ def parse():
     return p.parse_args()
 
 
-def decode_bytes(w):
-    """Algorithmic HBM bytes of one step, and of one layer of the whole batch."""
+def decode_bytes(w, T=None):
+    """Algorithmic HBM bytes of one step, and of one layer of the whole batch
+    (T text entries per sequence, w.T by default)."""
+    T = w.T if T is None else T
     e = 2 if w.dtype.itemsize == 2 else 4
     row = w.Hkv * w.D * e
     q = w.Hq * w.D * e
     scan = w.N * row + q + w.N * 4                       # keys once, query, fp32 scores out
     select = w.N * 4 + w.k * 4                            # scores in, indices out
-    attn = (w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4   # K,V of the attended rows
+    attn = (w.k + T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4   # K,V of the attended rows
     per_seq_layer = scan + select + attn
     return per_seq_layer * w.B * w.L, per_seq_layer * w.B
 
@@ -166,16 +168,47 @@ def main():
     ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
     torch.cuda.synchronize()
 
+    # Multi-turn workload: conversation rounds of decode steps over one reused
+    # visual cache.  Step i takes a fresh query and the text length of its
+    # place in the round schedule (partial eviction between rounds); the
+    # schedule repeats when more steps are timed than it holds.
+    sched = None
+    if w.name == "multiturn_128k":
+        lens = [t for rnd in synthetic.multiturn_text_lengths() for t in rnd]
+        sched = {"lens": lens,
+                 "txt": torch.tensor([[t] * w.B for t in lens], dtype=torch.int32, device=dev),
+                 "q": (torch.randn((len(lens), w.B, 1, w.Hq, w.D), device=dev,
+                                   generator=torch.Generator(device=dev).manual_seed(
+                                       synthetic.stream_seed(a.seed, w.name, "q_per_step")))
+                       .to(w.dtype)),
+                 "i": 0}
+
     def step():
         for l, d in enumerate(layers):
-            sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
-                               d["txt_len"], workspace=ws_f, out=out[l], idx_out=idx[l])
+            q, tl = d["q"], d["txt_len"]
+            if sched is not None:
+                j = sched["i"] % len(sched["lens"])
+                q, tl = sched["q"][j], sched["txt"][j]
+            sv.retrieve_attend(q, d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
+                               tl, workspace=ws_f, out=out[l], idx_out=idx[l])
+        if sched is not None:
+            sched["i"] += 1
 
     def step_two_call():
         for l, d in enumerate(layers):
-            sv.retrieve(d["q"], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
-            sv.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
-                                  d["txt_len"], workspace=ws_a, out=out[l])
+            q, tl = d["q"], d["txt_len"]
+            if sched is not None:
+                j = sched["i"] % len(sched["lens"])
+                q, tl = sched["q"][j], sched["txt"][j]
+            sv.retrieve(q, d["k_vis"], w.k, workspace=ws_r, out=idx[l])
+            sv.sparse_decode_attn(q, d["k_vis"], d["v_vis"], idx[l], d["k_txt"], d["v_txt"],
+                                  tl, workspace=ws_a, out=out[l])
+        if sched is not None:
+            sched["i"] += 1
+
+    def vis_checksum():
+        return [int(d[n].view(torch.int16).sum(dtype=torch.int64).item())
+                for d in layers for n in ("k_vis", "v_vis")]
 
     if a.profile_traffic:
         # Counter passes: the fused decode layer as timed, and a plain copy of
@@ -193,22 +226,30 @@ def main():
         return
 
     stream = torch.cuda.Stream(device=dev)      # default priority
+    sum_before = vis_checksum() if sched is not None else None
     with torch.cuda.stream(stream):
         for _ in range(max(1, a.warmup)):
             step()
             step_two_call()
         torch.cuda.synchronize()
-        g_step = None if a.no_graph else capture(step, stream)
-        g_two = None if a.no_graph else capture(step_two_call, stream)
+        # The multi-turn schedule changes the query and text length every step:
+        # eager launches (each step is one ~0.8 ms kernel).
+        eager = a.no_graph or sched is not None
+        g_step = None if eager else capture(step, stream)
+        g_two = None if eager else capture(step_two_call, stream)
         run_step = g_step.replay if g_step is not None else step
         run_two = g_two.replay if g_two is not None else step_two_call
         for _ in range(a.warmup):
             run_step()
         # ---------------------------------------------------- timed region: exactly K steps
         torch.cuda.synchronize()
+        if sched is not None:
+            sched["i"] = 0                       # the timed steps start the schedule
         t0 = time.perf_counter()
         secs = gpu_time(run_step, a.steps, stream)
         wall = time.perf_counter() - t0
+        timed_lens = ([sched["lens"][i % len(sched["lens"])] for i in range(a.steps)]
+                      if sched is not None else None)
         # ---------------------------------------------------- the two-call path, for comparison
         for _ in range(3):
             run_two()
@@ -216,6 +257,10 @@ def main():
         two_secs = gpu_time(run_two, two_reps, stream) / two_reps
 
     step_bytes, layer_bytes = decode_bytes(w)
+    if timed_lens is not None:                   # mean over the timed steps' text lengths
+        per = [decode_bytes(w, T) for T in timed_lens]
+        step_bytes = sum(p[0] for p in per) // len(per)
+        layer_bytes = sum(p[1] for p in per) // len(per)
     steps_per_s = a.steps / secs
     gbs = step_bytes * steps_per_s / 1e9
     # One launch per layer: the average launch duration over the timed region.
@@ -254,6 +299,16 @@ def main():
                           "launches_per_layer": 2},
         "wall_s_timed": round(wall, 4),
     }
+    if sched is not None:
+        sum_after = vis_checksum()
+        if sum_after != sum_before:
+            raise RuntimeError("the visual cache changed during the multi-turn schedule")
+        res["config"].update({
+            "text_tokens": f"{min(timed_lens)}-{max(timed_lens)}",
+            "schedule": "3 rounds x 128 decode steps, fresh query per step; text = 64 system + "
+                        "64 question + step + 1, question and answer evicted between rounds; "
+                        "timed steps follow the schedule from its start",
+            "visual_cache_unchanged": True})
 
     # ------------------------------------------------------------ prefill salience
     if not a.no_salience:

@@ -318,3 +318,37 @@ def test_retrieve_attend_long_rows_reuse_and_graph_replay():
                                         host["txt_len"])
         ok, err = accept.check_attention(ref_out[l].cpu().numpy(), ref)
         assert ok, err
+
+
+def test_multiturn_rounds_reuse_the_visual_cache():
+    """Rounds of decode steps over one visual cache (the multi-turn reuse): every step a
+    fresh query and a text length that grows by one, then partial eviction back to the
+    system entries between rounds.  One workspace serves every step; each step matches
+    the oracle and the visual cache is bit-identical afterwards."""
+    w = synthetic.scaled_decode(synthetic.DECODE["multiturn_128k"], B=2, N=4100, k=300, T=24,
+                                Tmax=24)
+    sched = synthetic.multiturn_text_lengths(rounds=2, steps=4, system=8, question=8)
+    assert sched == [[17, 18, 19, 20], [17, 18, 19, 20]]
+    _say("multiturn rounds", w, sched)
+    d = synthetic.make_decode_layer(w, seed=14)
+    g = _to(d)
+    before = [g[n].clone() for n in ("k_vis", "v_vis", "k_txt", "v_txt")]
+    ws = sv.new_workspace(sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k,
+                                                             w.Tmax), DEV)
+    gen = torch.Generator().manual_seed(15)
+    for r, lens in enumerate(sched):
+        for t, T in enumerate(lens):
+            q = torch.randn(w.B, 1, w.Hq, w.D, generator=gen).to(w.dtype)
+            tl = torch.full((w.B,), T, dtype=torch.int32)
+            out, idx = sv.retrieve_attend(q.to(DEV), g["k_vis"], g["v_vis"], w.k, g["k_txt"],
+                                          g["v_txt"], tl.to(DEV), workspace=ws)
+            torch.cuda.synchronize()
+            s_ref = oracle.retrieval_scores(q, d["k_vis"])
+            ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.k)
+            assert ok, (r, t, msgs[:2])
+            ref = oracle.sparse_decode_attn(q, d["k_vis"], d["v_vis"], idx.cpu().numpy(),
+                                            d["k_txt"], d["v_txt"], tl.numpy())
+            ok, err = accept.check_attention(out.cpu().numpy(), ref)
+            assert ok, (r, t, err)
+    for a_, n in zip(before, ("k_vis", "v_vis", "k_txt", "v_txt")):
+        assert torch.equal(a_, g[n]), n
