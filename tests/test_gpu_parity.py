@@ -476,10 +476,10 @@ def test_salience_mixed_items_split_between_kernels():
 
 
 @pytest.mark.parametrize("D", [64, 72, 80, 96])
-@pytest.mark.parametrize("N", [32, 129, 250, 256, 729])
+@pytest.mark.parametrize("N", [32, 129, 196, 250, 256, 400, 576, 729])
 def test_salience_head_dim_grid(D, N):
-    """Every head dim of both on-chip kernels (the row kernel takes N = 241..256 and
-    721..736), with and without a ragged last tile."""
+    """Every head dim of both on-chip kernels (the row kernel takes N in 193..208,
+    241..256, 385..400, 561..576 and 721..736), with and without a ragged last tile."""
     w = synthetic.scaled_salience(synthetic.SALIENCE["siglip_256f"], F=1, H=2, N=N, D=D, keep=N // 2)
     _say("salience grid", N, D)
     Q, K = synthetic.make_salience(w, seed=3)

@@ -953,10 +953,12 @@ static hipError_t colstat_any(const void* q, const void* k, int FH, int N, int D
 }
 
 // Row-stationary kernel: compiled for an exact number of 16-key column tiles,
-// 16 (N in 241..256) or 46 (N in 721..736, e.g. 27 x 27 = 729 patches).
+// the square patch grids of common vision encoders: 13 (N in 193..208, e.g.
+// 14 x 14 = 196), 16 (241..256), 25 (385..400, 20 x 20), 36 (561..576,
+// 24 x 24) and 46 (721..736, 27 x 27 = 729).
 static int pick_ntm_rows(int N) {
   const int nt = (N + 15) / 16;
-  return (nt == 16 || nt == 46) ? nt : -1;
+  return (nt == 13 || nt == 16 || nt == 25 || nt == 36 || nt == 46) ? nt : -1;
 }
 
 static size_t rows_lds_bytes(int ntm, int D) {
@@ -991,8 +993,14 @@ static hipError_t rows_go(const void* q, const void* k, int FH, int N, float c2,
 template <int D>
 static hipError_t rows_ntm(const void* q, const void* k, int FH, int N, float c2, float* colsum,
                            int32_t* redo, hipStream_t st) {
-  return pick_ntm_rows(N) == 16 ? rows_go<D, 16>(q, k, FH, N, c2, colsum, redo, st)
-                                : rows_go<D, 46>(q, k, FH, N, c2, colsum, redo, st);
+  switch (pick_ntm_rows(N)) {
+    case 13: return rows_go<D, 13>(q, k, FH, N, c2, colsum, redo, st);
+    case 16: return rows_go<D, 16>(q, k, FH, N, c2, colsum, redo, st);
+    case 25: return rows_go<D, 25>(q, k, FH, N, c2, colsum, redo, st);
+    case 36: return rows_go<D, 36>(q, k, FH, N, c2, colsum, redo, st);
+    case 46: return rows_go<D, 46>(q, k, FH, N, c2, colsum, redo, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D, float scale,
