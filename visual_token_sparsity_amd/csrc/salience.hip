@@ -208,11 +208,6 @@ __global__ __launch_bounds__(kSalWaves* kWave, 1) void salience_colsum_kernel(
 // ----------------------------------------------------------------------------
 constexpr int kColWaves = 8;  // waves per workgroup, each owning a column slice
 constexpr int kRowBlocks = 1;  // 16-row blocks per iteration
-#ifndef SV_SAL_PREFETCH
-#define SV_SAL_PREFETCH 1
-#endif
-constexpr int kPrefetch = SV_SAL_PREFETCH;  // iterations of query fragments in flight
-static_assert(kPrefetch == 1 || kPrefetch == 2 || kPrefetch == 4, "ring slots must divide the unroll");
 
 __device__ __forceinline__ float sumsq8(const bf16x8& v) {
   float s = 0.f;
@@ -397,16 +392,11 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
       for (int t = 0; t < TPW; ++t) npad += (c0 + 16 * t + li >= N) ? 1 : 0;
       const float fpad = (float)npad;
       const bool padw = __any(npad > 0);  // only the wave(s) owning columns >= N
-      // Query fragments are prefetched kPrefetch iterations ahead into a ring
-      // of register slots (slot = iteration mod kPrefetch): a row block that
-      // misses in L2 has several iterations to arrive.
-      bf16x8 afr[kPrefetch][kRowBlocks][KS];
+      bf16x8 af[kRowBlocks][KS];
 #pragma unroll
-      for (int sl = 0; sl < kPrefetch; ++sl)
-#pragma unroll
-        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * sl + h, afr[sl][h]);
+      for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, h, af[h]);
 
-      auto mfma_phase = [&](f32x4 (&S)[kRowBlocks][TPW], bf16x8 (&af)[kRowBlocks][KS], int it) {
+      auto mfma_phase = [&](f32x4 (&S)[kRowBlocks][TPW], int it) {
 #pragma unroll
         for (int h = 0; h < kRowBlocks; ++h) {
 #pragma unroll
@@ -418,9 +408,9 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
             S[h][t] = acc;
           }
         }
-        // The slot is consumed: the row blocks kPrefetch iterations ahead load into it.
+        // The A fragments are consumed: the next row blocks load into the same registers.
 #pragma unroll
-        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * (it + kPrefetch) + h, af[h]);
+        for (int h = 0; h < kRowBlocks; ++h) load_a_raw(q, kRowBlocks * (it + 1) + h, af[h]);
       };
       auto update_phase = [&](const f32x4 (&S)[kRowBlocks][TPW], const float (&f)[kRowBlocks][4]) {
 #pragma unroll
@@ -499,23 +489,32 @@ __global__ __launch_bounds__(kColWaves* kWave, 1) void salience_colstat_kernel(
         }
       };
 
-      f32x4 S2[2][kRowBlocks][TPW];
-      float f2[2][kRowBlocks][4];
-      // Iteration it: MFMA(it) | wait for it-1's partials, weights, column
-      // update of it-1 | publish(it).  Unrolled by kUnroll so the ring slot
-      // (it mod kPrefetch) and the score buffer (it mod 2) are static.
-      constexpr int kUnroll = kPrefetch > 2 ? kPrefetch : 2;
-      for (int base = 0; base <= iters; base += kUnroll) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int it = base + u;
-          if (it < iters) mfma_phase(S2[u & 1], afr[u % kPrefetch], it);
-          if (it >= 1 && it <= iters) {
-            collect(it - 1, f2[(u + 1) & 1]);
-            update_phase(S2[(u + 1) & 1], f2[(u + 1) & 1]);
-          }
-          if (it < iters) publish(S2[u & 1], it);
-        }
+      f32x4 SA[kRowBlocks][TPW], SB[kRowBlocks][TPW];
+      float fA[kRowBlocks][4], fB[kRowBlocks][4];
+      // MFMA(it) | wait for it-1's partials, weights, column update of it-1 | publish(it)
+      mfma_phase(SA, 0);
+      publish(SA, 0);
+      int it = 1;
+      for (; it + 1 < iters; it += 2) {
+        mfma_phase(SB, it);
+        collect(it - 1, fA);
+        update_phase(SA, fA);
+        publish(SB, it);
+        mfma_phase(SA, it + 1);
+        collect(it, fB);
+        update_phase(SB, fB);
+        publish(SA, it + 1);
+      }
+      if (it < iters) {
+        mfma_phase(SB, it);
+        collect(it - 1, fA);
+        update_phase(SA, fA);
+        publish(SB, it);
+        collect(it, fB);
+        update_phase(SB, fB);
+      } else {
+        collect(it - 1, fA);
+        update_phase(SA, fA);
       }
       __syncthreads();  // every wave is done with the partials and the counter
       if (tid == 0) *arrived = 0u;  // ordered before the next publish by the item-start barrier
