@@ -642,6 +642,18 @@ __device__ __forceinline__ f16x4 pack_f16x4(float a, float b, float c, float d) 
   return f16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Fragment-major key tiles: byte offset of k-step s inside a 16-key tile, and
+// the number of 8-dim lane groups that step stores.
+template <int D>
+__device__ __forceinline__ int frag_step_off(int s) {
+  return 16 * 2 * (32 * s < D ? 32 * s : D);
+}
+template <int D>
+__device__ __forceinline__ int frag_step_nlg(int s) {
+  const int r = (D - 32 * s) / 8;
+  return r < 4 ? r : 4;
+}
+
 template <int D, int NTILE>
 __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
@@ -652,8 +664,14 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
   constexpr int NC = NTILE * 16;  // key columns rounded up to whole tiles
   static_assert(D % 8 == 0, "D must be a multiple of 8");
   extern __shared__ uint4 smem_u4[];
-  bf16_t* sK = reinterpret_cast<bf16_t*>(smem_u4);                    // [NC][D] keys
-  float* cacc = reinterpret_cast<float*>(sK + NC * D);                 // [kRowWaves][NC] wave sums
+  // Keys in LDS, fragment-major: tile t (16 keys, 16 * D * 2 bytes) holds,
+  // for each 32-wide k-step s, the 16-byte B fragments of the lanes that carry
+  // data (lg < nlg(s)), in lane order, so a wave's fragment read is one
+  // contiguous run of 16-byte chunks (no bank conflicts).  A zeroed 1 KB pad
+  // follows: a partial step's lanes past D read into the next tile or the pad,
+  // finite values that meet zero query data.
+  char* sK = reinterpret_cast<char*>(smem_u4);                         // [NTILE][16 D * 2] + 1 KB
+  float* cacc = reinterpret_cast<float*>(sK + NC * D * 2 + 1024);      // [kRowWaves][NC] wave sums
   uint32_t* ctl = reinterpret_cast<uint32_t*>(cacc + kRowWaves * NC);  // max|k|^2, redo
 
   const int tid = threadIdx.x;
@@ -661,11 +679,12 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
   const int wave = tid / kWave;
   const int li = lane & 15, lg = lane >> 4;
   const int RB = (N + 15) / 16;
-  const int kbytes = N * D * 2;
   float* myacc = cacc + wave * NC;
 
-  // Key rows N..NC-1 stay zero for every item.
-  for (int c = N * D / 8 + tid; c < NC * D / 8; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
+  constexpr int TB = 16 * D * 2;  // bytes per key tile
+  // Keys of rows N..NC-1 and the pad stay zero for every item (the staging
+  // never writes them).
+  for (int c = tid; c < (NC * D * 2 + 1024) / 16; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
 
   // A fragments of row block rb: lane (li, lg) holds row 16 rb + li, dims
   // 32 s + 8 lg .. +7.  Rows >= N and dims >= D read as zeros.
@@ -692,20 +711,31 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     __syncthreads();      // the previous item is done with sK, cacc and ctl
     if (tid < 2) ctl[tid] = 0u;
     {
+      // Direct global->LDS loads, one per (tile, k-step): lane (li, lg) fetches
+      // row 16 t + li, dims 32 s + 8 lg .. +7, and lands in lane order.
       const char* src = reinterpret_cast<const char*>(Kg + (int64_t)item * N * D);
-      char* dst = reinterpret_cast<char*>(sK);
-      for (int chunk = wave; chunk * 1024 < kbytes; chunk += kRowWaves) {
-        const int off = chunk * 1024 + lane * 16;
-        if (off < kbytes) __builtin_amdgcn_global_load_lds(src + off, dst + chunk * 1024, 16, 0, 0);
+      for (int f = wave; f < NTILE * KS; f += kRowWaves) {
+        const int t = f / KS, s2 = f - t * KS;
+        const int row = 16 * t + li;
+        if (row < N && lg < frag_step_nlg<D>(s2)) {
+          // (the LDS destination goes through a local: written inline as the
+          // builtin's argument, the host pass dropped the kernel's stub)
+          char* dst = sK + t * TB + frag_step_off<D>(s2);
+          __builtin_amdgcn_global_load_lds(src + ((int64_t)row * D + 32 * s2 + 8 * lg) * 2, dst, 16,
+                                           0, 0);
+        }
       }
     }
     wait_stores_complete();  // this wave's direct loads have landed (vmcnt = 0)
     __syncthreads();
     float kn2 = 0.f;
     for (int r = tid; r < N; r += NT) {
+      const int t = r / 16, rl = r - 16 * t;
       float n2 = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) n2 += sumsq8(load_bf16x8(sK + r * D + 8 * c));
+      for (int s2 = 0; s2 < KS; ++s2)
+        for (int g2 = 0; g2 < frag_step_nlg<D>(s2); ++g2)
+          n2 += sumsq8(*reinterpret_cast<const bf16x8*>(sK + t * TB + frag_step_off<D>(s2) + (16 * g2 + rl) * 16));
       kn2 = fmaxf(kn2, n2);
     }
     kn2 = group_max<kWave>(kn2);
@@ -743,19 +773,16 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       asm volatile("" : "+v"(one));
       constexpr int NB = 4;  // key-fragment buffers: reads run two steps ahead of use
       bf16x8 bkb[NB][KS];
-      // The lane's row offset is made opaque once per row block so the
+      // The lane's byte offset is made opaque once per row block so the
       // compiler does not keep one address register per tile live.
-      int lrow = li * D;
-      asm volatile("" : "+v"(lrow));
-      // Lanes whose dims lie beyond D read any finite key data: their query
-      // partners in A are zero, so the products vanish.
+      int lofs = lane * 16;
+      asm volatile("" : "+v"(lofs));
+      // Lanes whose dims lie beyond D read the next tile's data or the zero
+      // pad: finite values whose query partners in A are zero.
       auto lds_b = [&](int t, bf16x8 (&bk)[KS]) {
-        const bf16_t* kr = sK + lrow + 16 * t * D;
+        const char* kt = sK + lofs + t * TB;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int dd = 32 * s + 8 * lg;
-          bk[s] = load_bf16x8(kr + (dd < D ? dd : 0));
-        }
+        for (int s = 0; s < KS; ++s) bk[s] = *reinterpret_cast<const bf16x8*>(kt + frag_step_off<D>(s));
       };
       auto mm = [&](const bf16x8 (&bk)[KS]) {
         f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -961,7 +988,7 @@ static int pick_ntm_rows(int N) {
 }
 
 static size_t rows_lds_bytes(int ntm, int D) {
-  return (size_t)ntm * 16 * D * 2 + (size_t)kRowWaves * ntm * 16 * 4 + 16;
+  return (size_t)ntm * 16 * D * 2 + 1024 + (size_t)kRowWaves * ntm * 16 * 4 + 16;
 }
 
 static bool rows_ok(int N, int D) {
