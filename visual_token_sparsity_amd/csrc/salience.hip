@@ -654,12 +654,30 @@ __device__ __forceinline__ int frag_step_nlg(int s) {
   return r < 4 ? r : 4;
 }
 
+// With D = 32 m + 8 (D = 72) the last k-step carries one lane group of data
+// (16 lanes x 16 bytes).  Its fragments are packed four tiles to a 1 KB
+// block (lane group j holds tile 4 q + j), read once per four tiles; tile
+// 4 q + j multiplies it with a query fragment whose data sits in lane group
+// j (zeros elsewhere).  Group q of four tiles: [full k-steps of 4 tiles][tail].
+__host__ __device__ constexpr bool rows_tail_pack(int D) { return D % 32 == 8; }
+__host__ __device__ constexpr int rows_full_steps(int D) {
+  return rows_tail_pack(D) ? D / 32 : (D + 31) / 32;
+}
+// Bytes of the keys region in LDS.
+__host__ __device__ constexpr int rows_k_bytes(int D, int ntile) {
+  return rows_tail_pack(D) ? ((ntile + 3) / 4) * (4 * (D / 32) * 1024 + 1024)
+                           : ntile * 16 * D * 2 + 1024;
+}
+
 template <int D, int NTILE>
 __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg, int FH, int N, float c2,
     float* __restrict__ colsum, int32_t* __restrict__ redo) {
   // 32-wide k-steps; lanes whose 8 dims lie beyond D get zero query data.
   constexpr int KS = (D + 31) / 32;
+  constexpr bool TP = rows_tail_pack(D);  // packed last k-step (see rows_tail_pack)
+  constexpr int KF = rows_full_steps(D);  // k-steps stored per tile
+  constexpr int DT = 32 * KF;             // first dim of the packed step
   constexpr int NT = kRowWaves * kWave;
   constexpr int NC = NTILE * 16;  // key columns rounded up to whole tiles
   static_assert(D % 8 == 0, "D must be a multiple of 8");
@@ -670,8 +688,8 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
   // contiguous run of 16-byte chunks (no bank conflicts).  A zeroed 1 KB pad
   // follows: a partial step's lanes past D read into the next tile or the pad,
   // finite values that meet zero query data.
-  char* sK = reinterpret_cast<char*>(smem_u4);                         // [NTILE][16 D * 2] + 1 KB
-  float* cacc = reinterpret_cast<float*>(sK + NC * D * 2 + 1024);      // [kRowWaves][NC] wave sums
+  char* sK = reinterpret_cast<char*>(smem_u4);                         // keys (rows_k_bytes)
+  float* cacc = reinterpret_cast<float*>(sK + rows_k_bytes(D, NTILE)); // [kRowWaves][NC] wave sums
   uint32_t* ctl = reinterpret_cast<uint32_t*>(cacc + kRowWaves * NC);  // max|k|^2, redo
 
   const int tid = threadIdx.x;
@@ -681,24 +699,38 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
   const int RB = (N + 15) / 16;
   float* myacc = cacc + wave * NC;
 
-  constexpr int TB = 16 * D * 2;  // bytes per key tile
+  constexpr int TB = 16 * D * 2;            // bytes per key tile (unpacked)
+  constexpr int FSB = KF * 1024;            // packed: full-step bytes per tile
+  constexpr int GB = 4 * FSB + 1024;        // packed: bytes per group of four tiles
+  constexpr int NG = (NTILE + 3) / 4;       // packed: groups
+  // Byte offset of tile t's k-step s fragments, and of group q's tail block.
+  auto frag_at = [&](int t, int s) {
+    return TP ? (t / 4) * GB + (t % 4) * FSB + s * 1024 : t * TB + frag_step_off<D>(s);
+  };
+  auto tail_at = [&](int qg) { return qg * GB + 4 * FSB; };
   // Keys of rows N..NC-1 and the pad stay zero for every item (the staging
   // never writes them).
-  for (int c = tid; c < (NC * D * 2 + 1024) / 16; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
+  for (int c = tid; c < rows_k_bytes(D, NTILE) / 16; c += NT) smem_u4[c] = make_uint4(0, 0, 0, 0);
 
   // A fragments of row block rb: lane (li, lg) holds row 16 rb + li, dims
   // 32 s + 8 lg .. +7.  Rows >= N and dims >= D read as zeros.
+  // Packed tail (TP): af[KS-1] holds dims DT..DT+7 of row li in every lane;
+  // tail_frags() then keeps them in lane group j only, for each j.
   auto load_a = [&](const bf16_t* q, int rb, bf16x8 (&af)[KS]) {
     const int row = rb * 16 + li;
     const bool ok = row < N;
     const int64_t rowc = ok ? row : 0;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int dd = 32 * s + 8 * lg;
+      const int dd = (TP && s == KS - 1) ? DT : 32 * s + 8 * lg;
       const bool in = ok && dd < D;
       const uint4 u = *reinterpret_cast<const uint4*>(q + rowc * D + (dd < D ? dd : 0));
       af[s] = __builtin_bit_cast(bf16x8, in ? u : make_uint4(0, 0, 0, 0));
     }
+  };
+  auto tail_frags = [&](const bf16x8& raw, bf16x8 (&at)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) at[j] = lg == j ? raw : zero_bf16x8();
   };
 
   for (int item = blockIdx.x; item < FH; item += gridDim.x) {
@@ -713,16 +745,41 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     {
       // Direct global->LDS loads, one per (tile, k-step): lane (li, lg) fetches
       // row 16 t + li, dims 32 s + 8 lg .. +7, and lands in lane order.
+      // Packed tail: one more load per group, lane (li, j) fetching row
+      // 16 (4 q + j) + li, dims DT .. DT+7.
       const char* src = reinterpret_cast<const char*>(Kg + (int64_t)item * N * D);
-      for (int f = wave; f < NTILE * KS; f += kRowWaves) {
-        const int t = f / KS, s2 = f - t * KS;
+      constexpr int JOBS = TP ? NG * (4 * KF + 1) : NTILE * KS;
+      for (int f = wave; f < JOBS; f += kRowWaves) {
+        int t, s2, dim, off;
+        bool on;
+        if (TP) {
+          const int qg = f / (4 * KF + 1), r = f - qg * (4 * KF + 1);
+          if (r < 4 * KF) {
+            t = 4 * qg + r / KF;
+            s2 = r % KF;
+            dim = 32 * s2 + 8 * lg;
+            off = frag_at(t, s2);
+            on = t < NTILE;
+          } else {
+            t = 4 * qg + lg;
+            s2 = KS - 1;
+            dim = DT;
+            off = tail_at(qg);
+            on = t < NTILE;
+          }
+        } else {
+          t = f / KS;
+          s2 = f - t * KS;
+          dim = 32 * s2 + 8 * lg;
+          off = frag_at(t, s2);
+          on = lg < frag_step_nlg<D>(s2);
+        }
         const int row = 16 * t + li;
-        if (row < N && lg < frag_step_nlg<D>(s2)) {
+        if (on && row < N) {
           // (the LDS destination goes through a local: written inline as the
           // builtin's argument, the host pass dropped the kernel's stub)
-          char* dst = sK + t * TB + frag_step_off<D>(s2);
-          __builtin_amdgcn_global_load_lds(src + ((int64_t)row * D + 32 * s2 + 8 * lg) * 2, dst, 16,
-                                           0, 0);
+          char* dst = sK + off;
+          __builtin_amdgcn_global_load_lds(src + ((int64_t)row * D + dim) * 2, dst, 16, 0, 0);
         }
       }
     }
@@ -733,9 +790,10 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       const int t = r / 16, rl = r - 16 * t;
       float n2 = 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2)
+      for (int s2 = 0; s2 < KF; ++s2)
         for (int g2 = 0; g2 < frag_step_nlg<D>(s2); ++g2)
-          n2 += sumsq8(*reinterpret_cast<const bf16x8*>(sK + t * TB + frag_step_off<D>(s2) + (16 * g2 + rl) * 16));
+          n2 += sumsq8(*reinterpret_cast<const bf16x8*>(sK + frag_at(t, s2) + (16 * g2 + rl) * 16));
+      if (TP) n2 += sumsq8(*reinterpret_cast<const bf16x8*>(sK + tail_at(t / 4) + (16 * (t % 4) + rl) * 16));
       kn2 = fmaxf(kn2, n2);
     }
     kn2 = group_max<kWave>(kn2);
@@ -744,12 +802,16 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
     const float kc = __builtin_amdgcn_sqrtf(__uint_as_float(ctl[0])) * c2 * 1.0009765625f;
 
     for (int rb = wave; rb < RB; rb += kRowWaves) {
-      // |q|^2 of row li: the 4 lanes li + 16 lg hold its chunks.
+      // |q|^2 of row li: the 4 lanes li + 16 lg hold its chunks (a packed
+      // tail is in every lane: counted once).
       float n2 = 0.f;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) n2 += sumsq8(af[s]);
+      for (int s = 0; s < KF; ++s) n2 += sumsq8(af[s]);
+      if (TP) n2 += lg == 0 ? sumsq8(af[KS - 1]) : 0.f;
       n2 += __shfl_xor(n2, 16, kWave);
       n2 += __shfl_xor(n2, 32, kWave);
+      bf16x8 at[4];  // packed tail: query dims DT.. in lane group j only
+      if (TP) tail_frags(af[KS - 1], at);
       // Output rows of this lane are 16 rb + 4 lg + r.
       float b[4];
 #pragma unroll
@@ -772,33 +834,37 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
       float one = 1.0f;
       asm volatile("" : "+v"(one));
       constexpr int NB = 4;  // key-fragment buffers: reads run two steps ahead of use
-      bf16x8 bkb[NB][KS];
+      bf16x8 bkb[NB][KF];
+      bf16x8 tbk[2];  // packed tail blocks of two groups of four tiles
       // The lane's byte offset is made opaque once per row block so the
       // compiler does not keep one address register per tile live.
       int lofs = lane * 16;
       asm volatile("" : "+v"(lofs));
       // Lanes whose dims lie beyond D read the next tile's data or the zero
-      // pad: finite values whose query partners in A are zero.
-      auto lds_b = [&](int t, bf16x8 (&bk)[KS]) {
-        const char* kt = sK + lofs + t * TB;
+      // pad: finite values whose query partners in A are zero.  The packed
+      // tail block of group t/4 is read with tile 4 (t/4).
+      auto lds_b = [&](int t, bf16x8 (&bk)[KF]) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) bk[s] = *reinterpret_cast<const bf16x8*>(kt + frag_step_off<D>(s));
+        for (int s = 0; s < KF; ++s) bk[s] = *reinterpret_cast<const bf16x8*>(sK + lofs + frag_at(t, s));
+        if (TP && t % 4 == 0)
+          tbk[(t / 4) % 2] = *reinterpret_cast<const bf16x8*>(sK + lofs + tail_at(t / 4));
       };
-      auto mm = [&](const bf16x8 (&bk)[KS]) {
+      auto mm = [&](const bf16x8 (&bk)[KF], int t) {
         f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bk[s], a, 0, 0, 0);
+        for (int s = 0; s < KF; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bk[s], a, 0, 0, 0);
+        if (TP) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[t % 4], tbk[(t / 4) % 2], a, 0, 0, 0);
         return a;
       };
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t)
         if (t < NTILE) lds_b(t, bkb[t]);
-      f32x4 acc = mm(bkb[0]);
+      f32x4 acc = mm(bkb[0], 0);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) {
         if (t + NB - 1 < NTILE) lds_b(t + NB - 1, bkb[(t + NB - 1) % NB]);
         f32x4 accn = acc;
-        if (t + 1 < NTILE) accn = mm(bkb[(t + 1) % NB]);
+        if (t + 1 < NTILE) accn = mm(bkb[(t + 1) % NB], t + 1);
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(acc[r], c2, -b[r]));
@@ -988,7 +1054,7 @@ static int pick_ntm_rows(int N) {
 }
 
 static size_t rows_lds_bytes(int ntm, int D) {
-  return (size_t)ntm * 16 * D * 2 + 1024 + (size_t)kRowWaves * ntm * 16 * 4 + 16;
+  return (size_t)rows_k_bytes(D, ntm) + (size_t)kRowWaves * ntm * 16 * 4 + 16;
 }
 
 static bool rows_ok(int N, int D) {
