@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="llava_next_7b")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--no-salience", action="store_true")
+    p.add_argument("--salience-only", action="store_true",
+                   help="time only the prefill salience call (profiling runs); prints its object")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--seed", type=int, default=0)
@@ -154,6 +156,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.load()
+    if a.salience_only:
+        stream = torch.cuda.Stream(device=dev)  # default priority
+        print(json.dumps({"salience": bench_salience(a, dev, stream)}), flush=True)
+        return
     w = synthetic.DECODE[a.workload]
     print(f"[bench] workload {w.name}: B={w.B} L={w.L} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} "
           f"k={w.k} T={w.T}", file=sys.stderr, flush=True)
