@@ -170,6 +170,24 @@ def test_retrieve_long_rows_multi_token_query():
     _self_consistent(idx, sc, w.k)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [(torch.float32, 8, 8, 128), (torch.bfloat16, 16, 2, 64),
+                                             (torch.bfloat16, 32, 2, 128)])
+def test_retrieve_long_rows_dtypes_and_groups(dtype, Hq, Hkv, D):
+    """Long rows through sv_retrieve: fp32 caches, group size 8 (the parallel select) and
+    group size 16 (beyond it: the single-workgroup select)."""
+    B, N, k = 2, 3000, 400
+    g = torch.Generator().manual_seed(53)
+    q = torch.randn(B, 1, Hq, D, generator=g).to(dtype)
+    kv = torch.randn(B, N, Hkv, D, generator=g).to(dtype)
+    s_ref = oracle.retrieval_scores(q, kv)
+    _say("retrieve long rows", dtype, Hq, Hkv, D)
+    idx, sc = sv.retrieve(q.to(DEV), kv.to(DEV), k, scores=True)
+    torch.cuda.synchronize()
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, k)
+    assert ok, msgs[:3]
+    _self_consistent(idx, sc, k)
+
+
 @pytest.mark.parametrize("mode", ["all_equal", "outlier", "tied_block_300", "two_values"])
 def test_retrieve_long_rows_edge_distributions(mode):
     """The parallel select (rows over 2048 tokens) on rows that send it to its
