@@ -85,6 +85,23 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
+SALIENCE_SOURCES = ("salience.hip", "common.h")
+
+
+def committed_mfma_ops(workload, src_hash):
+    """MFMA flops one salience call executes, from the committed rocprofv3 counter
+    summary (bf16 score MFMAs plus f16 column sums), if still current."""
+    path = os.path.join(ROOT, "profiles", "salience_counters.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash:
+        return None
+    return (t["mfma_mops_bf16_per_call"] + t["mfma_mops_f16_per_call"]) * t["flops_per_mop"]
+
+
 def committed_traffic(kernel_key, src_hash, launches_per_unit=1):
     """Per-launch HBM bytes from the committed rocprofv3 counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -350,13 +367,19 @@ def bench_salience(a, dev, stream):
         secs = gpu_time(run, reps, stream) / reps
     flops = synthetic.flop_count_salience(sw)
     tflops = flops / secs / 1e12
+    executed = committed_mfma_ops(sw.name, source_hash(*SALIENCE_SOURCES))
     return {"workload": sw.name, "frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
             "head_dim": sw.D, "keep": sw.keep, "ms_per_call": round(secs * 1e3, 4),
             "tokens_per_s": round(sw.F * sw.N / secs, 1),
             "roofline": {"kernel": "salience_rows_kernel (+ flagged-item fp32 pass, head mean, per-frame top-k): whole call",
                          "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                         "flops_algorithmic": flops}}
+                         "flops_algorithmic": flops,
+                         # MFMA work the call executes (padding of D and of the key
+                         # tiles, column-sum MFMAs), from the committed counters
+                         "flops_executed_counters": executed,
+                         "executed_tflops": (round(executed / secs / 1e12, 2)
+                                             if executed else None)}}
 
 
 def cpu_baseline(a, w, layers):
