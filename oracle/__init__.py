@@ -1,5 +1,5 @@
 """CPU oracle (test infrastructure only; see oracle/sparsevila.py)."""
 from .sparsevila import (  # noqa: F401
     to_f64, retrieval_scores, topk_ascending, retrieve,
-    sparse_decode_attn, dense_decode_attn, salience, salience_prune,
+    sparse_decode_attn, dense_decode_attn, pack_selected, salience, salience_prune,
 )

@@ -26,7 +26,10 @@ its reason in the design notes):
   * the salience softmax uses scale 1/sqrt(D), full bidirectional attention
     within a frame, no mask;
   * decode attention attends the selected visual entries plus all txt_len[b]
-    text entries with scale 1/sqrt(D); query head h uses KV head h // G.
+    text entries with scale 1/sqrt(D); query head h uses KV head h // G;
+  * dense packing keeps the order of the index list and copies every KV head
+    of a selected token (one selected set per sequence); an index outside
+    [0, N) gives a zero row.
 
 Parity pins: every function here is pinned in tests/test_oracle.py against
 hand-derived fixtures (tests/golden/), closed forms, invariants, brute force
@@ -41,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "to_f64", "retrieval_scores", "topk_ascending", "retrieve",
-    "sparse_decode_attn", "dense_decode_attn", "salience", "salience_prune",
+    "sparse_decode_attn", "dense_decode_attn", "pack_selected", "salience", "salience_prune",
 ]
 
 
@@ -173,6 +176,36 @@ def dense_decode_attn(q, k_vis, v_vis, k_txt, v_txt, txt_len,
     B, N = Kv.shape[:2]
     idx = np.tile(np.arange(N, dtype=np.int64), (B, 1))
     return sparse_decode_attn(q, k_vis, v_vis, idx, k_txt, v_txt, txt_len, scale)
+
+
+def pack_selected(k_vis, v_vis, idx) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense packing of the selected visual KV entries into contiguous rows.
+
+    [summary] Sec. 3.2 (decode side): the selected KV entries are gathered
+    into contiguous memory, so that decode reads them with regular, coalesced
+    accesses instead of scattered ones; Sec. 3.3, kernel table (decoding
+    attention row): the packed, reduced cache is what decode attends.
+
+    k_vis, v_vis  [B][N][Hkv][D]
+    idx           [B][k] visual token indices
+    returns (k_pack, v_pack), each [B][k][Hkv][D] in the input's value type:
+        pack[b][j] = cache[b][idx[b][j]]   for 0 <= idx[b][j] < N,
+        pack[b][j] = 0                     otherwise.
+    Values are copied, never rounded (bit-exact).
+    """
+    Kv, Vv = np.asarray(to_f64(k_vis)), np.asarray(to_f64(v_vis))
+    ix = np.asarray(to_f64(idx))
+    B, N, Hkv, D = Kv.shape
+    k = ix.shape[1]
+    kp = np.zeros((B, k, Hkv, D), dtype=Kv.dtype)
+    vp = np.zeros((B, k, Hkv, D), dtype=Vv.dtype)
+    for b in range(B):
+        for j in range(k):
+            t = int(ix[b, j])
+            if 0 <= t < N:
+                kp[b, j] = Kv[b, t]
+                vp[b, j] = Vv[b, t]
+    return kp, vp
 
 
 def salience(vis_q, vis_k, scale: Optional[float] = None) -> np.ndarray:

@@ -311,6 +311,67 @@ def test_attention_empty_set_raises():
         oracle.sparse_decode_attn(q, kv, vv, np.zeros((1, 0), dtype=np.int64), kt, vt, np.array([0]))
 
 
+# ---------------------------------------------------------------- dense packing
+
+def _coded_cache(B, N, Hkv, D, tag):
+    """Cache whose every value spells out its own (b, t, g, d) position."""
+    b, t, g, d = np.meshgrid(np.arange(B), np.arange(N), np.arange(Hkv), np.arange(D),
+                             indexing="ij")
+    return tag * 1e7 + b * 1e5 + t * 1e2 + g * 1e1 + d * 1e0 + 0.25
+
+
+def _pack_decodes(kp, vp, idx, N):
+    """kp/vp hold, at (b, j, g, d), the code of (b, idx[b, j], g, d); zero if outside."""
+    B, k, Hkv, D = kp.shape
+    for b in range(B):
+        for j in range(k):
+            t = int(idx[b, j])
+            for g in range(Hkv):
+                for d in range(D):
+                    want_k = 1e7 + b * 1e5 + t * 1e2 + g * 1e1 + d + 0.25 if 0 <= t < N else 0.0
+                    want_v = 2e7 + b * 1e5 + t * 1e2 + g * 1e1 + d + 0.25 if 0 <= t < N else 0.0
+                    if kp[b, j, g, d] != want_k or vp[b, j, g, d] != want_v:
+                        return False
+    return True
+
+
+def test_pack_decodes_positions():
+    B, N, Hkv, D = 3, 11, 2, 4
+    K, V = _coded_cache(B, N, Hkv, D, 1), _coded_cache(B, N, Hkv, D, 2)
+    idx = np.array([[0, 4, 10], [9, 1, 3], [10, -1, 11]])
+    kp, vp = oracle.pack_selected(K, V, idx)
+    assert kp.shape == (B, 3, Hkv, D) and vp.shape == (B, 3, Hkv, D)
+    assert _pack_decodes(kp, vp, idx, N)
+
+
+def test_pack_identity_reverse_and_torch():
+    rng = np.random.default_rng(11)
+    K, V = rng.standard_normal((2, 9, 3, 5)), rng.standard_normal((2, 9, 3, 5))
+    ident = np.tile(np.arange(9), (2, 1))
+    kp, vp = oracle.pack_selected(K, V, ident)
+    assert np.array_equal(kp, K) and np.array_equal(vp, V)
+    kp, vp = oracle.pack_selected(K, V, ident[:, ::-1])
+    assert np.array_equal(kp, np.flip(K, axis=1)) and np.array_equal(vp, np.flip(V, axis=1))
+    idx = np.array([[2, 3, 7, 8], [0, 1, 5, 6]])
+    kp, _ = oracle.pack_selected(K, V, idx)
+    tk = torch.from_numpy(K)
+    want = torch.stack([tk[b].index_select(0, torch.from_numpy(idx[b])) for b in range(2)])
+    assert np.array_equal(kp, want.numpy())
+    kp, vp = oracle.pack_selected(K, V, np.zeros((2, 0), dtype=np.int64))
+    assert kp.shape == (2, 0, 3, 5) and vp.shape == (2, 0, 3, 5)
+
+
+def test_pack_then_attend_equals_sparse_attention_bitwise():
+    # Attending the packed rows 0..k-1 is the attention over the selected set.
+    rng = np.random.default_rng(12)
+    q, kv, vv, kt, vt = _rand_attn(rng, B=2, N=30, Hq=6, Hkv=2, D=8, Tmax=5)
+    idx, tl = np.array([[1, 4, 9, 29], [0, 2, 17, 18]]), np.array([5, 2])
+    kp, vp = oracle.pack_selected(kv, vv, idx)
+    a = oracle.sparse_decode_attn(q, kp, vp, np.tile(np.arange(4), (2, 1)), kt, vt, tl)
+    b = oracle.sparse_decode_attn(q, kv, vv, idx, kt, vt, tl)
+    assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------- salience
 def _rand_sal(rng, F=2, H=3, N=20, D=8, std=1.0):
     return rng.standard_normal((F, H, N, D)) * std, rng.standard_normal((F, H, N, D)) * std
@@ -423,6 +484,9 @@ _MUTANTS = [
     ("sparse_decode_attn", "scale = 1.0 / math.sqrt(D)", "scale = 1.0", "missing 1/sqrt(D)"),
     ("sparse_decode_attn", "z = (KE[:, g, :] @ q[b, h]) * scale", "z = (KE[:, 0, :] @ q[b, h]) * scale",
      "every head reads KV head 0"),
+    ("pack_selected", "vp[b, j] = Vv[b, t]", "vp[b, j] = Kv[b, t]", "pack copies K into V"),
+    ("pack_selected", "if 0 <= t < N:", "if 0 <= t < N - 1:", "pack drops the last token"),
+    ("pack_selected", "kp[b, j] = Kv[b, t]", "kp[b, j] = Kv[0, t]", "pack reads sequence 0"),
 ]
 
 
@@ -470,6 +534,10 @@ def _pins_pass(m, golden_dir):
         idx, tl = np.array([[0, 3, 8], [2, 5, 7]]), np.array([3, 1])
         if not np.allclose(m.sparse_decode_attn(q, kv, vv, idx, kt, vt, tl),
                            _loop_attn(q, kv, vv, idx, kt, vt, tl), rtol=1e-12, atol=1e-13):
+            return False
+        Kc, Vc = _coded_cache(2, 7, 2, 3, 1), _coded_cache(2, 7, 2, 3, 2)
+        pidx = np.array([[0, 6, 3], [6, 2, 7]])
+        if not _pack_decodes(*m.pack_selected(Kc, Vc, pidx), pidx, 7):
             return False
         g = _load(golden_dir, "attention_sparse.json")
         out = m.sparse_decode_attn(_arr(g["q"]), _arr(g["k_vis"]), _arr(g["v_vis"]),
