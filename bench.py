@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--salience-only", action="store_true",
                    help="time only the prefill salience call (profiling runs); prints its object")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-pack", action="store_true")
+    p.add_argument("--pack-only", action="store_true",
+                   help="time only the per-question pack and the decode over packed rows "
+                        "(profiling runs); prints its object")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--profile-traffic", action="store_true",
@@ -190,6 +194,10 @@ def main():
     ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
     ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
     torch.cuda.synchronize()
+    if a.pack_only:
+        stream = torch.cuda.Stream(device=dev)  # default priority
+        print(json.dumps({"packed": bench_packed(a, dev, stream, w, layers, ws_r, ws_a)}), flush=True)
+        return
 
     # Multi-turn workload: conversation rounds of decode steps over one reused
     # visual cache.  Step i takes a fresh query and the text length of its
@@ -333,6 +341,12 @@ def main():
                         "timed steps follow the schedule from its start",
             "visual_cache_unchanged": True})
 
+    # ------------------------------------------------------------ per-question dense packing
+    if not a.no_pack and sched is None:
+        res["packed"] = bench_packed(a, dev, stream, w, layers, ws_r, ws_a)
+        res["packed"]["decode_speedup_vs_fused_step"] = round(
+            res["packed"]["decode"]["steps_per_s"] / steps_per_s, 3)
+
     # ------------------------------------------------------------ prefill salience
     if not a.no_salience:
         res["salience"] = bench_salience(a, dev, stream)
@@ -342,6 +356,76 @@ def main():
         res["cpu_baseline"] = cpu_baseline(a, w, layers)
 
     print(json.dumps(res), flush=True)
+
+
+def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
+    """Per-question retrieval + dense packing, then decode steps over the packed rows.
+
+    One question (8 tokens) selects k visual tokens per sequence and layer;
+    sv_pack_selected copies their K and V rows into contiguous buffers; a
+    decode step then runs sv_sparse_decode_attn over the packed rows plus the
+    text entries at every layer.  Timed: the packs of one question (every
+    layer, whole batch; reported per launch) and the packed decode step (all
+    layers).
+    """
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+    e = 2 if w.dtype.itemsize == 2 else 4
+    row = w.Hkv * w.D * e
+    gq = torch.Generator(device=dev).manual_seed(synthetic.stream_seed(a.seed, w.name, "question"))
+    question = torch.randn((w.B, 8, w.Hq, w.D), generator=gq, device=dev).to(w.dtype)
+    idx = [sv.retrieve(question, d["k_vis"], w.k, workspace=ws_r) for d in layers]
+    packs = [sv.pack_selected(d["k_vis"], d["v_vis"], i) for d, i in zip(layers, idx)]
+    ar = torch.arange(w.k, dtype=torch.int32, device=dev).expand(w.B, w.k).contiguous()
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in layers]
+    torch.cuda.synchronize()
+
+    def pack_once():                       # every layer's pack for one question
+        for l, d in enumerate(layers):
+            sv.pack_selected(d["k_vis"], d["v_vis"], idx[l], out=packs[l])
+
+    def packed_step():
+        for l, d in enumerate(layers):
+            kp, vp = packs[l]
+            sv.sparse_decode_attn(d["q"], kp, vp, ar, d["k_txt"], d["v_txt"], d["txt_len"],
+                                  workspace=ws_a, out=out[l])
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            pack_once()
+            packed_step()
+        torch.cuda.synchronize()
+        g_pack = None if a.no_graph else capture(pack_once, stream)
+        g_step = None if a.no_graph else capture(packed_step, stream)
+        run_pack = g_pack.replay if g_pack is not None else pack_once
+        run_step = g_step.replay if g_step is not None else packed_step
+        for _ in range(3):
+            run_pack()
+            run_step()
+        reps = max(5, a.steps // 4)
+        pack_secs = gpu_time(run_pack, reps, stream) / (reps * w.L)
+        step_secs = gpu_time(run_step, a.steps, stream) / a.steps
+    pack_bytes = w.B * w.k * (4 * row + 4)                 # K and V rows read and written, idx
+    q = w.Hq * w.D * e
+    step_bytes = w.L * w.B * ((w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4)
+    pack_gbs = pack_bytes / pack_secs / 1e9
+    step_gbs = step_bytes / step_secs / 1e9
+    return {"question_tokens": 8,
+            "pack": {"kernel": "pack_kernel (one layer of the whole batch per launch)",
+                     "us_per_launch": round(pack_secs * 1e6, 3), "bytes_per_launch": pack_bytes,
+                     "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(pack_gbs / HBM_PEAK_GBS, 4)},
+                     "launches_per_question": w.L,
+                     "ms_per_question": round(pack_secs * w.L * 1e3, 4)},
+            "decode": {"what": "sv_sparse_decode_attn over packed rows 0..k-1 plus text, every layer",
+                       "steps_per_s": round(1.0 / step_secs, 2),
+                       "ms_per_step": round(step_secs * 1e3, 4), "bytes_per_step": step_bytes,
+                       "hbm_gbs_algorithmic": round(step_gbs, 1),
+                       "hbm_frac_algorithmic": round(step_gbs / HBM_PEAK_GBS, 4),
+                       "launch": "hipgraph" if g_step is not None else "eager"}}
 
 
 def bench_salience(a, dev, stream):

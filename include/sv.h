@@ -198,6 +198,40 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Dense packing of the selected visual entries (decode stage, once per
+ * question)
+ *
+ * SparseVILA velog summary, Sec. 3.2, decode side: the selected KV entries
+ * are gathered into contiguous memory, so that decode reads them with
+ * regular, coalesced accesses; Sec. 3.3, kernel table, decoding-attention
+ * row: decode attends that packed, reduced cache.  Typical use: sv_retrieve
+ * with Tq = the question's tokens, then sv_pack_selected, then every decode
+ * step of the answer calls sv_sparse_decode_attn on the packed rows
+ * (N = k, idx = 0..k-1) plus the text entries.
+ *
+ * For each sequence b and j < k, with t = idx[b][j]:
+ *     k_pack[b][j][:][:] = K[b][t][:][:],  v_pack[b][j][:][:] = V[b][t][:][:]
+ * for 0 <= t < N; a zero row for any other t.  Every KV head of the token is
+ * copied; values are moved, never converted (bit-exact).
+ *
+ *  k_vis,v_vis visual cache, element (b,t,g,d) at
+ *             ptr[b*vis_bstride + t*vis_tstride + g*D + d], t < N.  Read only.
+ *  idx        [B][k] int32 (any order; repeats allowed).
+ *  k_pack,v_pack  [B][k][Hkv][D] contiguous, dtype `dtype`; must not overlap
+ *             the caches.
+ * No workspace.  k == 0 enqueues nothing and returns SV_OK.
+ * Supported: dtype SV_BF16 or SV_F32; Hkv*D a multiple of 8 (bf16) or 4
+ * (fp32), at most 2^24; 16-byte aligned pointers.
+ * Errors: SV_EINVAL (B < 1, N < 1, Hkv < 1, D < 1, k < 0, NULL pointer,
+ * strides smaller than a row or not multiples of 16 bytes, misalignment),
+ * SV_EUNSUPPORTED, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+sv_status sv_pack_selected(const void* k_vis, const void* v_vis, int64_t vis_bstride,
+                           int64_t vis_tstride, int N, int Hkv, int D, sv_dtype dtype,
+                           const int32_t* idx, int B, int k, void* k_pack, void* v_pack,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Query-agnostic salience and per-frame pruning (prefill stage)
  *
  * SparseVILA velog summary, Sec. 3.1: salience is read off the vision

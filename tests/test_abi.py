@@ -162,3 +162,28 @@ def _fused(**kw):
 def test_retrieve_attend_rejects(kw, status):
     assert _fused(**kw) == status
     assert sv.load().sv_last_error()
+
+
+def _pack(**kw):
+    a = dict(kv=FAKE, vv=FAKE, bs=1440 * 4096, ts=4096, N=1440, Hkv=32, D=128, dt=sv.SV_BF16,
+             idx=FAKE, B=8, k=360, kp=FAKE, vp=FAKE, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_pack_selected(a["kv"], a["vv"], a["bs"], a["ts"], a["N"], a["Hkv"], a["D"],
+                                a["dt"], a["idx"], a["B"], a["k"], a["kp"], a["vp"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(N=0), 1), (dict(k=-1), 1), (dict(Hkv=0), 1),
+    (dict(idx=None), 1), (dict(kv=None), 1), (dict(vp=None), 1),
+    (dict(ts=4000), 1), (dict(ts=4100), 1), (dict(bs=-8), 1), (dict(Hkv=1, D=4), 1),
+    (dict(kp=FAKE + 8), 1), (dict(vv=FAKE + 4), 1),
+    (dict(dt=3), 2), (dict(Hkv=1 << 13, D=1 << 12, ts=1 << 25, bs=1 << 35), 2),
+])
+def test_pack_rejects(kw, status):
+    assert _pack(**kw) == status
+
+
+def test_pack_k0_enqueues_nothing():
+    # k == 0 is a valid empty request: OK without touching any pointer.
+    assert _pack(k=0, kv=None, vv=None, idx=None, kp=None, vp=None) == 0

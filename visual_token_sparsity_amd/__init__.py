@@ -25,7 +25,7 @@ __all__ = [
     "SvError", "lib_path", "load", "retrieve", "retrieve_workspace_bytes",
     "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
     "salience_prune_workspace_bytes", "new_workspace", "retrieve_attend",
-    "retrieve_attend_workspace_bytes", "SV_F32", "SV_BF16",
+    "retrieve_attend_workspace_bytes", "pack_selected", "SV_F32", "SV_BF16",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -72,6 +72,9 @@ def load() -> ctypes.CDLL:
                                        c_p, c_p, c_i64, c_i64, c_p, c_i, c_i, c_f, c_p, c_p, c_p,
                                        c_p, c_sz, c_p]
     lib.sv_retrieve_attend.restype = c_i
+    lib.sv_pack_selected.argtypes = [c_p, c_p, c_i64, c_i64, c_i, c_i, c_i, c_i, c_p, c_i, c_i,
+                                     c_p, c_p, c_p]
+    lib.sv_pack_selected.restype = c_i
     lib.sv_salience_prune_workspace.argtypes = [c_i, c_i, c_i]
     lib.sv_salience_prune_workspace.restype = c_sz
     lib.sv_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_p, c_p,
@@ -224,6 +227,39 @@ def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor
         _dtype(q), float(scale) if scale else 0.0, res.data_ptr(), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(dev)))
     return res
+
+
+def pack_selected(k_vis: torch.Tensor, v_vis: torch.Tensor, idx: torch.Tensor, *,
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Copy the selected visual rows into contiguous [B][k][Hkv][D] buffers.
+
+    k_vis, v_vis  [B][N][Hkv][D] (same strides), bf16/fp32
+    idx           int32 [B][k]; an index outside [0, N) gives a zero row
+    returns (k_pack, v_pack), same dtype as the caches
+    """
+    lib = load()
+    dev = _on_gpu(k_vis, v_vis, idx)
+    if k_vis.stride() != v_vis.stride() or k_vis.shape != v_vis.shape or k_vis.dtype != v_vis.dtype:
+        raise ValueError("k_vis and v_vis must share shape, strides and dtype")
+    bs, ts = _cache_strides(k_vis, "k_vis")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != k_vis.shape[0]:
+        raise TypeError("idx must be int32 [B][k]")
+    idx = idx.contiguous()
+    B, N, Hkv, D = k_vis.shape
+    k = idx.shape[1]
+    if out is not None:
+        kp, vp = out
+        for t in (kp, vp):
+            if t.shape != (B, k, Hkv, D) or t.dtype != k_vis.dtype or not t.is_contiguous():
+                raise ValueError("out buffers must be contiguous [B][k][Hkv][D] of the cache dtype")
+    else:
+        kp = torch.empty((B, k, Hkv, D), dtype=k_vis.dtype, device=dev)
+        vp = torch.empty_like(kp)
+    _check(lib.sv_pack_selected(k_vis.data_ptr(), v_vis.data_ptr(), bs, ts, N, Hkv, D,
+                                _dtype(k_vis), idx.data_ptr(), B, k, kp.data_ptr(), vp.data_ptr(),
+                                _stream(dev)))
+    return kp, vp
 
 
 def retrieve_attend_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, N: int, k: int,

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "common.h"
+#include "pack.h"
 #include "sv.h"
 
 namespace {
@@ -209,6 +210,32 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
                                     (int)dtype, sc, out, (float*)workspace, counters, 0,
                                     (hipStream_t)stream),
                     "sv_sparse_decode_attn");
+}
+
+// ---------------------------------------------------------------- dense packing
+sv_status sv_pack_selected(const void* k_vis, const void* v_vis, int64_t vis_bstride,
+                           int64_t vis_tstride, int N, int Hkv, int D, sv_dtype dtype,
+                           const int32_t* idx, int B, int k, void* k_pack, void* v_pack,
+                           void* stream) {
+  if (B < 1 || N < 1 || Hkv < 1 || D < 1 || k < 0)
+    return fail(SV_EINVAL, "sv_pack_selected: bad sizes B=%d N=%d Hkv=%d D=%d k=%d", B, N, Hkv, D, k);
+  if (k == 0) return SV_OK;
+  if (!k_vis || !v_vis || !idx || !k_pack || !v_pack)
+    return fail(SV_EINVAL, "sv_pack_selected: NULL cache, idx or destination");
+  if (!dtype_ok(dtype)) return fail(SV_EUNSUPPORTED, "sv_pack_selected: dtype %d", (int)dtype);
+  const int ve = vec_elems(dtype);
+  const int64_t R = (int64_t)Hkv * D;
+  if (R % ve) return fail(SV_EINVAL, "sv_pack_selected: Hkv*D=%lld not a multiple of %d", (long long)R, ve);
+  if (R > ((int64_t)1 << 24))
+    return fail(SV_EUNSUPPORTED, "sv_pack_selected: row of %lld elements too long", (long long)R);
+  if (vis_tstride < R || vis_bstride < 0 || vis_tstride % ve || vis_bstride % ve)
+    return fail(SV_EINVAL, "sv_pack_selected: strides must be >= row and multiples of %d", ve);
+  if (!aligned16(k_vis) || !aligned16(v_vis) || !aligned16(k_pack) || !aligned16(v_pack))
+    return fail(SV_EINVAL, "sv_pack_selected: caches and destinations must be 16-byte aligned");
+  return hip_status(sv::launch_pack(k_vis, v_vis, vis_bstride, vis_tstride, N, (int)R,
+                                    dtype == SV_BF16 ? 2 : 4, idx, B, k, k_pack, v_pack,
+                                    (hipStream_t)stream),
+                    "sv_pack_selected");
 }
 
 // ---------------------------------------------------------------- fused layer
