@@ -81,6 +81,10 @@ FUSED_SOURCES = ("fused.hip", "fused_kernel.h", "fused_bf16.hip", "fused_f32.hip
                  "decode_items.h", "long_select.h", "select.h", "common.h")
 
 
+# Sources of the dense-packing kernel.
+PACK_SOURCES = ("pack.hip", "pack.h", "common.h")
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -117,6 +121,17 @@ def committed_traffic(kernel_key, src_hash, launches_per_unit=1):
     if t.get("source_hash") != src_hash:
         return None
     return t.get("bytes_per_launch")
+
+
+def calibration_copy(torch, dev):
+    """Two 1 GiB device-to-device copies: the known-size reference of the counter passes."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return src.numel()
 
 
 def gpu_time(fn, reps, stream):
@@ -196,7 +211,9 @@ def main():
     torch.cuda.synchronize()
     if a.pack_only:
         stream = torch.cuda.Stream(device=dev)  # default priority
-        print(json.dumps({"packed": bench_packed(a, dev, stream, w, layers, ws_r, ws_a)}), flush=True)
+        res = bench_packed(a, dev, stream, w, layers, ws_r, ws_a)
+        if res is not None:
+            print(json.dumps({"packed": res}), flush=True)
         return
 
     # Multi-turn workload: conversation rounds of decode steps over one reused
@@ -246,14 +263,10 @@ def main():
         # known size whose counters give the scale factor of the counters.
         for _ in range(2):
             step()
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        nbytes = calibration_copy(torch, dev)
         print(json.dumps({"profile_traffic": w.name, "layer_bytes": decode_bytes(w)[1],
-                          "copy_bytes": src.numel()}), flush=True)
+                          "copy_bytes": nbytes}), flush=True)
         return
 
     stream = torch.cuda.Stream(device=dev)      # default priority
@@ -386,6 +399,18 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
         for l, d in enumerate(layers):
             sv.pack_selected(d["k_vis"], d["v_vis"], idx[l], out=packs[l])
 
+    pack_bytes = w.B * w.k * (4 * row + 4)                 # K and V rows read and written, idx
+    if a.profile_traffic:
+        # Counter passes: the packs of two questions (eager), then the copy
+        # calibration.
+        for _ in range(2):
+            pack_once()
+        torch.cuda.synchronize()
+        calibration_copy(torch, dev)
+        print(json.dumps({"profile_traffic": f"pack_{w.name}", "launch_bytes": pack_bytes}),
+              flush=True)
+        return None
+
     def packed_step():
         for l, d in enumerate(layers):
             kp, vp = packs[l]
@@ -407,7 +432,6 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
         reps = max(5, a.steps // 4)
         pack_secs = gpu_time(run_pack, reps, stream) / (reps * w.L)
         step_secs = gpu_time(run_step, a.steps, stream) / a.steps
-    pack_bytes = w.B * w.k * (4 * row + 4)                 # K and V rows read and written, idx
     q = w.Hq * w.D * e
     step_bytes = w.L * w.B * ((w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4)
     pack_gbs = pack_bytes / pack_secs / 1e9
@@ -417,7 +441,9 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
                      "us_per_launch": round(pack_secs * 1e6, 3), "bytes_per_launch": pack_bytes,
                      "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(pack_gbs / HBM_PEAK_GBS, 4)},
+                                  "frac": round(pack_gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": committed_traffic(f"pack_{w.name}",
+                                                               source_hash(*PACK_SOURCES))},
                      "launches_per_question": w.L,
                      "ms_per_question": round(pack_secs * w.L * 1e3, 4)},
             "decode": {"what": "sv_sparse_decode_attn over packed rows 0..k-1 plus text, every layer",
