@@ -126,3 +126,31 @@ def test_question_retrieve_pack_then_decode_steps(wl, ov):
         assert ok, (step, err)
         ok, err = accept.check_attention(out_s.cpu().numpy(), ref)
         assert ok, (step, err)
+
+
+def test_pack_graph_replays_match_oracle():
+    """A captured pack, replayed with new index lists written between replays."""
+    B, N, Hkv, D, k = 4, 300, 8, 128, 45
+    _say("pack graph replays", B, N, Hkv, D, k)
+    kc, vc = _cache((B, N, Hkv, D), torch.bfloat16, 9), _cache((B, N, Hkv, D), torch.bfloat16, 10)
+    idx = torch.zeros((B, k), dtype=torch.int32, device=DEV)
+    kp = torch.empty((B, k, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    vp = torch.empty_like(kp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sv.pack_selected(kc, vc, idx, out=(kp, vp))       # warm-up before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            sv.pack_selected(kc, vc, idx, out=(kp, vp))
+    g = torch.Generator().manual_seed(synthetic.stream_seed(11, "pack_graph"))
+    for rep in range(4):
+        new = torch.stack([torch.randperm(N, generator=g)[:k].sort().values for _ in range(B)])
+        idx.copy_(new.to(torch.int32).to(DEV))
+        kp.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want_k, want_v = oracle.pack_selected(kc, vc, new.numpy())
+        assert np.array_equal(_f64(kp), want_k), rep
+        assert np.array_equal(_f64(vp), want_v), rep
