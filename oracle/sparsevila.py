@@ -27,6 +27,11 @@ its reason in the design notes):
     within a frame, no mask;
   * decode attention attends the selected visual entries plus all txt_len[b]
     text entries with scale 1/sqrt(D); query head h uses KV head h // G;
+  * summary-token salience (CLIP: one summary token, RADIO: several) is the
+    attention the summary tokens pay to each token, averaged over the
+    summary tokens and the heads; the summary tokens are the first S tokens
+    of the frame, and every token (summary tokens included) is scored and
+    can be kept;
   * dense packing keeps the order of the index list and copies every KV head
     of a selected token (one selected set per sequence); an index outside
     [0, N) gives a zero row.
@@ -45,6 +50,7 @@ import numpy as np
 __all__ = [
     "to_f64", "retrieval_scores", "topk_ascending", "retrieve",
     "sparse_decode_attn", "dense_decode_attn", "pack_selected", "salience", "salience_prune",
+    "summary_salience", "summary_salience_prune",
 ]
 
 
@@ -248,4 +254,46 @@ def salience_prune(vis_q, vis_k, keep: int,
     returns (s [F][N] float64, idx [F][keep] int64 ascending)
     """
     s = salience(vis_q, vis_k, scale)
+    return s, topk_ascending(s, keep)
+
+
+def summary_salience(vis_q, vis_k, S: int, scale: Optional[float] = None) -> np.ndarray:
+    """Salience read off the attention of the summary tokens (CLIP, RADIO).
+
+    [summary] Sec. 3.1, salience table: with one summary token (CLIP) a
+    token's importance is the attention through which it feeds the global
+    (summary) embedding; with several summary tokens (RADIO) it is that
+    attention averaged over the summary tokens.  Read as the softmax rows of
+    the summary tokens' queries: summary token s attends over all N tokens,
+    and token j receives A_h[s, j].
+
+    vis_q, vis_k [F][H][N][D]; the summary tokens are rows 0..S-1.
+    returns s [F][N] float64:
+        A_h = row-softmax(scale * Q_h[0:S] K_h^T)   (S x N)
+        s[f, j] = (1/H) sum_h (1/S) sum_{s<S} A_h[s, j]
+    Each frame sums to 1 over j.
+    """
+    Q, K = to_f64(vis_q), to_f64(vis_k)
+    F, H, N, D = Q.shape
+    if not 1 <= S <= N:
+        raise ValueError("need 1 <= S <= N summary tokens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((F, N), dtype=np.float64)
+    for f in range(F):
+        for h in range(H):
+            Z = (Q[f, h, :S] @ K[f, h].T) * scale          # [S][N]
+            Z = Z - Z.max(axis=1, keepdims=True)
+            A = np.exp(Z)
+            A = A / A.sum(axis=1, keepdims=True)
+            out[f] += A.sum(axis=0) / S
+        out[f] /= H
+    return out
+
+
+def summary_salience_prune(vis_q, vis_k, S: int, keep: int,
+                           scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Summary-token salience and the ``keep`` most salient tokens per frame
+    (ascending indices, ties toward the lower index), as ``salience_prune``."""
+    s = summary_salience(vis_q, vis_k, S, scale)
     return s, topk_ascending(s, keep)

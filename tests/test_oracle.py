@@ -311,6 +311,51 @@ def test_attention_empty_set_raises():
         oracle.sparse_decode_attn(q, kv, vv, np.zeros((1, 0), dtype=np.int64), kt, vt, np.array([0]))
 
 
+# ---------------------------------------------------------------- summary-token salience
+
+def test_summary_salience_all_tokens_is_the_intra_visual_mean():
+    # Every token a summary token: the no-summary (SigLIP/QwenVL) definition.
+    rng = np.random.default_rng(21)
+    Q, K = _rand_sal(rng, F=2, H=3, N=12, D=8)
+    np.testing.assert_allclose(oracle.summary_salience(Q, K, 12), oracle.salience(Q, K),
+                               rtol=1e-13, atol=1e-16)
+
+
+def test_summary_salience_one_token_is_scipy_softmax():
+    from scipy.special import softmax
+    rng = np.random.default_rng(22)
+    Q, K = _rand_sal(rng, F=3, H=1, N=17, D=8)
+    got = oracle.summary_salience(Q, K, 1)
+    for f in range(3):
+        want = softmax(K[f, 0] @ Q[f, 0, 0] / math.sqrt(8))
+        np.testing.assert_allclose(got[f], want, rtol=1e-13)
+
+
+def test_summary_salience_bruteforce_and_sums():
+    rng = np.random.default_rng(23)
+    F, H, N, D, S = 2, 2, 7, 4, 3
+    Q, K = _rand_sal(rng, F=F, H=H, N=N, D=D)
+    got = oracle.summary_salience(Q, K, S, scale=0.7)
+    want = np.zeros((F, N))
+    for f in range(F):
+        for h in range(H):
+            for s in range(S):
+                z = [sum(Q[f, h, s, d] * K[f, h, j, d] for d in range(D)) * 0.7 for j in range(N)]
+                e = [math.exp(v) for v in z]
+                for j in range(N):
+                    want[f, j] += e[j] / sum(e) / (S * H)
+    np.testing.assert_allclose(got, want, rtol=1e-12)
+    np.testing.assert_allclose(got.sum(axis=1), 1.0, rtol=1e-13)
+    # rows S.. do not matter
+    Q2 = Q.copy()
+    Q2[:, :, S:] = rng.standard_normal(Q2[:, :, S:].shape)
+    np.testing.assert_array_equal(oracle.summary_salience(Q2, K, S, scale=0.7), got)
+    _, idx = oracle.summary_salience_prune(Q, K, S, 4, scale=0.7)
+    assert idx.shape == (F, 4) and all(list(r) == sorted(r) for r in idx.tolist())
+    with pytest.raises(ValueError):
+        oracle.summary_salience(Q, K, 0)
+
+
 # ---------------------------------------------------------------- dense packing
 
 def _coded_cache(B, N, Hkv, D, tag):
@@ -485,6 +530,11 @@ _MUTANTS = [
     ("sparse_decode_attn", "z = (KE[:, g, :] @ q[b, h]) * scale", "z = (KE[:, 0, :] @ q[b, h]) * scale",
      "every head reads KV head 0"),
     ("pack_selected", "vp[b, j] = Vv[b, t]", "vp[b, j] = Kv[b, t]", "pack copies K into V"),
+    ("summary_salience", "Q[f, h, :S] @ K[f, h].T", "Q[f, h, 1:S + 1] @ K[f, h].T",
+     "summary rows shifted by one"),
+    ("summary_salience", "out[f] += A.sum(axis=0) / S", "out[f] += A.sum(axis=1).mean() / S",
+     "row sums instead of column sums"),
+    ("summary_salience", "out[f] /= H", "out[f] /= 1", "heads summed, not averaged"),
     ("pack_selected", "if 0 <= t < N:", "if 0 <= t < N - 1:", "pack drops the last token"),
     ("pack_selected", "kp[b, j] = Kv[b, t]", "kp[b, j] = Kv[0, t]", "pack reads sequence 0"),
 ]
@@ -534,6 +584,12 @@ def _pins_pass(m, golden_dir):
         idx, tl = np.array([[0, 3, 8], [2, 5, 7]]), np.array([3, 1])
         if not np.allclose(m.sparse_decode_attn(q, kv, vv, idx, kt, vt, tl),
                            _loop_attn(q, kv, vv, idx, kt, vt, tl), rtol=1e-12, atol=1e-13):
+            return False
+        from scipy.special import softmax
+        Qs, Ks = rng.standard_normal((2, 2, 6, 4)), rng.standard_normal((2, 2, 6, 4))
+        ss = m.summary_salience(Qs, Ks, 2)
+        want = sum(softmax(Ks[0, h] @ Qs[0, h, s] / 2.0) for h in range(2) for s in range(2)) / 4
+        if not np.allclose(ss[0], want, rtol=1e-12):
             return False
         Kc, Vc = _coded_cache(2, 7, 2, 3, 1), _coded_cache(2, 7, 2, 3, 2)
         pidx = np.array([[0, 6, 3], [6, 2, 7]])
