@@ -50,6 +50,10 @@ def parse():
                    help="time only the prefill salience call (profiling runs); prints its object")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pack", action="store_true")
+    p.add_argument("--no-summary", action="store_true")
+    p.add_argument("--summary-only", action="store_true",
+                   help="time only the summary-token salience calls (profiling runs); prints "
+                        "their object")
     p.add_argument("--pack-only", action="store_true",
                    help="time only the per-question pack and the decode over packed rows "
                         "(profiling runs); prints its object")
@@ -195,6 +199,10 @@ def main():
     if a.salience_only:
         stream = torch.cuda.Stream(device=dev)  # default priority
         print(json.dumps({"salience": bench_salience(a, dev, stream)}), flush=True)
+        return
+    if a.summary_only:
+        stream = torch.cuda.Stream(device=dev)  # default priority
+        print(json.dumps({"summary_salience": bench_summary(a, dev, stream)}), flush=True)
         return
     w = synthetic.DECODE[a.workload]
     print(f"[bench] workload {w.name}: B={w.B} L={w.L} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} "
@@ -364,6 +372,9 @@ def main():
     if not a.no_salience:
         res["salience"] = bench_salience(a, dev, stream)
 
+    if not a.no_summary:
+        res["summary_salience"] = bench_summary(a, dev, stream)
+
     # ------------------------------------------------------------ CPU oracle baseline
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(a, w, layers)
@@ -452,6 +463,53 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
                        "hbm_gbs_algorithmic": round(step_gbs, 1),
                        "hbm_frac_algorithmic": round(step_gbs / HBM_PEAK_GBS, 4),
                        "launch": "hipgraph" if g_step is not None else "eager"}}
+
+
+def bench_summary(a, dev, stream):
+    """Summary-token salience and per-frame pruning: CLIP shape (one CLS token) and
+    RADIO shape (4 summary tokens), one graph-captured call each."""
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+    res = {}
+    for name, S in (("clip_l14_336_256f", 1), ("radio_1028_64f", 4)):
+        sw = synthetic.SALIENCE[name]
+        Q, K = synthetic.make_salience(sw, a.seed, device=dev, gen_device="cuda")
+        sal = torch.empty((sw.F, sw.N), dtype=torch.float32, device=dev)
+        keep = torch.empty((sw.F, sw.keep), dtype=torch.int32, device=dev)
+        ws = sv.new_workspace(sv.summary_salience_prune_workspace_bytes(sw.F, sw.H, sw.N), dev)
+
+        def once():
+            sv.summary_salience_prune(Q, K, S, sw.keep, workspace=ws, salience_out=sal,
+                                      idx_out=keep)
+
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                once()
+            g = None if a.no_graph else capture(once, stream)
+            run = g.replay if g is not None else once
+            for _ in range(3):
+                run()
+            reps = max(10, a.steps // 2)
+            secs = gpu_time(run, reps, stream) / reps
+        # keys once, the summary queries, per-head column values written and read
+        # back, the salience written and read by the select, the kept indices
+        nbytes = (sw.F * sw.H * sw.N * sw.D * 2 + sw.F * sw.H * S * sw.D * 2
+                  + 2 * sw.F * sw.H * sw.N * 4 + 2 * sw.F * sw.N * 4 + sw.F * sw.keep * 4)
+        gbs = nbytes / secs / 1e9
+        res[name] = {"frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
+                     "head_dim": sw.D, "summary_tokens": S, "keep": sw.keep,
+                     "ms_per_call": round(secs * 1e3, 4),
+                     "tokens_per_s": round(sw.F * sw.N / secs, 1),
+                     "roofline": {"kernel": "summary_cols_kernel + summary_mean_kernel + "
+                                            "per-frame top-k: whole call",
+                                  "bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "bytes_algorithmic": nbytes}}
+        del Q, K
+    return res
 
 
 def bench_salience(a, dev, stream):

@@ -267,6 +267,42 @@ sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H,
                             float* salience_out, int32_t* idx_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Summary-token salience and per-frame pruning (prefill stage)
+ *
+ * SparseVILA velog summary, Sec. 3.1, salience table: for an encoder with
+ * one summary token (CLIP) a token's importance is the attention through
+ * which it feeds that global token; with several summary tokens (RADIO) it
+ * is that attention averaged over them.  The summary tokens are the first S
+ * tokens of each frame (CLIP's CLS token: S = 1).
+ *
+ * For each frame f and head h:
+ *     A_h = row_softmax(scale * Q_h[0:S] K_h^T)            (S x N, never stored)
+ *     sal[f,j] = (1/H) sum_h (1/S) sum_{s<S} A_h[s,j]       (sums to 1)
+ * over every token j, summary tokens included; then the `keep` largest
+ * sal[f,.] (ties toward the lower index) in ascending order.
+ *
+ *  vis_q,vis_k [F][H][N][D] contiguous bf16 (one encoder layer's Q and K;
+ *             only rows 0..S-1 of Q are read).
+ *  scale       softmax scale; <= 0 selects 1/sqrt(D).
+ *  S           summary tokens, 1 <= S <= N.
+ *  keep        tokens kept per frame, 0 <= keep <= N.
+ *  salience_out optional [F][N] fp32 (NULL: kept in the workspace).
+ *  idx_out     [F][keep] int32 ascending (may be NULL if keep == 0).
+ *  workspace   at least sv_summary_salience_prune_workspace(F, H, N) bytes,
+ *              256-byte aligned; no zero-fill needed.
+ * Supported: dtype SV_BF16; D a multiple of 8, at most 128; S <= 16,
+ * N <= 4096, S*N <= 12288; F <= 65535.
+ * Errors: SV_EINVAL (NULL pointer, S or keep out of range, bad sizes,
+ * misalignment), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_summary_salience_prune_workspace(int F, int H, int N);
+
+sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F, int H, int N,
+                                    int D, sv_dtype dtype, float scale, int S, int keep,
+                                    float* salience_out, int32_t* idx_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,6 +99,13 @@ SALIENCE: Dict[str, SalienceWorkload] = {
     # Alternative reading of N(0, 1/sqrt(72)): standard deviation 1/sqrt(72).
     "siglip_256f_narrow": SalienceWorkload(
         name="siglip_256f_narrow", F=256, N=729, H=16, D=72, keep=364, std=72 ** -0.5),
+    # Summary-token encoders: CLIP ViT-L/14 at 336 px (one CLS token + 24 x 24
+    # patches, 16 heads of 64) and a RADIO-style encoder (4 summary tokens +
+    # 32 x 32 patches, 16 heads of 64); same entry distribution as above.
+    "clip_l14_336_256f": SalienceWorkload(
+        name="clip_l14_336_256f", F=256, N=577, H=16, D=64, keep=288, std=64 ** -0.25),
+    "radio_1028_64f": SalienceWorkload(
+        name="radio_1028_64f", F=64, N=1028, H=16, D=64, keep=514, std=64 ** -0.25),
 }
 
 # Multi-turn schedule of the 131072-token workload: 3 rounds x 128 decode steps,

@@ -187,3 +187,29 @@ def test_pack_rejects(kw, status):
 def test_pack_k0_enqueues_nothing():
     # k == 0 is a valid empty request: OK without touching any pointer.
     assert _pack(k=0, kv=None, vv=None, idx=None, kp=None, vp=None) == 0
+
+
+def _summ(**kw):
+    a = dict(q=FAKE, k=FAKE, F=2, H=16, N=577, D=64, dt=sv.SV_BF16, scale=0.0, S=1, keep=288,
+             sal=None, idx=FAKE, ws=FAKE, wsb=1 << 24, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_summary_salience_prune(a["q"], a["k"], a["F"], a["H"], a["N"], a["D"], a["dt"],
+                                         a["scale"], a["S"], a["keep"], a["sal"], a["idx"],
+                                         a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), 1), (dict(S=578), 1), (dict(keep=578), 1), (dict(keep=-1), 1), (dict(F=0), 1),
+    (dict(idx=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(k=FAKE + 8), 1),
+    (dict(dt=sv.SV_F32), 2), (dict(D=136), 2), (dict(D=60), 2), (dict(S=17, N=600), 2),
+    (dict(N=4097, keep=10), 2), (dict(S=16, N=800), 2), (dict(F=65536), 2),
+    (dict(wsb=1024), 3),
+])
+def test_summary_salience_rejects(kw, status):
+    assert _summ(**kw) == status
+
+
+def test_summary_salience_workspace_size():
+    lib = sv.load()
+    assert lib.sv_summary_salience_prune_workspace(2, 16, 577) >= (2 * 16 * 577 + 2 * 577) * 4

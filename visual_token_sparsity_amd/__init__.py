@@ -25,7 +25,8 @@ __all__ = [
     "SvError", "lib_path", "load", "retrieve", "retrieve_workspace_bytes",
     "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
     "salience_prune_workspace_bytes", "new_workspace", "retrieve_attend",
-    "retrieve_attend_workspace_bytes", "pack_selected", "SV_F32", "SV_BF16",
+    "retrieve_attend_workspace_bytes", "pack_selected", "summary_salience_prune",
+    "summary_salience_prune_workspace_bytes", "SV_F32", "SV_BF16",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -80,6 +81,11 @@ def load() -> ctypes.CDLL:
     lib.sv_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_p, c_p,
                                       c_p, c_sz, c_p]
     lib.sv_salience_prune.restype = c_i
+    lib.sv_summary_salience_prune_workspace.argtypes = [c_i, c_i, c_i]
+    lib.sv_summary_salience_prune_workspace.restype = c_sz
+    lib.sv_summary_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_i,
+                                              c_p, c_p, c_p, c_sz, c_p]
+    lib.sv_summary_salience_prune.restype = c_i
     _LIB = lib
     return lib
 
@@ -349,4 +355,35 @@ def salience_prune(vis_q: torch.Tensor, vis_k: torch.Tensor, keep: int,
                                  float(scale) if scale else 0.0, keep, sal.data_ptr(),
                                  idx.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream(dev)))
+    return sal, idx
+
+
+def summary_salience_prune_workspace_bytes(F: int, H: int, N: int) -> int:
+    return int(load().sv_summary_salience_prune_workspace(F, H, N))
+
+
+def summary_salience_prune(vis_q: torch.Tensor, vis_k: torch.Tensor, S: int, keep: int,
+                           scale: Optional[float] = None, *,
+                           workspace: Optional[torch.Tensor] = None,
+                           salience_out: Optional[torch.Tensor] = None,
+                           idx_out: Optional[torch.Tensor] = None):
+    """Salience from the attention of the first ``S`` (summary) tokens, and the
+    ``keep`` most salient tokens per frame.
+
+    vis_q, vis_k  [F][H][N][D] bf16, contiguous (rows 0..S-1 of vis_q are read)
+    returns (salience fp32 [F][N], idx int32 [F][keep] ascending)
+    """
+    lib = load()
+    dev = _on_gpu(vis_q, vis_k)
+    if vis_q.shape != vis_k.shape or vis_q.dim() != 4:
+        raise ValueError("vis_q and vis_k must both be [F][H][N][D]")
+    vis_q, vis_k = vis_q.contiguous(), vis_k.contiguous()
+    F, H, N, D = vis_q.shape
+    sal = salience_out if salience_out is not None else torch.empty((F, N), dtype=torch.float32, device=dev)
+    idx = idx_out if idx_out is not None else torch.empty((F, max(keep, 0)), dtype=torch.int32, device=dev)
+    ws = _workspace(summary_salience_prune_workspace_bytes(F, H, N), dev, workspace)
+    _check(lib.sv_summary_salience_prune(vis_q.data_ptr(), vis_k.data_ptr(), F, H, N, D,
+                                         _dtype(vis_q), float(scale) if scale else 0.0, S, keep,
+                                         sal.data_ptr(), idx.data_ptr(), ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(dev)))
     return sal, idx

@@ -10,6 +10,7 @@
 
 #include "common.h"
 #include "pack.h"
+#include "summary.h"
 #include "sv.h"
 
 namespace {
@@ -370,3 +371,43 @@ sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- summary-token salience
+// Workspace: [per-head column values F*H*N][salience F*N, when salience_out is NULL]
+size_t sv_summary_salience_prune_workspace(int F, int H, int N) {
+  if (F < 1 || H < 1 || N < 1) return 256;
+  return align256((size_t)F * H * N * sizeof(float)) + align256((size_t)F * N * sizeof(float));
+}
+
+sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F, int H, int N,
+                                    int D, sv_dtype dtype, float scale, int S, int keep,
+                                    float* salience_out, int32_t* idx_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const char* fn = "sv_summary_salience_prune";
+  if (!vis_q || !vis_k || !workspace) return fail(SV_EINVAL, "%s: NULL q, k or workspace", fn);
+  if (F < 1 || H < 1 || N < 1 || D < 1)
+    return fail(SV_EINVAL, "%s: bad sizes F=%d H=%d N=%d D=%d", fn, F, H, N, D);
+  if (S < 1 || S > N) return fail(SV_EINVAL, "%s: S=%d summary tokens outside [1, N=%d]", fn, S, N);
+  if (keep < 0 || keep > N) return fail(SV_EINVAL, "%s: keep=%d outside [0, N=%d]", fn, keep, N);
+  if (keep > 0 && !idx_out) return fail(SV_EINVAL, "%s: NULL idx_out", fn);
+  if (!aligned16(vis_q) || !aligned16(vis_k))
+    return fail(SV_EINVAL, "%s: q and k must be 16-byte aligned", fn);
+  if (dtype != SV_BF16) return fail(SV_EUNSUPPORTED, "%s: dtype %d (bf16 only)", fn, (int)dtype);
+  if (D % 8 || D > 128) return fail(SV_EUNSUPPORTED, "%s: D=%d (a multiple of 8, at most 128)", fn, D);
+  if (S > sv::kSummaryMaxS || N > sv::kSummaryMaxN || (int64_t)S * N > sv::kSummaryMaxLogits)
+    return fail(SV_EUNSUPPORTED, "%s: S=%d, N=%d outside S <= %d, N <= %d, S*N <= %d", fn, S, N,
+                sv::kSummaryMaxS, sv::kSummaryMaxN, sv::kSummaryMaxLogits);
+  if (F > 65535 || (int64_t)F * H > 2147483647LL)
+    return fail(SV_EUNSUPPORTED, "%s: F=%d, F*H too large", fn, F);
+  const size_t need = sv_summary_salience_prune_workspace(F, H, N);
+  if (workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  float* colh = (float*)workspace;
+  float* sal = salience_out
+                   ? salience_out
+                   : (float*)((char*)workspace + align256((size_t)F * H * N * sizeof(float)));
+  return hip_status(sv::launch_summary_salience(vis_q, vis_k, F, H, N, D, S, sc, keep, colh, sal,
+                                                idx_out, (hipStream_t)stream),
+                    fn);
+}

@@ -1,0 +1,147 @@
+// Summary-token salience for prefill pruning: SparseVILA velog summary,
+// Sec. 3.1, salience table (CLIP: the attention through which each token
+// feeds the one summary token; RADIO: that attention averaged over several
+// summary tokens).  The summary tokens are the first S tokens of a frame;
+// their softmax rows over all N tokens are averaged over the summary tokens
+// and the heads.
+//
+// summary_cols_kernel: one workgroup per (frame, head).  It holds the S
+// summary queries (fp32, pre-scaled into base 2) and the S x N logits in
+// LDS; each thread scores whole key rows (16-byte loads of one contiguous
+// row), each wave then reduces whole logit rows (max, then the sum of
+// exponentials), and each thread finally sums its columns' probabilities
+// over the summary rows.  The per-head column values go to a workspace and
+// summary_mean_kernel averages them over the heads in a fixed order, so the
+// result does not depend on scheduling.  The keys are read once: the work is
+// HBM-bound (about S*2 flops per key byte).
+#include "summary.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kSumThreads = 256;
+constexpr int kSumCols = kSummaryMaxN / kSumThreads;  // columns per thread
+constexpr int kSumMaxChunks = 16;                      // 16-byte chunks of a key row (D <= 128)
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__global__ __launch_bounds__(kSumThreads) void summary_cols_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int D, int S,
+    float qscale, float* __restrict__ colh) {
+  extern __shared__ __align__(16) float sm[];
+  float* z = sm;                          // [S][N] logits (base 2)
+  float* qf = z + S * N;                  // [S][D] scaled queries
+  float* rmax = qf + S * D;               // [S]
+  float* rinv = rmax + kSummaryMaxS;      // [S]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const size_t item = blockIdx.x;         // f * H + h
+  const uint16_t* qh = q + item * (size_t)N * D;
+  const uint16_t* kh = k + item * (size_t)N * D;
+
+  for (int e = tid; e < S * D; e += kSumThreads) qf[e] = bf16_lo(qh[e]) * qscale;
+  __syncthreads();
+
+  const int D8 = D / 8;
+  for (int j = tid; j < N; j += kSumThreads) {
+    float acc[kSummaryMaxS];
+#pragma unroll
+    for (int s = 0; s < kSummaryMaxS; ++s) acc[s] = 0.f;
+    // The whole key row's loads go out before any arithmetic.
+    const uint4* kr = reinterpret_cast<const uint4*>(kh + (size_t)j * D);
+    uint4 kw[kSumMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kSumMaxChunks; ++c)
+      if (c < D8) kw[c] = kr[c];
+#pragma unroll
+    for (int c = 0; c < kSumMaxChunks; ++c) {
+      if (c < D8) {
+        const uint4 w = kw[c];
+        const float kv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        for (int s = 0; s < S; ++s) {
+          const float* qs = qf + s * D + c * 8;
+          float a = acc[s];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = fmaf(qs[e], kv[e], a);
+          acc[s] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kSummaryMaxS; ++s)
+      if (s < S) z[s * N + j] = acc[s];
+  }
+  __syncthreads();
+
+  for (int s = wave; s < S; s += kSumThreads / kWave) {
+    const float* zs = z + s * N;
+    float m = -INFINITY;
+    for (int j = lane; j < N; j += kWave) m = fmaxf(m, zs[j]);
+    m = wave_max_f(m);
+    float l = 0.f;
+    for (int j = lane; j < N; j += kWave) l += exp2f(zs[j] - m);
+    l = wave_sum_f(l);
+    if (lane == 0) {
+      rmax[s] = m;
+      rinv[s] = 1.f / ((float)S * l);
+    }
+  }
+  __syncthreads();
+
+  float* out = colh + item * (size_t)N;
+#pragma unroll
+  for (int i = 0; i < kSumCols; ++i) {
+    const int j = tid + i * kSumThreads;
+    if (j < N) {
+      float a = 0.f;
+      for (int s = 0; s < S; ++s) a += exp2f(z[s * N + j] - rmax[s]) * rinv[s];
+      out[j] = a;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSumThreads) void summary_mean_kernel(const float* __restrict__ colh,
+                                                                   int H, int N, float inv_h,
+                                                                   float* __restrict__ sal) {
+  const int f = blockIdx.y;
+  const int j = blockIdx.x * kSumThreads + threadIdx.x;
+  if (j >= N) return;
+  const float* c = colh + (size_t)f * H * N + j;
+  float a = 0.f;
+  for (int h = 0; h < H; ++h) a += c[(size_t)h * N];
+  sal[(size_t)f * N + j] = a * inv_h;
+}
+
+}  // namespace
+
+hipError_t launch_summary_salience(const void* q, const void* k, int F, int H, int N, int D, int S,
+                                   float scale, int keep, float* colh_ws, float* sal,
+                                   int32_t* idx_out, hipStream_t stream) {
+  const size_t lds = ((size_t)S * N + (size_t)S * D + 2 * kSummaryMaxS) * sizeof(float);
+  hipLaunchKernelGGL(summary_cols_kernel, dim3((unsigned)((int64_t)F * H)), dim3(kSumThreads), lds,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, N, D, S,
+                     scale * 1.4426950408889634f, colh_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(summary_mean_kernel, dim3((N + kSumThreads - 1) / kSumThreads, F),
+                     dim3(kSumThreads), 0, stream, colh_ws, H, N, 1.0f / (float)H, sal);
+  e = hipGetLastError();
+  if (e != hipSuccess || keep <= 0) return e;
+  return launch_topk_rows(sal, F, N, N, keep, idx_out, stream);
+}
+
+}  // namespace sv
