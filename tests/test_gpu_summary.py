@@ -36,6 +36,14 @@ CASES = [
     ("max_logits_s16", 2, 4, 768, 128, 16, 100),
     ("max_n_4096", 1, 2, 4096, 72, 3, 1000),
     ("ragged_d8", 4, 3, 37, 8, 2, 5),
+    ("d16_s5", 2, 3, 301, 16, 5, 77),
+    ("d32_s2", 2, 5, 1000, 32, 2, 499),
+    ("d96_row_per_lane", 2, 4, 333, 96, 3, 100),
+    ("s1_d8", 2, 3, 257, 8, 1, 40),
+    ("s1_d16", 2, 3, 300, 16, 1, 30),
+    ("s1_d32", 2, 3, 1001, 32, 1, 500),
+    ("s1_d128", 2, 3, 4096, 128, 1, 2048),
+    ("s1_d72_row_per_lane", 2, 3, 729, 72, 1, 364),
     ("n_one", 3, 2, 1, 64, 1, 1),
     ("keep_zero", 2, 2, 50, 64, 1, 0),
 ]

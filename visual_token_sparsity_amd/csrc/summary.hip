@@ -39,6 +39,44 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// Logits of every key row when D/8 = G is a power of two (used for S = 1, where
+// it measured faster; with four summary rows the per-row reductions cost more
+// than the coalescing gains): G consecutive lanes
+// share a key row, one 16-byte chunk each, so every wave load is one
+// contiguous 1 KB run; a shuffle reduction over the G lanes completes each
+// dot product.  U chunks per lane are in flight per pass.
+template <int G>
+__device__ __forceinline__ void score_grouped(const uint16_t* __restrict__ kh, const float* qf,
+                                              float* z, int N, int D, int S, int tid) {
+  constexpr int U = 4;
+  const uint4* kc = reinterpret_cast<const uint4*>(kh);
+  const int total = N * G;               // 16-byte chunks of the frame-head's keys
+  const int c = tid % G;                 // this lane's chunk within a row (fixed)
+  for (int base = 0; base < total; base += kSumThreads * U) {   // uniform trip count
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = base + u * kSumThreads + tid;
+      w[u] = e < total ? kc[e] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = base + u * kSumThreads + tid;
+      const float kv[8] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y),
+                           bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+      for (int s = 0; s < S; ++s) {
+        const float* qs = qf + s * D + c * 8;
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p = fmaf(qs[i], kv[i], p);
+#pragma unroll
+        for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
+        if (c == 0 && e < total) z[s * N + e / G] = p;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kSumThreads) void summary_cols_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int N, int D, int S,
     float qscale, float* __restrict__ colh) {
@@ -55,8 +93,20 @@ __global__ __launch_bounds__(kSumThreads) void summary_cols_kernel(
   for (int e = tid; e < S * D; e += kSumThreads) qf[e] = bf16_lo(qh[e]) * qscale;
   __syncthreads();
 
+  // One summary row (CLIP): lane groups per key row, coalesced.  Several
+  // rows: a key row per lane, whose loads serve all S dot products without
+  // a reduction per row.
   const int D8 = D / 8;
-  for (int j = tid; j < N; j += kSumThreads) {
+  const bool grouped = S == 1 && (D8 == 1 || D8 == 2 || D8 == 4 || D8 == 8 || D8 == 16);
+  if (grouped) switch (D8) {
+    case 1: score_grouped<1>(kh, qf, z, N, D, S, tid); break;
+    case 2: score_grouped<2>(kh, qf, z, N, D, S, tid); break;
+    case 4: score_grouped<4>(kh, qf, z, N, D, S, tid); break;
+    case 8: score_grouped<8>(kh, qf, z, N, D, S, tid); break;
+    case 16: score_grouped<16>(kh, qf, z, N, D, S, tid); break;
+    default: break;
+  }
+  for (int j = grouped ? N : tid; j < N; j += kSumThreads) {   // otherwise: a row per lane
     float acc[kSummaryMaxS];
 #pragma unroll
     for (int s = 0; s < kSummaryMaxS; ++s) acc[s] = 0.f;
