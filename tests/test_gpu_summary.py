@@ -91,3 +91,24 @@ def test_summary_explicit_scale_workspace_reuse_and_rows_beyond_s_unread():
     assert torch.equal(a, b) and torch.equal(ia, ib)
     ok, rel, sm = accept.check_salience(a.cpu().numpy(), oracle.summary_salience(Q, K, S, scale=0.3))
     assert ok, (rel, sm)
+
+
+@pytest.mark.parametrize("name,S", [("clip_l14_336_256f", 1), ("radio_1028_64f", 4)])
+def test_summary_salience_full_bench_shapes_sampled(name, S):
+    """The bench workloads at full size: sampled frames against the oracle, and
+    properties of every frame (sums to 1, kept indices ascending and in range)."""
+    sw = synthetic.SALIENCE[name]
+    _say("summary full size", name, sw.F, sw.H, sw.N, sw.D, S, sw.keep)
+    Q, K = synthetic.make_salience(sw, 0, device=DEV, gen_device="cuda")
+    sal, idx = sv.summary_salience_prune(Q, K, S, sw.keep)
+    torch.cuda.synchronize()
+    s_all = sal.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(s_all.sum(axis=1) - 1.0) < 1e-5)
+    ix = idx.cpu().numpy()
+    assert np.all(np.diff(ix, axis=1) > 0) and ix.min() >= 0 and ix.max() < sw.N
+    for f in (0, sw.F // 3, sw.F - 1):
+        ref = oracle.summary_salience(Q[f:f + 1], K[f:f + 1], S)
+        ok, rel, sm = accept.check_salience(s_all[f:f + 1], ref)
+        assert ok, (f, rel, sm)
+        ok, _, msgs = accept.check_index_sets(ix[f:f + 1], ref, sw.keep)
+        assert ok, (f, msgs)
