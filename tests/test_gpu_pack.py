@@ -49,6 +49,8 @@ CASES = [
     # name, B, N, Hkv, D, k, dtype
     ("llava_full_bf16", 8, 1440, 32, 128, 360, torch.bfloat16),
     ("qwen2_gqa_bf16", 2, 3001, 4, 128, 333, torch.bfloat16),
+    ("qwen2_video_full_bf16", 1, 25088, 4, 128, 2048, torch.bfloat16),
+    ("multiturn_scaled_bf16", 2, 8192, 32, 128, 256, torch.bfloat16),
     ("ragged_fp32", 3, 77, 2, 64, 33, torch.float32),
     ("tiny_rows_bf16", 5, 9, 1, 8, 7, torch.bfloat16),
     ("long_rows_fp32", 2, 50, 80, 128, 17, torch.float32),   # rows of 40 KB: sliced units
