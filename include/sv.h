@@ -14,9 +14,9 @@
  *    library never allocates, frees or writes its inputs; outputs and the
  *    caller-provided workspace are the only memory it writes.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream).  Nothing synchronises; results are valid once the stream has
- *    executed the enqueued work.  Device-side faults surface at the caller's
- *    next synchronisation.
+ *    stream).  Nothing synchronises (except sv_workspace_status); results
+ *    are valid once the stream has executed the enqueued work.  Device-side
+ *    faults surface at the caller's next synchronisation.
  *  - Arguments are validated on the host before anything is enqueued.  A
  *    non-OK status means nothing was launched (except SV_EHIP, which reports
  *    a failed launch); sv_last_error() then returns a thread-local message.
@@ -59,6 +59,42 @@ int sv_version(void);
 const char* sv_last_error(void);
 
 /* ------------------------------------------------------------------------
+ * Bounded in-kernel waits
+ *
+ * sv_retrieve (rows of more than 2048 tokens) and sv_retrieve_attend run
+ * work items that wait on other workgroups of the same launch (a select on
+ * the scan items, the attention items on the select).  The hardware
+ * dispatches each XCD's share of a 1-D grid in increasing workgroup order
+ * and every item waits only on items of lower index, so every wait ends;
+ * each is still bounded, by a number of polls.  A wait that reaches the
+ * bound gives up: the item carries on with what it read (memory-safe, but
+ * the launch's indices and outputs are then invalid) and ORs a bit into the
+ * workspace's STATUS WORD, the first 32-bit word of the workspace (the
+ * workspaces of these two calls begin with a 256-byte status line that the
+ * kernels never clear):
+ *     1 scores never complete (select)      2 indices never complete (attention)
+ *     4 scan items never all counted        8 candidate items never all counted
+ *    16 threshold never published           (4, 8, 16: rows over 2048 tokens)
+ * After a give-up the workspace's other control words may be left non-zero:
+ * zero the whole workspace before its next use.
+ *
+ * sv_workspace_status: enqueues a copy of the status word on `stream`, WAITS
+ * for the stream (the only call of this library that synchronises) and
+ * returns SV_OK if the word is zero, SV_EHIP (with the bits in
+ * sv_last_error()) if a wait has given up since the workspace was zeroed.
+ * Errors: SV_EINVAL (NULL workspace), SV_EHIP (copy or sync failed).
+ *
+ * sv_set_wait_limit: sets the bound, in polls, for launches enqueued after
+ * it in this process (0 restores the default, 2^24 polls, seconds of
+ * polling) and returns the previous bound.  A small bound makes waits give
+ * up early; this is meant for testing the failure path, where every kernel
+ * still runs to completion.
+ * ---------------------------------------------------------------------- */
+sv_status sv_workspace_status(const void* workspace, void* stream);
+
+uint32_t sv_set_wait_limit(uint32_t polls);
+
+/* ------------------------------------------------------------------------
  * Query-aware retrieval (decode stage)
  *
  * SparseVILA velog summary, Sec. 3.2 "Query-Aware Token Selection": the
@@ -81,8 +117,9 @@ const char* sv_last_error(void);
  *  idx_out    [B][k] int32, ascending, distinct, each in [0, N).
  *  scores_out optional [B][N] fp32 scores s (NULL to skip).
  *  workspace  at least sv_retrieve_workspace(B, N, k) bytes, 256-byte
- *             aligned, ZERO-FILLED before its first use.  It holds the
- *             scores and one completion counter per sequence and, for rows
+ *             aligned, ZERO-FILLED before its first use.  It holds the status
+ *             line (see sv_workspace_status), the scores and one completion
+ *             counter per sequence and, for rows
  *             of more than 2048 tokens, the histograms, counters and
  *             candidate lists of the parallel select; every call returns
  *             the counters and histograms to zero, so the same workspace can
@@ -172,8 +209,9 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq,
  *  out        [B][Hq][D] fp32 attention output.
  *  workspace  at least sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax)
  *             bytes, 256-byte aligned, ZERO-FILLED before its first use.  It
- *             holds the scores, the split partials and a control block
- *             (completion counters, per-sequence ready flags); every call
+ *             holds the status line (see sv_workspace_status), the scores,
+ *             the split partials and a control block (completion counters,
+ *             per-sequence ready flags); every call
  *             leaves it ready for the next call with the same B, N, Hq, Hkv,
  *             D, k and Tmax, so it can be reused as is and the call captured
  *             in a HIP graph.  For other sizes, zero it again (or use

@@ -41,6 +41,26 @@ def test_version_and_empty_error():
     assert isinstance(lib.sv_last_error(), bytes)
 
 
+def test_wait_limit_and_status_query_host_side():
+    """The wait bound is a host-side setting (no launch); the status query
+    rejects a NULL workspace before touching the device."""
+    lib = sv.load()
+    default = sv.set_wait_limit(5)
+    assert default == 1 << 24
+    assert sv.set_wait_limit(0) == 5          # 0 restores the default
+    assert sv.set_wait_limit(0) == 1 << 24
+    assert lib.sv_workspace_status(None, None) == 1
+    assert b"NULL" in lib.sv_last_error()
+
+
+def test_waiting_workspaces_begin_with_a_status_line():
+    # sv_retrieve and sv_retrieve_attend reserve 256 bytes ahead of their
+    # scores; the smallest request still holds the status line
+    assert sv.retrieve_workspace_bytes(0, 0, 0) == 256
+    assert sv.retrieve_workspace_bytes(1, 1, 1) >= 256 + 256
+    assert sv.retrieve_attend_workspace_bytes(0, 1, 1, 64, 1, 1, 0) == 256
+
+
 def test_workspace_sizes():
     assert sv.retrieve_workspace_bytes(8, 1440, 360) >= 8 * 1440 * 4
     assert sv.retrieve_workspace_bytes(8, 1440, 360) % 256 == 0

@@ -352,3 +352,47 @@ def test_multiturn_rounds_reuse_the_visual_cache():
             assert ok, (r, t, err)
     for a_, n in zip(before, ("k_vis", "v_vis", "k_txt", "v_txt")):
         assert torch.equal(a_, g[n]), n
+
+
+@pytest.mark.parametrize("wl,ov", [("llava_next_7b", dict(B=4)), ("qwen2_7b_video", {})],
+                         ids=["short_rows", "long_rows"])
+def test_wait_give_up_is_reported_and_every_kernel_finishes(wl, ov):
+    """The host lowers the bound of the in-kernel waits to one poll, so waits give
+    up (a select before its scores are complete, attention items before their
+    indices, long-row items before their counters): every kernel still runs to
+    completion, and the workspace's status word reports it.  With the default
+    bound and a fresh workspace, the same layer matches the oracle and reports
+    nothing."""
+    w = synthetic.scaled_decode(synthetic.DECODE[wl], **ov)
+    _say("wait give-up", wl, w)
+    d = synthetic.make_decode_layer(w, seed=21)
+    g = _to(d)
+    nbytes = sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax)
+    reported = 0
+    prev = sv.set_wait_limit(1)
+    try:
+        for _ in range(3):
+            ws = sv.new_workspace(nbytes, DEV)
+            sv.retrieve_attend(g["q"], g["k_vis"], g["v_vis"], w.k, g["k_txt"], g["v_txt"],
+                               g["txt_len"], workspace=ws)
+            torch.cuda.synchronize()        # every kernel has finished
+            try:
+                sv.workspace_status(ws)
+            except sv.SvError as e:
+                assert e.status == 4 and "gave up" in str(e)
+                reported += 1
+    finally:
+        sv.set_wait_limit(prev)
+    assert reported > 0
+    ws = sv.new_workspace(nbytes, DEV)
+    out, idx = sv.retrieve_attend(g["q"], g["k_vis"], g["v_vis"], w.k, g["k_txt"], g["v_txt"],
+                                  g["txt_len"], workspace=ws)
+    torch.cuda.synchronize()
+    sv.workspace_status(ws)
+    s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])
+    ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), s_ref, w.k)
+    assert ok, msgs[:3]
+    ref = oracle.sparse_decode_attn(d["q"], d["k_vis"], d["v_vis"], idx.cpu().numpy(), d["k_txt"],
+                                    d["v_txt"], d["txt_len"])
+    ok, err = accept.check_attention(out.cpu().numpy(), ref)
+    assert ok, err

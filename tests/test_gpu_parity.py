@@ -355,12 +355,14 @@ def test_workspace_reuse_leaves_counters_zero():
     torch.cuda.synchronize()
     for idx, out in outs[1:]:
         assert torch.equal(idx, outs[0][0]) and torch.equal(out, outs[0][1])
-    # counters (one 128-byte line each) live after the scores / partials, 256-byte aligned;
-    # for these long rows the parallel select's histograms and lists follow them
-    n_scores = ((w.B * w.N * 4 + 255) // 256) * 256
+    # counters (one 128-byte line each) live after the 256-byte status line and
+    # the scores / partials, 256-byte aligned; for these long rows the parallel
+    # select's histograms and lists follow them
+    n_scores = 256 + ((w.B * w.N * 4 + 255) // 256) * 256
     n_ctr = ((w.B * 128 + 255) // 256) * 256
     assert ws_r.numel() - n_scores >= n_ctr
     assert torch.count_nonzero(ws_r[n_scores:n_scores + n_ctr]) == 0
+    assert torch.count_nonzero(ws_r[:256]) == 0        # no wait gave up
     tail = ws_a[-((w.B * w.Hkv * 128 + 255) // 256) * 256:]
     assert torch.count_nonzero(tail) == 0
     s_ref = oracle.retrieval_scores(d["q"], d["k_vis"])

@@ -26,7 +26,8 @@ __all__ = [
     "sparse_decode_attn", "sparse_decode_attn_workspace_bytes", "salience_prune",
     "salience_prune_workspace_bytes", "new_workspace", "retrieve_attend",
     "retrieve_attend_workspace_bytes", "pack_selected", "summary_salience_prune",
-    "summary_salience_prune_workspace_bytes", "SV_F32", "SV_BF16",
+    "summary_salience_prune_workspace_bytes", "workspace_status", "set_wait_limit",
+    "SV_F32", "SV_BF16",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -86,6 +87,10 @@ def load() -> ctypes.CDLL:
     lib.sv_summary_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_i,
                                               c_p, c_p, c_p, c_sz, c_p]
     lib.sv_summary_salience_prune.restype = c_i
+    lib.sv_workspace_status.argtypes = [c_p, c_p]
+    lib.sv_workspace_status.restype = c_i
+    lib.sv_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.sv_set_wait_limit.restype = ctypes.c_uint32
     _LIB = lib
     return lib
 
@@ -146,6 +151,20 @@ def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
 def new_workspace(nbytes: int, device) -> torch.Tensor:
     """A zero-filled workspace of ``nbytes`` bytes, reusable across calls."""
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def workspace_status(workspace: torch.Tensor) -> None:
+    """Raise SvError if a bounded in-kernel wait of a call on this workspace
+    (retrieve on rows over 2048 tokens, retrieve_attend) gave up since it was
+    zeroed.  Waits for the current stream."""
+    dev = _on_gpu(workspace)
+    _check(load().sv_workspace_status(ctypes.c_void_p(workspace.data_ptr()), _stream(dev)))
+
+
+def set_wait_limit(polls: int) -> int:
+    """Bound of the in-kernel waits, in polls, for later launches (0: the
+    default); returns the previous bound.  For testing the give-up path."""
+    return int(load().sv_set_wait_limit(polls))
 
 
 def retrieve_workspace_bytes(B: int, N: int, k: int) -> int:

@@ -40,6 +40,13 @@ int vec_elems(sv_dtype dt) { return dt == SV_BF16 ? 8 : 4; }
 
 bool dtype_ok(sv_dtype dt) { return dt == SV_BF16 || dt == SV_F32; }
 
+// Polls before an in-kernel wait gives up (sv_set_wait_limit).
+std::atomic<uint32_t> g_wait_limit{sv::kSpinLimit};
+
+// Workspaces whose kernels wait on each other start with one 256-byte status
+// line; its first word collects the give-up bits of those waits.
+constexpr size_t kStatusBytes = 256;
+
 // The kernels address one sequence's cache slice (rows 0..n-1 at `tstride`
 // elements apart, each `row` elements long) with 32-bit byte offsets.
 bool extent_ok(int64_t n, int64_t tstride, int64_t row, sv_dtype dt) {
@@ -71,13 +78,35 @@ int device_cu_count() {
 
 extern "C" {
 
-int sv_version(void) { return 110; }
+int sv_version(void) { return 120; }
 
 const char* sv_last_error(void) { return g_err.c_str(); }
 
+uint32_t sv_set_wait_limit(uint32_t polls) {
+  return g_wait_limit.exchange(polls ? polls : sv::kSpinLimit);
+}
+
+sv_status sv_workspace_status(const void* workspace, void* stream) {
+  if (!workspace) return fail(SV_EINVAL, "sv_workspace_status: NULL workspace");
+  uint32_t word = 0;
+  hipStream_t st = (hipStream_t)stream;
+  sv_status s = hip_status(hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st),
+                           "sv_workspace_status copy");
+  if (s != SV_OK) return s;
+  s = hip_status(hipStreamSynchronize(st), "sv_workspace_status sync");
+  if (s != SV_OK) return s;
+  if (word == 0) return SV_OK;
+  return fail(SV_EHIP,
+              "sv_workspace_status: an in-kernel wait gave up (bits 0x%x: 1 scores, 2 indices, "
+              "4 scan count, 8 candidate count, 16 threshold); outputs of the calls on this "
+              "workspace since it was zeroed are invalid: zero it before reuse",
+              word);
+}
+
 // ---------------------------------------------------------------- retrieval
-// Workspace of sv_retrieve: [scores B*N fp32][counters B lines] and, for rows
-// longer than the single-workgroup select, the long-row select workspace.
+// Workspace of sv_retrieve: [status line][scores B*N fp32][counters B lines]
+// and, for rows longer than the single-workgroup select, the long-row select
+// workspace.
 static size_t retrieve_scores_bytes(int B, int N) { return align256((size_t)B * (size_t)N * sizeof(float)); }
 
 // Control words: one 128-byte line each.
@@ -85,8 +114,9 @@ static size_t ctr_bytes(size_t n) { return align256(n * sv::kCtrStride * sizeof(
 
 size_t sv_retrieve_workspace(int B, int N, int k) {
   (void)k;
-  if (B < 1 || N < 1) return 256;
-  return retrieve_scores_bytes(B, N) + ctr_bytes((size_t)B) + sv::long_select_bytes(B, N);
+  if (B < 1 || N < 1) return kStatusBytes;
+  return kStatusBytes + retrieve_scores_bytes(B, N) + ctr_bytes((size_t)B) +
+         sv::long_select_bytes(B, N);
 }
 
 sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, int64_t k_bstride,
@@ -116,8 +146,10 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
   if (workspace_bytes < sv_retrieve_workspace(B, N, k))
     return fail(SV_EWORKSPACE, "sv_retrieve: workspace %zu < %zu bytes", workspace_bytes,
                 sv_retrieve_workspace(B, N, k));
-  float* scores = scores_out ? scores_out : (float*)workspace;
-  uint32_t* counters = (uint32_t*)((char*)workspace + retrieve_scores_bytes(B, N));
+  uint32_t* status = (uint32_t*)workspace;
+  char* ws = (char*)workspace + kStatusBytes;
+  float* scores = scores_out ? scores_out : (float*)ws;
+  uint32_t* counters = (uint32_t*)(ws + retrieve_scores_bytes(B, N));
   if (k > 0 && sv::long_select_bytes(B, N) > 0 && Hq / Hkv <= 8) {
     // Long rows: the scan and the parallel select of the one-launch layer
     // (every pass over a row split into 2048-score chunks), no attention.
@@ -137,11 +169,13 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
     f.k = k;
     f.scale = 1.0f;
     f.idx = idx_out;
-    f.scores_ws = (float*)workspace;
+    f.scores_ws = (float*)ws;
     f.scores_out = scores_out;
     f.seq_ctr = counters;
     f.long_ws = (char*)counters + ctr_bytes((size_t)B);
     f.retrieve_only = true;
+    f.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+    f.status = status;
     return hip_status(sv::launch_fused(f, (hipStream_t)stream), "sv_retrieve");
   }
   return hip_status(sv::launch_retrieve(q, B, Tq, Hq, k_vis, k_bstride, k_tstride, N, Hkv, D,
@@ -241,7 +275,7 @@ sv_status sv_pack_selected(const void* k_vis, const void* v_vis, int64_t vis_bst
 
 // ---------------------------------------------------------------- fused layer
 // Workspace of sv_retrieve_attend:
-//   [scores B*N][partials][control: seq B | ready B | vis_done B | comb B*Hkv]
+//   [status line][scores B*N][partials][control: seq B | ready B | vis_done B | comb B*Hkv]
 //   [encoded index copy B*k]
 //   [long-row select: control lines and histograms | candidates, chunk offsets],
 // every control word on its own 128-byte line.  The score words, control
@@ -252,8 +286,8 @@ static size_t fused_ctl_bytes(int B, int Hkv) { return ctr_bytes((size_t)B * (3 
 static size_t fused_enc_bytes(int B, int k) { return align256((size_t)B * k * sizeof(uint32_t)); }
 
 size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return 256;
-  return retrieve_scores_bytes(B, N) +
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return kStatusBytes;
+  return kStatusBytes + retrieve_scores_bytes(B, N) +
          attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true) +
          fused_ctl_bytes(B, Hkv) + fused_enc_bytes(B, k) + sv::long_select_bytes(B, N);
 }
@@ -295,6 +329,9 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
 
   char* ws = (char*)workspace;
   sv::FusedLaunch f{};
+  f.status = (uint32_t*)ws;
+  f.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+  ws += kStatusBytes;
   f.q = q;
   f.B = B;
   f.Hq = Hq;

@@ -191,6 +191,10 @@ constexpr int kCtrStride = 32;  // uint32 words
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 
+// Default bound of every in-kernel wait, in polls (a few seconds of polling;
+// every awaited item is dispatched before its waiter, so no wait comes near it).
+constexpr uint32_t kSpinLimit = 1u << 24;
+
 // Compute units of the current device.
 int device_cu_count();
 
@@ -264,6 +268,8 @@ struct FusedLaunch {
   bool retrieve_only;
   int rows_per_item;   // 0: default
   int epl;             // 0: default
+  uint32_t spin_limit; // polls before an in-kernel wait gives up (0: kSpinLimit)
+  uint32_t* status;    // sticky status word: give-up bits are ORed in (may be null)
 };
 hipError_t launch_fused(const FusedLaunch& f, hipStream_t stream);
 size_t long_select_bytes(int B, int N);  // 0 when rows take the single-workgroup select

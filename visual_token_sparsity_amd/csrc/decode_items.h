@@ -37,7 +37,22 @@ constexpr int kItemThreads = kItemWaves * kWave;
 constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment
 constexpr int kScanSegChunks = 512;
 constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
-constexpr uint32_t kSpinLimit = 1u << 24;  // bound of every in-kernel wait
+
+// Bits of the sticky status word (the first word of a workspace whose kernels
+// wait on each other): a bounded wait that gave up ORs in its bit and the item
+// carries on with what it read, so the outputs of that launch are invalid.
+enum : uint32_t {
+  kGiveUpScores = 1u,      // select item: score row never complete
+  kGiveUpIndices = 2u,     // visual attention item: selected indices never complete
+  kGiveUpScanCount = 4u,   // long-row candidate item: scan items never all counted
+  kGiveUpCandCount = 8u,   // long-row threshold item: candidate items never all counted
+  kGiveUpThreshold = 16u,  // long-row compaction item: threshold never published
+};
+
+__device__ __forceinline__ void report_giveup(uint32_t* status, uint32_t bit) {
+  if (status) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int kLsReps = 8;         // replicas of a long row's first-level key histogram
 constexpr int kLsBins = 2048;      // 11-bit key digits
 
@@ -67,6 +82,8 @@ struct ScanArgs {
   // Fused kernel: [B][k] the selected indices plus one (zero: not written
   // yet), which the attention items poll; zero again after the launch.
   uint32_t* idx_enc;
+  uint32_t spin_limit;       // polls before a wait gives up (>= 1)
+  uint32_t* status;          // sticky status word (give-up bits), may be null
 };
 
 // Chunks of qhat kept in LDS (zero past C).
@@ -312,7 +329,11 @@ __device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float
                  : 1u;
       missing |= w[i] == 0u;
     }
-    if (!__syncthreads_or(missing) || n + 1 >= kSpinLimit) break;
+    if (!__syncthreads_or(missing)) break;
+    if (n + 1 >= a.spin_limit) {
+      if (tid == 0) report_giveup(a.status, kGiveUpScores);
+      break;
+    }
     __builtin_amdgcn_s_sleep(2);
   }
   __builtin_amdgcn_s_setprio(3);
@@ -365,6 +386,8 @@ struct AttnArgs {
   uint32_t* ready;       // [B] (stride kCtrStride; fused kernel only)
   uint32_t* vis_done;    // [B] (stride kCtrStride) finished visual items (fused kernel only)
   const uint32_t* idx_enc;  // [B][k] selected indices plus one, polled (fused kernel only)
+  uint32_t spin_limit;      // polls before a wait gives up (>= 1)
+  uint32_t* status;         // sticky status word (give-up bits), may be null
 };
 
 template <typename T, int D>
@@ -469,7 +492,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
           tok[j] = e < n_ent ? (int)w - 1 : -1;  // -1: no entry
           missing |= e < n_ent && w == 0u;
         }
-        if (!__syncthreads_or(missing) || n + 1 >= kSpinLimit) break;
+        if (!__syncthreads_or(missing)) break;
+        if (n + 1 >= a.spin_limit) {
+          if (tid == 0) report_giveup(a.status, kGiveUpIndices);
+          break;
+        }
         __builtin_amdgcn_s_sleep(8);
       }
     } else {

@@ -65,6 +65,8 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.seq_ctr = f.seq_ctr;
   sa.ready = f.retrieve_only ? nullptr : f.ready;
   sa.idx_enc = f.retrieve_only ? nullptr : f.idx_enc;
+  sa.spin_limit = f.spin_limit > 0 ? f.spin_limit : kSpinLimit;
+  sa.status = f.status;
   LongSelArgs ls{};
   if (!sa.encode) {
     if (!f.long_ws) return hipErrorInvalidValue;
@@ -117,6 +119,8 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   aa.out = f.out;
   aa.ready = f.ready;
   aa.idx_enc = f.idx_enc;
+  aa.spin_limit = sa.spin_limit;
+  aa.status = f.status;
 
   FusedCtl ctl{};
   ctl.vis_done = f.vis_done;

@@ -67,14 +67,17 @@ __device__ __forceinline__ uint32_t digit1(uint32_t key) { return key >> 21; }
 __device__ __forceinline__ uint32_t digit2(uint32_t key) { return (key >> 10) & (kLsBins - 1); }
 
 // Poll a counter line until it reaches `target` (thread 0 of the
-// workgroup; bounded).
-__device__ __forceinline__ uint32_t poll_until(const uint32_t* p, uint32_t target) {
+// workgroup), at most `limit` times; a wait that gives up ORs `bit` into the
+// status word.  Returns the last value read.
+__device__ __forceinline__ uint32_t poll_until(const uint32_t* p, uint32_t target, uint32_t limit,
+                                               uint32_t* status, uint32_t bit) {
   uint32_t v = 0;
-  for (uint32_t n = 0; n < kSpinLimit; ++n) {
+  for (uint32_t n = 0; n < limit; ++n) {
     v = load_flag(p);
-    if (v >= target) break;
+    if (v >= target) return v;
     __builtin_amdgcn_s_sleep(4);
   }
+  report_giveup(status, bit);
   return v;
 }
 
@@ -113,7 +116,9 @@ __device__ __forceinline__ void cand_item(const ScanArgs& a, const LongSelArgs& 
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   for (int i = tid; i < kLsBins; i += kItemThreads) sm.h2[i] = 0;
-  if (tid == 0) poll_until(&a.seq_ctr[b * kCtrStride], (uint32_t)a.items_per_seq);
+  if (tid == 0)
+    poll_until(&a.seq_ctr[b * kCtrStride], (uint32_t)a.items_per_seq, a.spin_limit, a.status,
+               kGiveUpScanCount);
   __syncthreads();
 
   uint32_t key[kSelKpt];
@@ -218,7 +223,7 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
   const int wave = tid / kWave;
   const int P = l.P;
   if (tid == 0) {
-    poll_until(ls_line(l, b, kLsCandDone), (uint32_t)P);
+    poll_until(ls_line(l, b, kLsCandDone), (uint32_t)P, a.spin_limit, a.status, kGiveUpCandCount);
     sm.nfin = 0;
   }
   __syncthreads();
@@ -360,7 +365,8 @@ __device__ __forceinline__ void compact_item(const ScanArgs& a, const LongSelArg
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  if (tid == 0) sm.mode = poll_until(ls_line(l, b, kLsThrReady), 1u);
+  if (tid == 0)
+    sm.mode = poll_until(ls_line(l, b, kLsThrReady), 1u, a.spin_limit, a.status, kGiveUpThreshold);
   __syncthreads();
   if (sm.mode == 1u) {
     uint32_t key[kSelKpt];

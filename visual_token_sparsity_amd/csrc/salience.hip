@@ -920,12 +920,13 @@ __global__ __launch_bounds__(kRowWaves* kWave, 1) void salience_rows_kernel(
   }
 }
 
-// sal[f][j] = (1 / (H*N)) * sum_h colsum[f][h][j]
+// sal[f][j] = (1 / (H*N)) * sum_h colsum[f][h][j]; workgroup x covers
+// columns 256 (x % bpf) .. of frame x / bpf (a 1-D grid: any frame count).
 __global__ __launch_bounds__(256) void salience_mean_kernel(const float* __restrict__ colsum,
-                                                           int H, int N, float inv,
+                                                           int H, int N, int bpf, float inv,
                                                            float* __restrict__ sal) {
-  const int f = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int f = blockIdx.x / bpf;
+  const int j = (blockIdx.x % bpf) * blockDim.x + threadIdx.x;
   if (j >= N) return;
   const float* c = colsum + (int64_t)f * H * N + j;
   float s = 0.f;
@@ -1123,9 +1124,9 @@ hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, in
     }
   }
   if (e != hipSuccess) return e;
-  dim3 grid((N + 255) / 256, F);
-  hipLaunchKernelGGL(salience_mean_kernel, grid, dim3(256), 0, st, colsum_ws, H, N,
-                     1.0f / ((float)H * (float)N), sal);
+  const int bpf = (N + 255) / 256;
+  hipLaunchKernelGGL(salience_mean_kernel, dim3((unsigned)((int64_t)F * bpf)), dim3(256), 0, st,
+                     colsum_ws, H, N, bpf, 1.0f / ((float)H * (float)N), sal);
   return hipGetLastError();
 }
 

@@ -200,9 +200,13 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
       uint32_t* cand = sm.hist[1];  // [kSelMaxCand] keys, then [kSelMaxCand] indices
       for_each([&](int e, bool valid, uint32_t kk) {
         if (valid && bin_of(kk) == bstar) {
+          // cnt <= kSelMaxCand keys fall in bin bstar; the bound only guards
+          // against inconsistent inputs (a wait that gave up).
           const uint32_t slot = atomicAdd(&sm.ncand, 1u);
-          cand[slot] = kk;
-          cand[kSelMaxCand + slot] = (uint32_t)e;
+          if (slot < (uint32_t)kSelMaxCand) {
+            cand[slot] = kk;
+            cand[kSelMaxCand + slot] = (uint32_t)e;
+          }
         }
       });
       __syncthreads();
