@@ -82,7 +82,10 @@ const char* sv_last_error(void);
  * for the stream (the only call of this library that synchronises) and
  * returns SV_OK if the word is zero, SV_EHIP (with the bits in
  * sv_last_error()) if a wait has given up since the workspace was zeroed.
- * Errors: SV_EINVAL (NULL workspace), SV_EHIP (copy or sync failed).
+ * workspace == NULL reads the static scratch of the current device instead
+ * (sv_retrieve_attend_noalloc, which zeroes it at every call: the status of
+ * the last such call on the device).
+ * Errors: SV_EHIP (copy or sync failed).
  *
  * sv_set_wait_limit: sets the bound, in polls, for launches enqueued after
  * it in this process (0 restores the default, 2^24 polls, seconds of
@@ -234,6 +237,37 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq,
                              sv_dtype dtype, float scale,
                              int32_t* idx_out, float* scores_out, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * sv_retrieve_attend without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Computes exactly what sv_retrieve_attend computes (same kernel, same
+ * arguments and errors, minus the workspace).  Its workspace is a static
+ * device array of SV_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every device it runs on until the process ends; the call zeroes the part
+ * it needs on `stream` (a fill kernel, no memset node) before the layer's
+ * kernel.  Nothing is allocated.  All calls on one device share that array:
+ * two calls that overlap on one device (different streams, or host threads)
+ * race and both give undefined results; serialise them.
+ * Errors: as sv_retrieve_attend, and SV_EWORKSPACE when
+ * sv_retrieve_attend_workspace(...) of the sizes exceeds
+ * SV_NOALLOC_SCRATCH_BYTES (16 MiB: enough for 8 x 131072 visual tokens of
+ * 32 x 128 heads with k = 4096 and 256 text rows).
+ * ---------------------------------------------------------------------- */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+sv_status sv_retrieve_attend_noalloc(const void* q, int B, int Hq,
+                                     const void* k_vis, const void* v_vis,
+                                     int64_t vis_bstride, int64_t vis_tstride, int N,
+                                     int Hkv, int D, int k,
+                                     const void* k_txt, const void* v_txt,
+                                     int64_t txt_bstride, int64_t txt_tstride,
+                                     const int32_t* txt_len, int Tmax,
+                                     sv_dtype dtype, float scale,
+                                     int32_t* idx_out, float* scores_out, float* out,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------
  * Dense packing of the selected visual entries (decode stage, once per

@@ -42,15 +42,12 @@ def test_version_and_empty_error():
 
 
 def test_wait_limit_and_status_query_host_side():
-    """The wait bound is a host-side setting (no launch); the status query
-    rejects a NULL workspace before touching the device."""
+    """The wait bound is a host-side setting (no launch)."""
     lib = sv.load()
     default = sv.set_wait_limit(5)
     assert default == 1 << 24
     assert sv.set_wait_limit(0) == 5          # 0 restores the default
     assert sv.set_wait_limit(0) == 1 << 24
-    assert lib.sv_workspace_status(None, None) == 1
-    assert b"NULL" in lib.sv_last_error()
 
 
 def test_waiting_workspaces_begin_with_a_status_line():
@@ -233,3 +230,19 @@ def test_summary_salience_rejects(kw, status):
 def test_summary_salience_workspace_size():
     lib = sv.load()
     assert lib.sv_summary_salience_prune_workspace(2, 16, 577) >= (2 * 16 * 577 + 2 * 577) * 4
+
+
+def test_noalloc_rejects_sizes_beyond_the_static_scratch():
+    """Eight sequences of 131072 tokens at 32 x 128 heads fit the 16 MiB scratch;
+    sixteen do not: SV_EWORKSPACE before anything is launched."""
+    lib = sv.load()
+    lib.sv_retrieve_attend_noalloc.restype = ctypes.c_int
+    assert sv.retrieve_attend_workspace_bytes(8, 32, 32, 128, 131072, 4096, 256) <= 16 << 20
+    assert sv.retrieve_attend_workspace_bytes(16, 32, 32, 128, 131072, 4096, 256) > 16 << 20
+    p = ctypes.c_void_p(FAKE)
+    st = lib.sv_retrieve_attend_noalloc(p, 16, 32, p, p, ctypes.c_int64(131072 * 4096),
+                                        ctypes.c_int64(4096), 131072, 32, 128, 4096, p, p,
+                                        ctypes.c_int64(256 * 4096), ctypes.c_int64(4096), p, 256,
+                                        sv.SV_BF16, ctypes.c_float(0.0), p, None, p, None)
+    assert st == 3, lib.sv_last_error()
+    assert b"static scratch" in lib.sv_last_error()

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -76,6 +77,64 @@ int device_cu_count() {
 
 }  // namespace sv
 
+// ---------------------------------------------------------------- static scratch
+// Workspace of sv_retrieve_attend_noalloc: SV_NOALLOC_SCRATCH_BYTES per device,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in; only the address hipGetSymbolAddress returns (per device) is used.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Zero n16 16-byte words (a kernel rather than a memset node, so the call
+// can be captured in a HIP graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The device address of the current device's scratch (looked up on its
+// first use on that device, with the device current).
+sv_status scratch_ptr(void** out, const char* fn) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SV_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SV_EUNSUPPORTED, "%s: device %d beyond the %d supported", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || !p)
+      return fail(SV_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(g));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
+}  // namespace
+
+// The static scratch as the workspace of one call: at most
+// SV_NOALLOC_SCRATCH_BYTES, its first `need` bytes zeroed on the stream (the
+// control words, index copy and status line must start at zero; the array
+// keeps whatever the previous call left).
+static sv_status scratch_workspace(size_t need, hipStream_t st, void** ws, const char* fn) {
+  if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES)
+    return fail(SV_EWORKSPACE, "%s: needs %zu bytes of scratch, more than the %zu-byte static scratch",
+                fn, need, (size_t)SV_NOALLOC_SCRATCH_BYTES);
+  const sv_status s = scratch_ptr(ws, fn);
+  if (s != SV_OK) return s;
+  const size_t n16 = (need + 15) / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint4*)*ws, n16);
+  return hip_status(hipGetLastError(), fn);
+}
+
 extern "C" {
 
 int sv_version(void) { return 120; }
@@ -87,7 +146,13 @@ uint32_t sv_set_wait_limit(uint32_t polls) {
 }
 
 sv_status sv_workspace_status(const void* workspace, void* stream) {
-  if (!workspace) return fail(SV_EINVAL, "sv_workspace_status: NULL workspace");
+  if (!workspace) {
+    // The static scratch of the current device (sv_retrieve_attend_noalloc).
+    void* p = nullptr;
+    const sv_status s = scratch_ptr(&p, "sv_workspace_status");
+    if (s != SV_OK) return s;
+    workspace = p;
+  }
   uint32_t word = 0;
   hipStream_t st = (hipStream_t)stream;
   sv_status s = hip_status(hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st),
@@ -292,14 +357,21 @@ size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k,
          fused_ctl_bytes(B, Hkv) + fused_enc_bytes(B, k) + sv::long_select_bytes(B, N);
 }
 
-sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
-                             int64_t vis_bstride, int64_t vis_tstride, int N, int Hkv, int D,
-                             int k, const void* k_txt, const void* v_txt, int64_t txt_bstride,
-                             int64_t txt_tstride, const int32_t* txt_len, int Tmax,
-                             sv_dtype dtype, float scale, int32_t* idx_out, float* scores_out,
-                             float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "sv_retrieve_attend";
-  if (!q || !k_vis || !v_vis || !idx_out || !out || !workspace)
+}  // extern "C"
+
+// The no-allocation variant resolves its workspace (the static scratch) only
+// after every argument has been validated.
+static sv_status scratch_workspace(size_t need, hipStream_t st, void** ws, const char* fn);
+
+static sv_status retrieve_attend_impl(const char* fn, bool noalloc, const void* q, int B, int Hq,
+                                      const void* k_vis, const void* v_vis, int64_t vis_bstride,
+                                      int64_t vis_tstride, int N, int Hkv, int D, int k,
+                                      const void* k_txt, const void* v_txt, int64_t txt_bstride,
+                                      int64_t txt_tstride, const int32_t* txt_len, int Tmax,
+                                      sv_dtype dtype, float scale, int32_t* idx_out,
+                                      float* scores_out, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!q || !k_vis || !v_vis || !idx_out || !out || (!workspace && !noalloc))
     return fail(SV_EINVAL, "%s: NULL q, k_vis, v_vis, idx_out, out or workspace", fn);
   if (B < 1 || B > 65535 || Hq < 1 || Hkv < 1 || N < 1 || Tmax < 0)
     return fail(SV_EINVAL, "%s: bad sizes B=%d Hq=%d Hkv=%d N=%d Tmax=%d", fn, B, Hq, Hkv, N, Tmax);
@@ -324,8 +396,12 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
   if (!extent_ok(N, vis_tstride, R, dtype) || !extent_ok(Tmax, txt_tstride, R, dtype))
     return fail(SV_EUNSUPPORTED, "%s: one sequence's cache slice spans 2 GiB or more", fn);
   const size_t need = sv_retrieve_attend_workspace(B, Hq, Hkv, D, N, k, Tmax);
-  if (workspace_bytes < need)
+  if (noalloc) {
+    const sv_status st = scratch_workspace(need, (hipStream_t)stream, &workspace, fn);
+    if (st != SV_OK) return st;
+  } else if (workspace_bytes < need) {
     return fail(SV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  }
 
   char* ws = (char*)workspace;
   sv::FusedLaunch f{};
@@ -368,6 +444,39 @@ sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, co
   ws += fused_enc_bytes(B, k);
   f.long_ws = sv::long_select_bytes(B, N) ? ws : nullptr;
   return hip_status(sv::launch_fused(f, (hipStream_t)stream), fn);
+}
+
+extern "C" {
+
+sv_status sv_retrieve_attend(const void* q, int B, int Hq, const void* k_vis, const void* v_vis,
+                             int64_t vis_bstride, int64_t vis_tstride, int N, int Hkv, int D,
+                             int k, const void* k_txt, const void* v_txt, int64_t txt_bstride,
+                             int64_t txt_tstride, const int32_t* txt_len, int Tmax,
+                             sv_dtype dtype, float scale, int32_t* idx_out, float* scores_out,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return retrieve_attend_impl("sv_retrieve_attend", false, q, B, Hq, k_vis, v_vis, vis_bstride,
+                              vis_tstride, N, Hkv, D, k, k_txt, v_txt, txt_bstride, txt_tstride,
+                              txt_len, Tmax, dtype, scale, idx_out, scores_out, out, workspace,
+                              workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): sv_retrieve_attend_noalloc takes its workspace from a file-scope
+// device array instead of an argument.  Each device holds its own copy, at its
+// own address, found once per device with hipGetSymbolAddress; every call on
+// a device shares it.
+sv_status sv_retrieve_attend_noalloc(const void* q, int B, int Hq, const void* k_vis,
+                                     const void* v_vis, int64_t vis_bstride, int64_t vis_tstride,
+                                     int N, int Hkv, int D, int k, const void* k_txt,
+                                     const void* v_txt, int64_t txt_bstride, int64_t txt_tstride,
+                                     const int32_t* txt_len, int Tmax, sv_dtype dtype, float scale,
+                                     int32_t* idx_out, float* scores_out, float* out,
+                                     void* stream) {
+  return retrieve_attend_impl("sv_retrieve_attend_noalloc", true, q, B, Hq, k_vis, v_vis,
+                              vis_bstride, vis_tstride, N, Hkv, D, k, k_txt, v_txt, txt_bstride,
+                              txt_tstride, txt_len, Tmax, dtype, scale, idx_out, scores_out, out,
+                              nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------- salience
