@@ -1,4 +1,4 @@
-"""Throughput of the SparseVILA decode hot path on one MI355X.
+"""Throughput of the SparseVILA decode and prefill hot paths on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -6,7 +6,7 @@ A step is one decode step of the whole batch through every layer: for each
 layer, query-aware retrieval (relevance scan + top-k select) and sparse
 decode attention over the selected visual entries plus the text entries
 (split-K partials + combine), all in one launch per layer
-(sv_retrieve_attend).  The default workload is LLaVA-NeXT-7B shaped: 8
+(sv_retrieve_attend).  The headline workload is LLaVA-NeXT-7B shaped: 8
 sequences, 32 layers x 32 heads, head dim 128, bf16, 1440 retained visual
 tokens, k = 360, 256 text entries.  All caches are resident in HBM before
 timing starts (7.1 GB, far above the 256 MB Infinity Cache, so every step
@@ -16,10 +16,17 @@ replayed.
 Printed: one JSON line with steps/s (whole job), algorithmic HBM GB/s, the
 roofline of the dominant kernel (the one-launch decode layer, timed live
 with HIP events over the timed region on the stream it runs on), the same
-step through the two-call path (sv_retrieve + sv_sparse_decode_attn) for
-comparison, the prefill salience workload (256 frames x 729 tokens, 16
-heads, D = 72: tokens/s and MFMA utilisation), and the CPU oracle timed on a
-bounded sample of the same decode workload.
+step through the two-call path, and the CPU oracle timed on a bounded sample
+of the same workload.  The same line carries, each with its own roofline and
+oracle baseline:
+  workloads.image576_fp32     576-token fp32 image, one layer (64 rotating replicas)
+  workloads.qwen2_7b_video    Qwen2-7B GQA long video, batch 1, 28 layers, N = 25088
+  workloads.multiturn_128k    4 x 131072 visual tokens, the 3-round x 128-step schedule
+  salience                    SigLIP-shaped prefill salience, 256 frames x 729 tokens
+  summary_salience            CLIP (one summary token) and RADIO (four) shapes,
+                              rotating over >= 1 GB of encoder Q/K
+  packed                      per-question retrieval + dense packing, decode over packed rows
+  hbm_measured                1 GiB device copy and read: the bandwidth actually reachable
 """
 from __future__ import annotations
 
@@ -37,6 +44,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
+EXTRA_DECODE = ("image576_fp32", "qwen2_7b_video", "multiturn_128k")
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -51,13 +60,16 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pack", action="store_true")
     p.add_argument("--no-summary", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="time only the headline decode workload (no other decode workloads)")
     p.add_argument("--summary-only", action="store_true",
                    help="time only the summary-token salience calls (profiling runs); prints "
                         "their object")
     p.add_argument("--pack-only", action="store_true",
                    help="time only the per-question pack and the decode over packed rows "
                         "(profiling runs); prints its object")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="budget of each CPU oracle sample")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--profile-traffic", action="store_true",
                    help="no timing: run two one-launch decode steps and a 1 GiB device copy "
@@ -114,7 +126,7 @@ def committed_mfma_ops(workload, src_hash):
     return (t["mfma_mops_bf16_per_call"] + t["mfma_mops_f16_per_call"]) * t["flops_per_mop"]
 
 
-def committed_traffic(kernel_key, src_hash, launches_per_unit=1):
+def committed_traffic(kernel_key, src_hash):
     """Per-launch HBM bytes from the committed rocprofv3 counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -177,6 +189,25 @@ def cpu_info():
     return n, model
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def free(torch):
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -184,7 +215,6 @@ def main():
                           "n_gpus": a.gpus}), flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synthetic
@@ -196,38 +226,124 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.load()
+    stream = torch.cuda.Stream(device=dev)      # default priority
     if a.salience_only:
-        stream = torch.cuda.Stream(device=dev)  # default priority
         print(json.dumps({"salience": bench_salience(a, dev, stream)}), flush=True)
         return
     if a.summary_only:
-        stream = torch.cuda.Stream(device=dev)  # default priority
         print(json.dumps({"summary_salience": bench_summary(a, dev, stream)}), flush=True)
         return
     w = synthetic.DECODE[a.workload]
-    print(f"[bench] workload {w.name}: B={w.B} L={w.L} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} "
-          f"k={w.k} T={w.T}", file=sys.stderr, flush=True)
-
-    # ------------------------------------------------------------ inputs (resident in HBM)
-    layers = [synthetic.make_decode_layer(w, a.seed, layer=l, device=dev, gen_device="cuda")
-              for l in range(w.L)]
-    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in range(w.L)]
-    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(w.L)]
-    ws_f = sv.new_workspace(sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax), dev)
-    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
-    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
-    torch.cuda.synchronize()
     if a.pack_only:
-        stream = torch.cuda.Stream(device=dev)  # default priority
-        res = bench_packed(a, dev, stream, w, layers, ws_r, ws_a)
+        layers = make_layers(a, dev, w)
+        res = bench_packed(a, dev, stream, w, layers)
         if res is not None:
             print(json.dumps({"packed": res}), flush=True)
         return
+    if a.profile_traffic:
+        profile_traffic(a, dev, w)
+        return
+
+    # ------------------------------------------------------------ headline decode workload
+    layers = make_layers(a, dev, w)
+    head = bench_decode(a, dev, stream, w, layers, two_call=True)
+    dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    res = {
+        "metric": "decode steps/s (retrieval + sparse attention, all layers, whole batch)",
+        "value": head["value"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": head["timed_steps"],
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded Gaussian caches, 5% planted relevant tokens; no weights)",
+        "config": dict(head["config"], parallelism="none (1 GPU)"),
+    }
+    for key in ("hbm_gbs_algorithmic", "hbm_frac_algorithmic", "step_bytes_algorithmic",
+                "roofline", "two_call_path", "wall_s_timed"):
+        if key in head:
+            res[key] = head[key]
+
+    # ------------------------------------------------------------ per-question dense packing
+    if not a.no_pack and w.name != "multiturn_128k":
+        res["packed"] = bench_packed(a, dev, stream, w, layers)
+        res["packed"]["decode_speedup_vs_fused_step"] = round(
+            res["packed"]["decode"]["steps_per_s"] / res["value"], 3)
+
+    # ------------------------------------------------------------ CPU oracle, headline workload
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(a, w, layers)
+    del layers
+    free(torch)
+
+    # ------------------------------------------------------------ the other decode workloads
+    if not a.no_extra:
+        res["workloads"] = {}
+        for name in EXTRA_DECODE:
+            if name == w.name:
+                continue
+            wx = synthetic.DECODE[name]
+            lx = make_layers(a, dev, wx)
+            obj = bench_decode(a, dev, stream, wx, lx, two_call=False, full_schedule=True)
+            if not a.no_cpu_baseline:
+                obj["cpu_baseline"] = cpu_baseline_decode(a, wx, lx)
+            res["workloads"][name] = obj
+            del lx
+            free(torch)
+
+    # ------------------------------------------------------------ prefill salience
+    if not a.no_salience:
+        res["salience"] = bench_salience(a, dev, stream)
+        free(torch)
+    if not a.no_summary:
+        res["summary_salience"] = bench_summary(a, dev, stream)
+        free(torch)
+
+    res["hbm_measured"] = hbm_measured(dev, stream)
+    print(json.dumps(res), flush=True)
+
+
+def replicas(w):
+    """Independent input sets per timed unit: the one-layer fp32 image workload
+    fits the last-level cache, so 64 replicas (1.3 GB) rotate through HBM."""
+    return 64 if w.name == "image576_fp32" else w.L
+
+
+def make_layers(a, dev, w):
+    import synthetic
+    n = replicas(w)
+    say(f"workload {w.name}: B={w.B} L={w.L} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} k={w.k} "
+        f"T={w.T} ({n} input sets)")
+    return [synthetic.make_decode_layer(w, a.seed, layer=l, device=dev, gen_device="cuda")
+            for l in range(n)]
+
+
+def bench_decode(a, dev, stream, w, layers, two_call, full_schedule=False):
+    """Time decode steps of workload w over its resident layers.
+
+    One unit is a decode step through w.L layers; the fp32 image workload has
+    one layer and rotates over its replicas (each replica one step).  The
+    multi-turn workload times --steps steps of its round schedule, or the whole
+    schedule with full_schedule."""
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+    L = len(layers)
+    units_per_call = L // w.L                     # steps per pass over the input sets
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in range(L)]
+    out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
+    ws_f = sv.new_workspace(sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax), dev)
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
+    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
 
     # Multi-turn workload: conversation rounds of decode steps over one reused
     # visual cache.  Step i takes a fresh query and the text length of its
-    # place in the round schedule (partial eviction between rounds); the
-    # schedule repeats when more steps are timed than it holds.
+    # place in the round schedule (partial eviction between rounds).
     sched = None
     if w.name == "multiturn_128k":
         lens = [t for rnd in synthetic.multiturn_text_lengths() for t in rnd]
@@ -266,77 +382,59 @@ def main():
         return [int(d[n].view(torch.int16).sum(dtype=torch.int64).item())
                 for d in layers for n in ("k_vis", "v_vis")]
 
-    if a.profile_traffic:
-        # Counter passes: the fused decode layer as timed, and a plain copy of
-        # known size whose counters give the scale factor of the counters.
-        for _ in range(2):
-            step()
-        torch.cuda.synchronize()
-        nbytes = calibration_copy(torch, dev)
-        print(json.dumps({"profile_traffic": w.name, "layer_bytes": decode_bytes(w)[1],
-                          "copy_bytes": nbytes}), flush=True)
-        return
-
-    stream = torch.cuda.Stream(device=dev)      # default priority
+    calls = len(sched["lens"]) if (sched is not None and full_schedule) else a.steps
     sum_before = vis_checksum() if sched is not None else None
     with torch.cuda.stream(stream):
         for _ in range(max(1, a.warmup)):
             step()
-            step_two_call()
+            if two_call:
+                step_two_call()
         torch.cuda.synchronize()
         # The multi-turn schedule changes the query and text length every step:
         # eager launches (each step is one ~0.8 ms kernel).
         eager = a.no_graph or sched is not None
         g_step = None if eager else capture(step, stream)
-        g_two = None if eager else capture(step_two_call, stream)
+        g_two = None if (eager or not two_call) else capture(step_two_call, stream)
         run_step = g_step.replay if g_step is not None else step
         run_two = g_two.replay if g_two is not None else step_two_call
         for _ in range(a.warmup):
             run_step()
-        # ---------------------------------------------------- timed region: exactly K steps
+        # ---------------------------------------------------- timed region: exactly `calls` passes
         torch.cuda.synchronize()
         if sched is not None:
             sched["i"] = 0                       # the timed steps start the schedule
         t0 = time.perf_counter()
-        secs = gpu_time(run_step, a.steps, stream)
+        secs = gpu_time(run_step, calls, stream)
         wall = time.perf_counter() - t0
-        timed_lens = ([sched["lens"][i % len(sched["lens"])] for i in range(a.steps)]
+        timed_lens = ([sched["lens"][i % len(sched["lens"])] for i in range(calls)]
                       if sched is not None else None)
-        # ---------------------------------------------------- the two-call path, for comparison
-        for _ in range(3):
-            run_two()
-        two_reps = max(5, a.steps // 2)
-        two_secs = gpu_time(run_two, two_reps, stream) / two_reps
+        sv.workspace_status(ws_f)               # no in-kernel wait gave up
+        two_secs = None
+        if two_call:
+            for _ in range(3):
+                run_two()
+            two_reps = max(5, a.steps // 2)
+            two_secs = gpu_time(run_two, two_reps, stream) / two_reps
 
+    steps = calls * units_per_call
     step_bytes, layer_bytes = decode_bytes(w)
     if timed_lens is not None:                   # mean over the timed steps' text lengths
         per = [decode_bytes(w, T) for T in timed_lens]
         step_bytes = sum(p[0] for p in per) // len(per)
         layer_bytes = sum(p[1] for p in per) // len(per)
-    steps_per_s = a.steps / secs
+    steps_per_s = steps / secs
     gbs = step_bytes * steps_per_s / 1e9
     # One launch per layer: the average launch duration over the timed region.
-    layer_avg = secs / (a.steps * w.L)
+    layer_avg = secs / (calls * L)
     layer_gbs = layer_bytes / layer_avg / 1e9
     traffic = committed_traffic(f"fused_{w.name}", source_hash(*FUSED_SOURCES))
-    dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     res = {
-        "metric": "decode steps/s (retrieval + sparse attention, all layers, whole batch)",
-        "value": round(steps_per_s, 2),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(secs / a.steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic (seeded Gaussian caches, 5% planted relevant tokens; no weights)",
+        "value": round(steps_per_s, 2), "unit": "steps/s", "timed_steps": steps,
+        "ms_per_step": round(secs / steps * 1e3, 4),
         "config": {"workload": w.name, "batch": w.B, "layers": w.L, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "visual_tokens": w.N, "k": w.k,
-                   "text_tokens": w.T, "launch": "hipgraph" if g_step is not None else "eager",
-                   "parallelism": "none (1 GPU)"},
+                   "text_tokens": w.T, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+                   "launch": "hipgraph" if g_step is not None else "eager"},
         "hbm_gbs_algorithmic": round(gbs, 1),
         "hbm_frac_algorithmic": round(gbs / HBM_PEAK_GBS, 4),
         "step_bytes_algorithmic": step_bytes,
@@ -346,43 +444,45 @@ def main():
                      "unit": "GB/s", "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": layer_bytes,
                      "avg_launch_us": round(layer_avg * 1e6, 3)},
-        "two_call_path": {"ms_per_step": round(two_secs * 1e3, 4),
-                          "value": round(1.0 / two_secs, 2), "unit": "steps/s",
-                          "launches_per_layer": 2},
         "wall_s_timed": round(wall, 4),
     }
+    if units_per_call > 1:
+        res["config"]["input_sets"] = f"{L} replicas rotated, one step each (footprint >= 1 GB)"
+    if two_secs is not None:
+        res["two_call_path"] = {"ms_per_step": round(two_secs / units_per_call * 1e3, 4),
+                                "value": round(units_per_call / two_secs, 2), "unit": "steps/s",
+                                "launches_per_layer": 2}
     if sched is not None:
-        sum_after = vis_checksum()
-        if sum_after != sum_before:
+        if vis_checksum() != sum_before:
             raise RuntimeError("the visual cache changed during the multi-turn schedule")
         res["config"].update({
             "text_tokens": f"{min(timed_lens)}-{max(timed_lens)}",
             "schedule": "3 rounds x 128 decode steps, fresh query per step; text = 64 system + "
                         "64 question + step + 1, question and answer evicted between rounds; "
-                        "timed steps follow the schedule from its start",
+                        "the timed steps follow the schedule from its start",
             "visual_cache_unchanged": True})
-
-    # ------------------------------------------------------------ per-question dense packing
-    if not a.no_pack and sched is None:
-        res["packed"] = bench_packed(a, dev, stream, w, layers, ws_r, ws_a)
-        res["packed"]["decode_speedup_vs_fused_step"] = round(
-            res["packed"]["decode"]["steps_per_s"] / steps_per_s, 3)
-
-    # ------------------------------------------------------------ prefill salience
-    if not a.no_salience:
-        res["salience"] = bench_salience(a, dev, stream)
-
-    if not a.no_summary:
-        res["summary_salience"] = bench_summary(a, dev, stream)
-
-    # ------------------------------------------------------------ CPU oracle baseline
-    if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(a, w, layers)
-
-    print(json.dumps(res), flush=True)
+    return res
 
 
-def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
+def profile_traffic(a, dev, w):
+    """Counter passes: the fused decode layer as timed, and a plain copy of known
+    size whose counters give the scale factor of the counters."""
+    import torch
+
+    import visual_token_sparsity_amd as sv
+    layers = make_layers(a, dev, w)
+    ws_f = sv.new_workspace(sv.retrieve_attend_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.N, w.k, w.Tmax), dev)
+    for _ in range(2):
+        for d in layers:
+            sv.retrieve_attend(d["q"], d["k_vis"], d["v_vis"], w.k, d["k_txt"], d["v_txt"],
+                               d["txt_len"], workspace=ws_f)
+    torch.cuda.synchronize()
+    nbytes = calibration_copy(torch, dev)
+    print(json.dumps({"profile_traffic": w.name, "layer_bytes": decode_bytes(w)[1],
+                      "copy_bytes": nbytes}), flush=True)
+
+
+def bench_packed(a, dev, stream, w, layers):
     """Per-question retrieval + dense packing, then decode steps over the packed rows.
 
     One question (8 tokens) selects k visual tokens per sequence and layer;
@@ -398,6 +498,8 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
     import visual_token_sparsity_amd as sv
     e = 2 if w.dtype.itemsize == 2 else 4
     row = w.Hkv * w.D * e
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
+    ws_a = sv.new_workspace(sv.sparse_decode_attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.k, w.Tmax), dev)
     gq = torch.Generator(device=dev).manual_seed(synthetic.stream_seed(a.seed, w.name, "question"))
     question = torch.randn((w.B, 8, w.Hq, w.D), generator=gq, device=dev).to(w.dtype)
     idx = [sv.retrieve(question, d["k_vis"], w.k, workspace=ws_r) for d in layers]
@@ -441,7 +543,7 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
             run_pack()
             run_step()
         reps = max(5, a.steps // 4)
-        pack_secs = gpu_time(run_pack, reps, stream) / (reps * w.L)
+        pack_secs = gpu_time(run_pack, reps, stream) / (reps * len(layers))
         step_secs = gpu_time(run_step, a.steps, stream) / a.steps
     q = w.Hq * w.D * e
     step_bytes = w.L * w.B * ((w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4)
@@ -467,7 +569,8 @@ def bench_packed(a, dev, stream, w, layers, ws_r, ws_a):
 
 def bench_summary(a, dev, stream):
     """Summary-token salience and per-frame pruning: CLIP shape (one CLS token) and
-    RADIO shape (4 summary tokens), one graph-captured call each."""
+    RADIO shape (4 summary tokens).  Each call takes the next of several Q/K sets
+    (>= 1 GB of keys in all), so the keys stream from HBM, not the last-level cache."""
     import torch
 
     import synthetic
@@ -475,24 +578,28 @@ def bench_summary(a, dev, stream):
     res = {}
     for name, S in (("clip_l14_336_256f", 1), ("radio_1028_64f", 4)):
         sw = synthetic.SALIENCE[name]
-        Q, K = synthetic.make_salience(sw, a.seed, device=dev, gen_device="cuda")
+        key_bytes = sw.F * sw.H * sw.N * sw.D * 2
+        nsets = max(1, -(-(1 << 30) // key_bytes))
+        sets = [synthetic.make_salience(sw, a.seed + i, device=dev, gen_device="cuda")
+                for i in range(nsets)]
         sal = torch.empty((sw.F, sw.N), dtype=torch.float32, device=dev)
         keep = torch.empty((sw.F, sw.keep), dtype=torch.int32, device=dev)
         ws = sv.new_workspace(sv.summary_salience_prune_workspace_bytes(sw.F, sw.H, sw.N), dev)
 
-        def once():
-            sv.summary_salience_prune(Q, K, S, sw.keep, workspace=ws, salience_out=sal,
-                                      idx_out=keep)
+        def once():                          # one call per set
+            for Q, K in sets:
+                sv.summary_salience_prune(Q, K, S, sw.keep, workspace=ws, salience_out=sal,
+                                          idx_out=keep)
 
         with torch.cuda.stream(stream):
-            for _ in range(3):
+            for _ in range(2):
                 once()
             g = None if a.no_graph else capture(once, stream)
             run = g.replay if g is not None else once
-            for _ in range(3):
+            for _ in range(2):
                 run()
-            reps = max(10, a.steps // 2)
-            secs = gpu_time(run, reps, stream) / reps
+            reps = max(5, a.steps // 10)
+            secs = gpu_time(run, reps, stream) / (reps * nsets)
         # keys once, the summary queries, per-head column values written and read
         # back, the salience written and read by the select, the kept indices
         nbytes = (sw.F * sw.H * sw.N * sw.D * 2 + sw.F * sw.H * S * sw.D * 2
@@ -502,13 +609,20 @@ def bench_summary(a, dev, stream):
                      "head_dim": sw.D, "summary_tokens": S, "keep": sw.keep,
                      "ms_per_call": round(secs * 1e3, 4),
                      "tokens_per_s": round(sw.F * sw.N / secs, 1),
+                     "rotation": f"{nsets} Q/K sets, {nsets * key_bytes / 1e9:.2f} GB of keys",
                      "roofline": {"kernel": "summary_cols_kernel + summary_mean_kernel + "
                                             "per-frame top-k: whole call",
                                   "bound": "hbm", "achieved": round(gbs, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
                                   "bytes_algorithmic": nbytes}}
-        del Q, K
+        if not a.no_cpu_baseline:
+            import oracle
+            Q, K = sets[0]
+            res[name]["cpu_baseline"] = cpu_baseline_salience(
+                a, sw, Q, K, lambda q, k: oracle.summary_salience(q, k, S))
+        del sets
+        free(torch)
     return res
 
 
@@ -536,46 +650,111 @@ def bench_salience(a, dev, stream):
     flops = synthetic.flop_count_salience(sw)
     tflops = flops / secs / 1e12
     executed = committed_mfma_ops(sw.name, source_hash(*SALIENCE_SOURCES))
-    return {"workload": sw.name, "frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
-            "head_dim": sw.D, "keep": sw.keep, "ms_per_call": round(secs * 1e3, 4),
-            "tokens_per_s": round(sw.F * sw.N / secs, 1),
-            "roofline": {"kernel": "salience_rows_kernel (+ flagged-item fp32 pass, head mean, per-frame top-k): whole call",
-                         "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                         "flops_algorithmic": flops,
-                         # MFMA work the call executes (padding of D and of the key
-                         # tiles, column-sum MFMAs), from the committed counters
-                         "flops_executed_counters": executed,
-                         "executed_tflops": (round(executed / secs / 1e12, 2)
-                                             if executed else None)}}
+    res = {"workload": sw.name, "frames": sw.F, "tokens_per_frame": sw.N, "heads": sw.H,
+           "head_dim": sw.D, "keep": sw.keep, "ms_per_call": round(secs * 1e3, 4),
+           "tokens_per_s": round(sw.F * sw.N / secs, 1),
+           "roofline": {"kernel": "salience_rows_kernel (+ flagged-item fp32 pass, head mean, per-frame top-k): whole call",
+                        "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                        "flops_algorithmic": flops,
+                        # MFMA work the call executes (padding of D and of the key
+                        # tiles, column-sum MFMAs), from the committed counters
+                        "flops_executed_counters": executed,
+                        "executed_tflops": (round(executed / secs / 1e12, 2)
+                                            if executed else None)}}
+    if not a.no_cpu_baseline:
+        import oracle
+        res["cpu_baseline"] = cpu_baseline_salience(a, sw, Q, K, oracle.salience)
+    return res
 
 
-def cpu_baseline(a, w, layers):
-    """The fp64 oracle on the host, over as many whole layers as fit the time budget."""
+def hbm_measured(dev, stream):
+    """The bandwidth a plain streaming kernel reaches on this GPU: a 1 GiB
+    device-to-device copy (read + write) and a 1 GiB reduction (read)."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    nbytes = src.numel() * 4
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+            torch.sum(src, dim=0, out=acc)
+        copy_s = gpu_time(lambda: dst.copy_(src), 10, stream) / 10
+        read_s = gpu_time(lambda: torch.sum(src, dim=0, out=acc), 10, stream) / 10
+    return {"what": "torch device copy and sum over 1 GiB buffers (HIP events): what generic "
+                    "streaming kernels reach, next to the 8 TB/s peak",
+            "copy_gbs": round(2 * nbytes / copy_s / 1e9, 1),
+            "read_gbs": round(nbytes / read_s / 1e9, 1),
+            "peak_gbs": HBM_PEAK_GBS}
+
+
+# ---------------------------------------------------------------- CPU oracle baselines
+def cpu_baseline_decode(a, w, layers):
+    """The fp64 oracle on the host over whole (sequence, layer) units of the same
+    decode inputs until the time budget is spent, scaled to steps/s.  Rows of the
+    131072-token workload are scored in token chunks (every score depends on its
+    own token only) so the fp64 copy of a sequence's keys fits in memory."""
     import numpy as np
+    import torch
+
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    ncores, model = cpu_info()
+    units = [(l, b) for l in range(len(layers)) for b in range(w.B)]
+    per_step = w.L * w.B                       # (layer, sequence) units per step
+    done, spent = 0, 0.0
+    for l, b in units:
+        d = layers[l]
+        q = d["q"][b:b + 1].cpu()
+        kt, vt = d["k_txt"][b:b + 1].cpu(), d["v_txt"][b:b + 1].cpu()
+        tl = d["txt_len"][b:b + 1].cpu()
+        if w.N > 32768:
+            chunks = [d["k_vis"][b:b + 1, t0:t0 + 16384].cpu() for t0 in range(0, w.N, 16384)]
+            t0 = time.perf_counter()
+            s = np.concatenate([oracle.retrieval_scores(q, c) for c in chunks], axis=1)
+            idx = oracle.topk_ascending(s, w.k)
+            spent += time.perf_counter() - t0
+            sel = torch.from_numpy(idx[0]).to(d["k_vis"].device)
+            kv, vv = d["k_vis"][b:b + 1, sel].cpu(), d["v_vis"][b:b + 1, sel].cpu()
+            t0 = time.perf_counter()
+            oracle.sparse_decode_attn(q, kv, vv, np.arange(w.k)[None], kt, vt, tl)
+            spent += time.perf_counter() - t0
+        else:
+            kv, vv = d["k_vis"][b:b + 1].cpu(), d["v_vis"][b:b + 1].cpu()
+            t0 = time.perf_counter()
+            idx = oracle.retrieve(q, kv, w.k)
+            oracle.sparse_decode_attn(q, kv, vv, idx, kt, vt, tl)
+            spent += time.perf_counter() - t0
+        done += 1
+        if spent >= a.cpu_seconds:
+            break
+    steps_per_s = done / per_step / spent
+    return {"value": round(steps_per_s, 6), "unit": "steps/s", "cores": blas_threads(),
+            "host_cores_visible": ncores, "cpu_model": model, "kind": "oracle",
+            "sample": f"{done} (layer, sequence) units, {per_step} per step (retrieve + sparse "
+                      f"attention, fp64 NumPy, on the same inputs), {spent:.1f} s, scaled to "
+                      f"whole steps"}
+
+
+def cpu_baseline_salience(a, sw, Q, K, fn):
+    """The fp64 oracle over whole frames until the time budget is spent, scaled to
+    tokens/s."""
     ncores, model = cpu_info()
     done, spent = 0, 0.0
-    for d in layers:
-        host = {k: v.cpu() for k, v in d.items()}
+    for f in range(sw.F):
+        q, k = Q[f:f + 1].cpu(), K[f:f + 1].cpu()
         t0 = time.perf_counter()
-        idx = oracle.retrieve(host["q"], host["k_vis"], w.k)
-        oracle.sparse_decode_attn(host["q"], host["k_vis"], host["v_vis"], idx, host["k_txt"],
-                                  host["v_txt"], host["txt_len"])
+        fn(q, k)
         spent += time.perf_counter() - t0
         done += 1
         if spent >= a.cpu_seconds:
             break
-    steps_per_s = done / w.L / spent
-    return {"value": round(steps_per_s, 5), "unit": "steps/s", "cores": threads,
+    tok_s = done * sw.N / spent
+    return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": blas_threads(),
             "host_cores_visible": ncores, "cpu_model": model, "kind": "oracle",
-            "sample": f"{done} of {w.L} layers x {w.B} sequences (retrieve + sparse attention, "
-                      f"fp64 NumPy), {spent:.1f} s, scaled to whole steps"}
+            "ms_per_call_equivalent": round(sw.F * sw.N / tok_s * 1e3, 1),
+            "sample": f"{done} of {sw.F} frames ({sw.H} heads each, materialised fp64 softmax), "
+                      f"{spent:.1f} s, scaled to tokens/s"}
 
 
 if __name__ == "__main__":
