@@ -132,24 +132,37 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   int r1 = r0 + a.rows_per_item;
   r1 = r1 < a.N ? r1 : a.N;
   const int nrows = r1 - r0;
-  int wrows = (nrows + kItemWaves - 1) / kItemWaves;
-  wrows = ((wrows + RPS - 1) / RPS) * RPS;
-  const int wr0 = wave * wrows;  // relative to r0
-  int wn = nrows - wr0;
-  wn = wn < 0 ? 0 : (wn > wrows ? wrows : wn);
-  const int nunits = wn * nseg;
+  // One-segment rows: blocks of RPS rows go to the waves in turn, so the four
+  // waves read one contiguous run together (one stream per item).  Longer
+  // rows: each wave a contiguous run of whole rows (its units are the
+  // segments of one row after another).
+  int nunits, wr0 = 0;
+  if (nseg == 1) {
+    const int nblk = (nrows + RPS - 1) / RPS;
+    nunits = nblk > wave ? ((nblk - wave + kItemWaves - 1) / kItemWaves) * RPS : 0;
+  } else {
+    const int wrows = (nrows + kItemWaves - 1) / kItemWaves;
+    wr0 = wave * wrows;  // relative to r0
+    int wn = nrows - wr0;
+    wn = wn < 0 ? 0 : (wn > wrows ? wrows : wn);
+    nunits = wn * nseg;
+  }
 
   // The item's rows as one buffer: row r at byte (r - r0) * row_bytes.
   const uint32_t row_bytes = (uint32_t)(a.tstride * ES);
   const BufRsrc rs = make_rsrc(
       reinterpret_cast<const char*>(a.kv) + ((int64_t)b * a.bstride + (int64_t)r0 * a.tstride) * ES,
       (uint32_t)(nrows - 1) * row_bytes + (uint32_t)a.C * 16u);
-  // Unit u of this wave: row wr0 + u / nseg, segment u % nseg.  Units past the
-  // wave's run read past the extent (zeros, no memory traffic).
+  // Unit u of this wave: row unit_row(u) (relative to r0), segment u % nseg.
+  // Units past the wave's run, or rows past the item, read past the extent
+  // (zeros, no memory traffic).
   auto unit_seg = [&](int u) { return nseg == 1 ? 0 : u % nseg; };
+  auto unit_row = [&](int u) {
+    return nseg == 1 ? ((u / RPS) * kItemWaves + wave) * RPS + u % RPS : wr0 + u / nseg;
+  };
   auto unit_off = [&](int u) -> uint32_t {
-    if (u >= nunits) return kBufOob;
-    const int row = wr0 + (nseg == 1 ? u : u / nseg);
+    const int row = unit_row(u);
+    if (u >= nunits || row >= nrows) return kBufOob;
     return (uint32_t)row * row_bytes + (uint32_t)(unit_seg(u) * kScanSegChunks + sub) * 16u;
   };
   // Chunk j of a unit is chunk sub + j*LPR of its segment; chunks past the
@@ -173,9 +186,11 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
       if (sub + j * LPR >= slen) v[j].zero();
   };
 
-  // First keys in flight before the query is summed.
-  Vec<T> nxt[kScanCpl];
-  load_unit(rsub, nxt);
+  // The wave's first two units of keys in flight before the query is summed
+  // (units past the wave's run read nothing).
+  Vec<T> va[kScanCpl], vb[kScanCpl];
+  load_unit(rsub, va);
+  load_unit(RPS + rsub, vb);
 
   // Long rows: a local histogram of the item's score digits, past qhat.
   uint32_t* lh = reinterpret_cast<uint32_t*>(smem + (size_t)CP * VE * sizeof(float));
@@ -217,12 +232,9 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   const bool coherent = a.k > 0;
   float* srow = a.scores + (int64_t)b * a.N + r0;
   float acc = 0.f;
-  for (int u0 = 0; u0 < nunits; u0 += RPS) {
-    Vec<T> cur[kScanCpl];
-#pragma unroll
-    for (int j = 0; j < kScanCpl; ++j) cur[j] = nxt[j];
-    if (u0 + RPS < nunits) load_unit(u0 + RPS + rsub, nxt);
-    const int u = u0 + rsub;
+  // Unit u (keys in cur): the lanes' partial dot products, reduced and stored
+  // at the row's last segment.
+  auto consume = [&](Vec<T>* cur, int u) {
     const int seg = unit_seg(u);
     mask_ragged(u, cur);
 #pragma unroll
@@ -242,8 +254,8 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
     if (seg == nseg - 1) {
       const float s = sum_lanes_rt(acc, LPR);
       acc = 0.f;
-      if (sub == 0 && u < nunits) {
-        const int row = wr0 + u / nseg;
+      const int row = unit_row(u);
+      if (sub == 0 && u < nunits && row < nrows) {
         if (a.encode)
           __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + row, ~__float_as_uint(s),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -253,6 +265,16 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
         } else
           srow[row] = s;
       }
+    }
+  };
+  // Two buffers, each refilled right after it is consumed, so two units per
+  // lane stay in flight (steps are wave-uniform).
+  for (int u0 = 0; u0 < nunits; u0 += 2 * RPS) {
+    consume(va, u0 + rsub);
+    if (u0 + 2 * RPS < nunits) load_unit(u0 + 2 * RPS + rsub, va);
+    if (u0 + RPS < nunits) {
+      consume(vb, u0 + RPS + rsub);
+      if (u0 + 3 * RPS < nunits) load_unit(u0 + 3 * RPS + rsub, vb);
     }
   }
 
