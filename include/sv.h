@@ -328,8 +328,12 @@ sv_status sv_pack_selected(const void* k_vis, const void* v_vis, int64_t vis_bst
  *  idx_out     [F][keep] int32 ascending (may be NULL if keep == 0).
  *  workspace   at least sv_salience_prune_workspace(F, H, N) bytes,
  *              256-byte aligned.
- * Supported: dtype SV_BF16; D a multiple of 8 with 8 <= D <= 96;
- * 1 <= N <= 768 (one frame-head's keys stay in LDS); F*H <= 2^31-1.
+ * Kernels: frames of N <= 768 tokens with D <= 96 keep one frame-head's
+ * keys on chip (one fused pass); longer frames (QwenVL-style encoders,
+ * 10^4 - 10^5 tokens) or wider heads take two streaming passes (row
+ * log-sum-exp, then column sums), the attention map never stored either way.
+ * Supported: dtype SV_BF16; D a multiple of 8 with 8 <= D <= 128; N >= 1;
+ * F*H*ceil(N/256) <= 2^31-1.
  * Errors: SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
  * ---------------------------------------------------------------------- */
 size_t sv_salience_prune_workspace(int F, int H, int N);

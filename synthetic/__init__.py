@@ -106,6 +106,10 @@ SALIENCE: Dict[str, SalienceWorkload] = {
         name="clip_l14_336_256f", F=256, N=577, H=16, D=64, keep=288, std=64 ** -0.25),
     "radio_1028_64f": SalienceWorkload(
         name="radio_1028_64f", F=64, N=1028, H=16, D=64, keep=514, std=64 ** -0.25),
+    # QwenVL-style encoder attending over one long visual input: 16384 tokens
+    # (e.g. a 128 x 128 patch grid) in one attention, 16 heads of 80; keep 50%.
+    "qwenvl_16k": SalienceWorkload(
+        name="qwenvl_16k", F=1, N=16384, H=16, D=80, keep=8192, std=80 ** -0.25),
 }
 
 # Multi-turn schedule of the 131072-token workload: 3 rounds x 128 decode steps,

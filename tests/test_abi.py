@@ -141,8 +141,9 @@ def _sal(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(keep=730), 1), (dict(keep=-1), 1), (dict(F=0), 1), (dict(idx=None), 1),
     (dict(q=None), 1), (dict(q=FAKE + 8), 1),
-    (dict(dt=sv.SV_F32), 2), (dict(N=769), 2), (dict(D=100), 2), (dict(D=70), 2),
-    (dict(wsb=1024), 3),
+    (dict(dt=sv.SV_F32), 2), (dict(D=136), 2), (dict(D=100), 2), (dict(D=70), 2),
+    (dict(wsb=1024), 3), (dict(N=16384, keep=100, wsb=1 << 20), 3),
+    (dict(F=1 << 20, H=1 << 10, N=16384, keep=100), 2),
 ])
 def test_salience_rejects(kw, status):
     assert _sal(**kw) == status

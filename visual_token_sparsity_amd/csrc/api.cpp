@@ -480,10 +480,12 @@ sv_status sv_retrieve_attend_noalloc(const void* q, int B, int Hq, const void* k
 }
 
 // ---------------------------------------------------------------- salience
+// Workspace of sv_salience_prune: [column sums F*H*N][salience F*N][flags F*H]
+// [row lse F*H*N, used by frames beyond the on-chip kernels].
 size_t sv_salience_prune_workspace(int F, int H, int N) {
   if (F < 1 || H < 1 || N < 1) return 256;
-  return align256((size_t)F * H * N * sizeof(float)) + align256((size_t)F * N * sizeof(float)) +
-         align256((size_t)F * H * sizeof(int32_t));
+  return 2 * align256((size_t)F * H * N * sizeof(float)) +
+         align256((size_t)F * N * sizeof(float)) + align256((size_t)F * H * sizeof(int32_t));
 }
 
 sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, int N, int D,
@@ -497,6 +499,8 @@ sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, 
   if (keep < 0 || keep > N) return fail(SV_EINVAL, "sv_salience_prune: keep=%d outside [0, N=%d]", keep, N);
   if (keep > 0 && !idx_out) return fail(SV_EINVAL, "sv_salience_prune: NULL idx_out");
   if (dtype != SV_BF16) return fail(SV_EUNSUPPORTED, "sv_salience_prune: only SV_BF16");
+  if ((int64_t)F * H * ((N + 255) / 256) > 2147483647LL)
+    return fail(SV_EUNSUPPORTED, "sv_salience_prune: F*H*ceil(N/256) workgroups too many");
   if (!sv::salience_supported(N, D))
     return fail(SV_EUNSUPPORTED, "sv_salience_prune: N=%d, D=%d outside the on-chip kernel", N, D);
   if (!aligned16(vis_q) || !aligned16(vis_k))
@@ -508,10 +512,12 @@ sv_status sv_salience_prune(const void* vis_q, const void* vis_k, int F, int H, 
   char* sal_ws = (char*)workspace + align256((size_t)F * H * N * sizeof(float));
   float* sal = salience_out ? salience_out : (float*)sal_ws;
   int32_t* redo = (int32_t*)(sal_ws + align256((size_t)F * N * sizeof(float)));
+  float* lse = (float*)((char*)redo + align256((size_t)F * H * sizeof(int32_t)));
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   hipStream_t st = (hipStream_t)stream;
-  sv_status s = hip_status(sv::launch_salience(vis_q, vis_k, F, H, N, D, sc, colsum, redo, sal, st),
-                           "sv_salience_prune salience");
+  sv_status s = hip_status(
+      sv::launch_salience(vis_q, vis_k, F, H, N, D, sc, colsum, redo, lse, sal, st),
+      "sv_salience_prune salience");
   if (s != SV_OK) return s;
   return hip_status(sv::launch_topk_rows(sal, F, N, N, keep, idx_out, st), "sv_salience_prune select");
 }

@@ -277,8 +277,16 @@ size_t long_select_zero_bytes(int B, int N);
 
 bool salience_supported(int N, int D);
 
+// colsum_ws [F*H][N], redo_ws [F*H], lse_ws [F*H][N] (used by the two-pass
+// streaming kernels for frames beyond the on-chip kernels), sal [F][N].
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D,
-                           float scale, float* colsum_ws, int32_t* redo_ws, float* sal,
-                           hipStream_t stream);
+                           float scale, float* colsum_ws, int32_t* redo_ws, float* lse_ws,
+                           float* sal, hipStream_t stream);
+
+// Two streaming passes for any N (8 <= D <= 128, D % 8 == 0): per-row lse,
+// then column sums; c2 = scale * log2(e).
+bool salience_stream_supported(int N, int D);
+hipError_t launch_salience_stream(const void* q, const void* k, int FH, int N, int D, float c2,
+                                  float* lse_ws, float* colsum_ws, hipStream_t stream);
 
 }  // namespace sv

@@ -946,12 +946,6 @@ static size_t sal_lds_bytes(int tpw, int D) {
   return (size_t)2 * tpw * 16 * D * 2 + kSalXchFloats * sizeof(float);
 }
 
-bool salience_supported(int N, int D) {
-  if (N < 1 || D < 8 || D > 96 || D % 8) return false;
-  const int tpw = pick_tpw(N);
-  if (tpw < 0) return false;
-  return sal_lds_bytes(tpw, D) <= (size_t)kSalMaxLds;
-}
 
 template <int TPW, int KS>
 static hipError_t sal_go(const void* q, const void* k, int FH, int N, int D, float c2,
@@ -1096,12 +1090,25 @@ static hipError_t rows_ntm(const void* q, const void* k, int FH, int N, float c2
   }
 }
 
+// The on-chip kernels (one frame-head's keys in LDS): N <= 768, D <= 96.
+static bool onchip_ok(int N, int D) {
+  if (N < 1 || D < 8 || D > 96 || D % 8) return false;
+  const int tpw = pick_tpw(N);
+  return tpw > 0 && sal_lds_bytes(tpw, D) <= (size_t)kSalMaxLds;
+}
+
+bool salience_supported(int N, int D) { return onchip_ok(N, D) || salience_stream_supported(N, D); }
+
 hipError_t launch_salience(const void* q, const void* k, int F, int H, int N, int D, float scale,
-                           float* colsum_ws, int32_t* redo_ws, float* sal, hipStream_t st) {
+                           float* colsum_ws, int32_t* redo_ws, float* lse_ws, float* sal,
+                           hipStream_t st) {
   const float c2 = scale * 1.4426950408889634f;
   const int FH = F * H;
   hipError_t e;
-  if (rows_ok(N, D)) {
+  if (!onchip_ok(N, D)) {
+    // Long frames (or wide heads): two streaming passes, lse then column sums.
+    e = launch_salience_stream(q, k, FH, N, D, c2, lse_ws, colsum_ws, st);
+  } else if (rows_ok(N, D)) {
     // fp16-probability row kernel, then the fp32 kernel on the items it flagged.
     switch (D) {
       case 64: e = rows_ntm<64>(q, k, FH, N, c2, colsum_ws, redo_ws, st); break;
