@@ -50,7 +50,7 @@ import numpy as np
 __all__ = [
     "to_f64", "retrieval_scores", "topk_ascending", "retrieve",
     "sparse_decode_attn", "dense_decode_attn", "pack_selected", "salience", "salience_prune",
-    "summary_salience", "summary_salience_prune",
+    "summary_salience", "summary_salience_prune", "prefill_attention",
 ]
 
 
@@ -62,8 +62,8 @@ def to_f64(x) -> np.ndarray:
     """
     if hasattr(x, "detach"):                       # torch tensor, without importing torch
         x = x.detach().to("cpu")
-        if x.is_floating_point():
-            x = x.float()
+        if x.is_floating_point() and x.element_size() < 4:
+            x = x.float()                          # bf16 / fp16: exact in fp32
         x = x.numpy()
     x = np.asarray(x)
     if np.issubdtype(x.dtype, np.floating):
@@ -297,3 +297,52 @@ def summary_salience_prune(vis_q, vis_k, S: int, keep: int,
     (ascending indices, ties toward the lower index), as ``salience_prune``."""
     s = summary_salience(vis_q, vis_k, S, scale)
     return s, topk_ascending(s, keep)
+
+
+def prefill_attention(q, k_vis, v_vis, k_txt, v_txt, txt_len,
+                      scale: Optional[float] = None) -> np.ndarray:
+    """Attention of a chunk of query tokens (the current question) at prefill.
+
+    [summary] Sec. 3.2 (query-aware retrieval, its implementation note): the
+    retrieval salience of the question is computed while the question's
+    tokens go through the ordinary (FlashAttention) prefill attention, whose
+    logits against the visual keys are exactly the terms the retrieval score
+    sums.  This is that attention: standard causal softmax attention of the
+    question tokens over the whole context.
+
+    q       [B][Tq][Hq][D]: the question's tokens, in order
+    k_vis, v_vis  [B][N][Hkv][D]: the retained visual cache (earlier in the
+            sequence than the question, so every question token sees every
+            visual token)
+    k_txt, v_txt  [B][Tmax][Hkv][D]: text cache; the first txt_len[b] rows are
+            valid and the LAST Tq of them are the question's own rows (the
+            caller has appended them)
+    returns out [B][Tq][Hq][D] float64: question token tau (text position
+        p = txt_len[b] - Tq + tau) attends E = all N visual tokens, then text
+        rows 0..p (causal; none when p < 0):
+        z_j = scale * q[b,tau,h] . K_j[h // G];  out = sum_j softmax(z)_j V_j[h // G]
+    scale defaults to 1/sqrt(D).
+    """
+    q = to_f64(q)
+    Kv, Vv = to_f64(k_vis), to_f64(v_vis)
+    Kt, Vt = to_f64(k_txt), to_f64(v_txt)
+    tl = to_f64(txt_len)
+    B, Tq, Hq, D = q.shape
+    Hkv = Kv.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Tq, Hq, D), dtype=np.float64)
+    for b in range(B):
+        T = int(tl[b])
+        for tau in range(Tq):
+            p = min(T - Tq + tau, T - 1)
+            KE = np.concatenate([Kv[b], Kt[b, :max(p + 1, 0)]], axis=0)   # [E][Hkv][D]
+            VE = np.concatenate([Vv[b], Vt[b, :max(p + 1, 0)]], axis=0)
+            for h in range(Hq):
+                g = h // G
+                z = (KE[:, g, :] @ q[b, tau, h]) * scale
+                m = z.max()
+                w = np.exp(z - m)
+                out[b, tau, h] = (w @ VE[:, g, :]) / w.sum()
+    return out

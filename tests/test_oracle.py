@@ -516,6 +516,79 @@ def test_synthetic_salience_statistics():
     assert np.all(np.abs(s * 729 - 1) < 0.1)
 
 
+# ---------------------------------------------------------------- prefill attention of a question chunk
+def _prefill_inputs(B=2, Tq=5, Hq=4, Hkv=2, D=8, N=7, Tmax=9, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=torch.float64)  # noqa: E731
+    return (r(B, Tq, Hq, D), r(B, N, Hkv, D), r(B, N, Hkv, D), r(B, Tmax, Hkv, D),
+            r(B, Tmax, Hkv, D), np.array([Tmax, Tq + 2][:B]))
+
+
+def test_prefill_last_token_is_dense_decode_bitwise():
+    """The question's last token sees every text row: the dense decode attention."""
+    q, kv, vv, kt, vt, tl = _prefill_inputs()
+    out = oracle.prefill_attention(q, kv, vv, kt, vt, tl)
+    dense = oracle.dense_decode_attn(q[:, -1], kv, vv, kt, vt, tl)
+    np.testing.assert_array_equal(out[:, -1], dense)
+
+
+def test_prefill_is_causal():
+    """Text rows after a token's position cannot change its output; they do
+    change the outputs of the tokens that see them."""
+    q, kv, vv, kt, vt, tl = _prefill_inputs(B=1)
+    tl = np.array([9])
+    a = oracle.prefill_attention(q, kv, vv, kt, vt, tl)
+    kt2, vt2 = kt.clone(), vt.clone()
+    kt2[:, 7:] += 3.0                     # rows 7, 8: seen by tau = 3, 4 only (p = 4 + tau)
+    vt2[:, 7:] -= 2.0
+    b = oracle.prefill_attention(q, kv, vv, kt2, vt2, tl)
+    np.testing.assert_array_equal(a[:, :3], b[:, :3])
+    assert np.abs(a[:, 3:] - b[:, 3:]).min() > 0
+    # rows past txt_len are never read
+    kt3 = kt.clone()
+    kt3[:, 9:] = float("nan")
+    np.testing.assert_array_equal(a, oracle.prefill_attention(q, kv, vv, kt3, vt, tl))
+
+
+def test_prefill_matches_torch_masked_softmax():
+    """Against torch fp64: logits with an explicit mask (visual keys all visible,
+    text keys causal) filled with -inf, torch.softmax, then a matmul with V."""
+    B, Tq, Hq, Hkv, D, N, Tmax = 2, 6, 6, 3, 16, 11, 10
+    q, kv, vv, kt, vt, _ = _prefill_inputs(B, Tq, Hq, Hkv, D, N, Tmax, seed=3)
+    tl = np.array([10, 4])                # second sequence: the first two tokens see no text
+    out = oracle.prefill_attention(q, kv, vv, kt, vt, tl)
+    G = Hq // Hkv
+    for b in range(B):
+        K = torch.cat([kv[b], kt[b]], 0).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        V = torch.cat([vv[b], vt[b]], 0).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        mask = torch.zeros(Tq, N + Tmax, dtype=torch.bool)
+        mask[:, :N] = True
+        for tau in range(Tq):
+            p = int(tl[b]) - Tq + tau
+            mask[tau, N:N + max(p + 1, 0)] = True
+        z = torch.matmul(q[b].permute(1, 0, 2), K.transpose(1, 2).contiguous()) / math.sqrt(D)
+        z = z.masked_fill(~mask, float("-inf"))
+        ref = torch.matmul(torch.softmax(z, dim=-1), V)
+        np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_bruteforce_loops():
+    q, kv, vv, kt, vt, tl = _prefill_inputs(B=1, Tq=3, Hq=2, Hkv=1, D=3, N=2, Tmax=4, seed=5)
+    tl = np.array([4])
+    out = oracle.prefill_attention(q, kv, vv, kt, vt, tl)
+    for tau in range(3):
+        p = 4 - 3 + tau
+        rows = [(kv[0, j], vv[0, j]) for j in range(2)] + [(kt[0, j], vt[0, j]) for j in range(p + 1)]
+        for h in range(2):
+            z = [sum(float(q[0, tau, h, d]) * float(K[0, d]) for d in range(3)) / math.sqrt(3)
+                 for K, _ in rows]
+            m = max(z)
+            w = [math.exp(v - m) for v in z]
+            tot = math.fsum(w)
+            for d in range(3):
+                want = math.fsum(w[j] * float(rows[j][1][0, d]) for j in range(len(rows))) / tot
+                assert abs(out[0, tau, h, d] - want) < 1e-13
+
 # ---------------------------------------------------------------- mutation check
 _MUTANTS = [
     ("salience", "A.sum(axis=0) / N", "A.sum(axis=1) / N", "row mean instead of column mean"),
@@ -537,6 +610,12 @@ _MUTANTS = [
     ("summary_salience", "out[f] /= H", "out[f] /= 1", "heads summed, not averaged"),
     ("pack_selected", "if 0 <= t < N:", "if 0 <= t < N - 1:", "pack drops the last token"),
     ("pack_selected", "kp[b, j] = Kv[b, t]", "kp[b, j] = Kv[0, t]", "pack reads sequence 0"),
+    ("prefill_attention", "p = min(T - Tq + tau, T - 1)", "p = min(T - Tq + tau + 1, T - 1)",
+     "prefill sees one text row too many"),
+    ("prefill_attention", "p = min(T - Tq + tau, T - 1)", "p = T - 1",
+     "prefill without the causal mask"),
+    ("prefill_attention", "z = (KE[:, g, :] @ q[b, tau, h]) * scale",
+     "z = (KE[:, g, :] @ q[b, 0, h]) * scale", "prefill uses the first token's query"),
 ]
 
 
@@ -557,6 +636,30 @@ def _mutant_module(fn_name, old, new):
     for n in ov.__all__:
         setattr(m, n, ns[n])
     return m
+
+
+def _loop_prefill(q, kv, vv, kt, vt, tl):
+    """Causal prefill attention with Python loops and math.fsum (token tau at text
+    position tl - Tq + tau sees every visual row and text rows up to it)."""
+    B, Tq, Hq, D = q.shape
+    N, Hkv = kv.shape[1], kv.shape[2]
+    G = Hq // Hkv
+    out = np.zeros(q.shape)
+    for b in range(B):
+        for tau in range(Tq):
+            last = int(tl[b]) - Tq + tau
+            rows = [(kv[b, j], vv[b, j]) for j in range(N)]
+            rows += [(kt[b, j], vt[b, j]) for j in range(0, max(last + 1, 0))]
+            for h in range(Hq):
+                z = [math.fsum(q[b, tau, h, d] * K[h // G, d] for d in range(D)) / math.sqrt(D)
+                     for K, _ in rows]
+                mx = max(z)
+                w = [math.exp(v - mx) for v in z]
+                tot = math.fsum(w)
+                for d in range(D):
+                    out[b, tau, h, d] = math.fsum(w[j] * rows[j][1][h // G, d]
+                                                  for j in range(len(rows))) / tot
+    return out
 
 
 def _pins_pass(m, golden_dir):
@@ -594,6 +697,13 @@ def _pins_pass(m, golden_dir):
         Kc, Vc = _coded_cache(2, 7, 2, 3, 1), _coded_cache(2, 7, 2, 3, 2)
         pidx = np.array([[0, 6, 3], [6, 2, 7]])
         if not _pack_decodes(*m.pack_selected(Kc, Vc, pidx), pidx, 7):
+            return False
+        qp = rng.standard_normal((2, 3, 4, 3))
+        kvp, vvp = rng.standard_normal((2, 2, 2, 3)), rng.standard_normal((2, 2, 2, 3))
+        ktp, vtp = rng.standard_normal((2, 5, 2, 3)), rng.standard_normal((2, 5, 2, 3))
+        tlp = np.array([5, 2])
+        if not np.allclose(m.prefill_attention(qp, kvp, vvp, ktp, vtp, tlp),
+                           _loop_prefill(qp, kvp, vvp, ktp, vtp, tlp), rtol=1e-12, atol=1e-13):
             return False
         g = _load(golden_dir, "attention_sparse.json")
         out = m.sparse_decode_attn(_arr(g["q"]), _arr(g["k_vis"]), _arr(g["v_vis"]),
