@@ -379,6 +379,62 @@ sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F,
                                     float* salience_out, int32_t* idx_out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Prefill attention of a question chunk with the query-aware retrieval
+ * fused into it (once per question)
+ *
+ * SparseVILA velog summary, Sec. 3.2 (query-aware token selection, its
+ * implementation note): the question's retrieval salience is computed
+ * alongside its ordinary (FlashAttention) prefill attention; Sec. 3.3,
+ * kernel table (retrieval-salience row).  The logits of every question token
+ * against every visual key feed both: the causal softmax attention of the
+ * question, and (raw, summed over the question's tokens and the query heads
+ * of each KV head) the retrieval score.  One pass over the caches does both.
+ *
+ * For each sequence b, question token tau < Tq (text position
+ * p = txt_len[b] - Tq + tau) and query head h (KV head g = h / G):
+ *     E = { all N visual tokens } U { text rows 0..p }      (none if p < 0)
+ *     out[b,tau,h,:] = sum_{j in E} softmax_j(scale * q[b,tau,h,:] . K_j[g,:]) V_j[g,:]
+ *     s[b,t] = sum_{tau<Tq} sum_{h<Hq} q[b,tau,h,:] . K_vis[b,t,g,:]
+ * (s exactly as sv_retrieve with the same Tq), then the k largest s[b,.]
+ * (ties toward the lower index) in ascending order.
+ *
+ *  q          [B][Tq][Hq][D], contiguous, bf16 (post-RoPE question tokens).
+ *  k_vis,v_vis visual cache, element (b,t,g,d) at
+ *             ptr[b*vis_bstride + t*vis_tstride + g*D + d], t < N.  Read only.
+ *  k_txt,v_txt text cache, element (b,t,g,d) at
+ *             ptr[b*txt_bstride + t*txt_tstride + g*D + d], t < Tmax; the
+ *             first txt_len[b] rows are valid and the LAST Tq of them are
+ *             the question's own K/V (appended by the caller).  May be NULL
+ *             only if Tmax == 0.
+ *  txt_len    [B] int32 device array (clamped to [0, Tmax]).
+ *  scale      softmax scale; <= 0 selects 1/sqrt(D).
+ *  k          tokens to select, 0 <= k <= N (0: no selection).
+ *  out        [B][Tq][Hq][D] fp32.
+ *  idx_out    [B][k] int32, ascending (may be NULL if k == 0).
+ *  scores_out optional [B][N] fp32 retrieval scores (NULL: workspace).
+ *  workspace  at least sv_prefill_attend_retrieve_workspace(...) bytes,
+ *             256-byte aligned; no zero-fill needed.
+ * Supported: dtype SV_BF16; D in {64, 128}; Hq % Hkv == 0;
+ * Tq * Hq / Hkv <= 2^20.
+ * Errors: SV_EINVAL (bad sizes or k, NULL required pointer, strides smaller
+ * than a row or not multiples of 8 elements, misalignment),
+ * SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t sv_prefill_attend_retrieve_workspace(int B, int Tq, int Hq, int Hkv, int D, int N,
+                                            int Tmax);
+
+sv_status sv_prefill_attend_retrieve(const void* q, int B, int Tq, int Hq,
+                                     const void* k_vis, const void* v_vis,
+                                     int64_t vis_bstride, int64_t vis_tstride, int N,
+                                     int Hkv, int D,
+                                     const void* k_txt, const void* v_txt,
+                                     int64_t txt_bstride, int64_t txt_tstride,
+                                     const int32_t* txt_len, int Tmax,
+                                     sv_dtype dtype, float scale, int k,
+                                     float* out, int32_t* idx_out, float* scores_out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -247,3 +247,32 @@ def test_noalloc_rejects_sizes_beyond_the_static_scratch():
                                         sv.SV_BF16, ctypes.c_float(0.0), p, None, p, None)
     assert st == 3, lib.sv_last_error()
     assert b"static scratch" in lib.sv_last_error()
+
+
+def _pf(**kw):
+    a = dict(q=FAKE, B=2, Tq=8, Hq=8, kv=FAKE, vv=FAKE, vbs=1000 * 1024, vts=1024, N=1000, Hkv=8,
+             D=128, kt=FAKE, vt=FAKE, tbs=64 * 1024, tts=1024, tl=FAKE, Tmax=64, dt=sv.SV_BF16,
+             scale=0.0, k=100, out=FAKE, idx=FAKE, sc=None, ws=FAKE, wsb=16, st=None)
+    a.update(kw)
+    lib = sv.load()
+    return lib.sv_prefill_attend_retrieve(
+        a["q"], a["B"], a["Tq"], a["Hq"], a["kv"], a["vv"], a["vbs"], a["vts"], a["N"], a["Hkv"],
+        a["D"], a["kt"], a["vt"], a["tbs"], a["tts"], a["tl"], a["Tmax"], a["dt"], a["scale"],
+        a["k"], a["out"], a["idx"], a["sc"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(ws=None), 1), (dict(B=0), 1), (dict(Tq=0), 1),
+    (dict(k=1001), 1), (dict(k=-1), 1), (dict(idx=None), 1), (dict(tl=None), 1),
+    (dict(Hq=12), 1), (dict(vts=1000), 1), (dict(tts=1020), 1), (dict(kv=FAKE + 8), 1),
+    (dict(dt=sv.SV_F32), 2), (dict(D=96), 2), (dict(Tq=1 << 18, Hq=64, Hkv=8), 2),
+    (dict(wsb=16), 3),
+])
+def test_prefill_rejects(kw, status):
+    assert _pf(**kw) == status
+
+
+def test_prefill_workspace_grows_with_the_question():
+    small = sv.prefill_attend_retrieve_workspace_bytes(8, 8, 32, 32, 128, 1440, 256)
+    big = sv.prefill_attend_retrieve_workspace_bytes(8, 64, 32, 32, 128, 1440, 256)
+    assert small % 256 == 0 and big > small >= 8 * 1440 * 4

@@ -27,6 +27,7 @@ __all__ = [
     "salience_prune_workspace_bytes", "new_workspace", "retrieve_attend",
     "retrieve_attend_workspace_bytes", "pack_selected", "summary_salience_prune",
     "summary_salience_prune_workspace_bytes", "workspace_status", "set_wait_limit",
+    "prefill_attend_retrieve", "prefill_attend_retrieve_workspace_bytes",
     "SV_F32", "SV_BF16",
 ]
 
@@ -87,6 +88,12 @@ def load() -> ctypes.CDLL:
     lib.sv_summary_salience_prune.argtypes = [c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_f, c_i, c_i,
                                               c_p, c_p, c_p, c_sz, c_p]
     lib.sv_summary_salience_prune.restype = c_i
+    lib.sv_prefill_attend_retrieve_workspace.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_i]
+    lib.sv_prefill_attend_retrieve_workspace.restype = c_sz
+    lib.sv_prefill_attend_retrieve.argtypes = [c_p, c_i, c_i, c_i, c_p, c_p, c_i64, c_i64, c_i,
+                                               c_i, c_i, c_p, c_p, c_i64, c_i64, c_p, c_i, c_i,
+                                               c_f, c_i, c_p, c_p, c_p, c_p, c_sz, c_p]
+    lib.sv_prefill_attend_retrieve.restype = c_i
     lib.sv_workspace_status.argtypes = [c_p, c_p]
     lib.sv_workspace_status.restype = c_i
     lib.sv_set_wait_limit.argtypes = [ctypes.c_uint32]
@@ -151,6 +158,64 @@ def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
 def new_workspace(nbytes: int, device) -> torch.Tensor:
     """A zero-filled workspace of ``nbytes`` bytes, reusable across calls."""
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def prefill_attend_retrieve_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, N: int,
+                                            Tmax: int) -> int:
+    return int(load().sv_prefill_attend_retrieve_workspace(B, Tq, Hq, Hkv, D, N, Tmax))
+
+
+def prefill_attend_retrieve(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor,
+                            k_txt: Optional[torch.Tensor], v_txt: Optional[torch.Tensor],
+                            txt_len: Optional[torch.Tensor], k: int,
+                            scale: Optional[float] = None, *, scores: bool = False,
+                            workspace: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None,
+                            idx_out: Optional[torch.Tensor] = None):
+    """Causal prefill attention of a question chunk plus the query-aware retrieval
+    of its top-k visual tokens, from one pass over the caches.
+
+    q        [B][Tq][Hq][D] bf16 (the question's tokens)
+    k_vis, v_vis  [B][N][Hkv][D] (same strides)
+    k_txt, v_txt  [B][Tmax][Hkv][D] (same strides; the last Tq of the txt_len[b]
+             valid rows are the question's own) or None
+    txt_len  int32 [B] on the device, or None when there is no text
+    returns (out fp32 [B][Tq][Hq][D], idx int32 [B][k] ascending[, scores fp32 [B][N]])
+    """
+    lib = load()
+    dev = _on_gpu(q, k_vis, v_vis, k_txt, v_txt, txt_len)
+    if q.dtype != torch.bfloat16 or k_vis.dtype != q.dtype or v_vis.dtype != q.dtype:
+        raise TypeError("prefill_attend_retrieve takes bf16 q and caches")
+    q = q.contiguous()
+    B, Tq, Hq, D = q.shape
+    _, N, Hkv, Dk = k_vis.shape
+    if Dk != D or k_vis.shape[0] != B:
+        raise ValueError("q and k_vis shapes disagree")
+    if k_vis.stride() != v_vis.stride() or k_vis.shape != v_vis.shape:
+        raise ValueError("k_vis and v_vis must share shape and strides")
+    vbs, vts = _cache_strides(k_vis, "k_vis")
+    if k_txt is not None:
+        if k_txt.stride() != v_txt.stride() or k_txt.shape != v_txt.shape:
+            raise ValueError("k_txt and v_txt must share shape and strides")
+        tbs, tts = _cache_strides(k_txt, "k_txt")
+        Tmax = k_txt.shape[1]
+        if txt_len is None or txt_len.dtype != torch.int32:
+            raise TypeError("txt_len must be an int32 device tensor")
+        txt_len = txt_len.contiguous()
+    else:
+        tbs = tts = Tmax = 0
+    res = out if out is not None else torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=dev)
+    idx = idx_out if idx_out is not None else torch.empty((B, max(k, 0)), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, N), dtype=torch.float32, device=dev) if scores else None
+    ws = _workspace(prefill_attend_retrieve_workspace_bytes(B, Tq, Hq, Hkv, D, N, Tmax), dev,
+                    workspace)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.sv_prefill_attend_retrieve(
+        q.data_ptr(), B, Tq, Hq, k_vis.data_ptr(), v_vis.data_ptr(), vbs, vts, N, Hkv, D,
+        ptr(k_txt), ptr(v_txt), tbs, tts, ptr(txt_len) if Tmax else None, Tmax, SV_BF16,
+        float(scale) if scale else 0.0, k, res.data_ptr(), idx.data_ptr() if k > 0 else None,
+        ptr(sc), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev)))
+    return (res, idx, sc) if scores else (res, idx)
 
 
 def workspace_status(workspace: torch.Tensor) -> None:

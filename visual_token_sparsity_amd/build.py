@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsv.so")
 
 SOURCES = ["api.cpp", "retrieve.hip", "attn.hip", "fused.hip", "fused_bf16.hip", "fused_f32.hip",
-           "salience.hip", "salience_stream.hip", "pack.hip", "summary.hip"]
+           "salience.hip", "salience_stream.hip", "pack.hip", "summary.hip",
+           "prefill.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -11,6 +11,7 @@
 
 #include "common.h"
 #include "pack.h"
+#include "prefill.h"
 #include "summary.h"
 #include "sv.h"
 
@@ -562,4 +563,89 @@ sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F,
   return hip_status(sv::launch_summary_salience(vis_q, vis_k, F, H, N, D, S, sc, keep, colh, sal,
                                                 idx_out, (hipStream_t)stream),
                     fn);
+}
+
+// ---------------------------------------------------------------- prefill attention + retrieval
+// Workspace: [split partials][partial retrieval scores B*NP*N][scores B*N].
+size_t sv_prefill_attend_retrieve_workspace(int B, int Tq, int Hq, int Hkv, int D, int N,
+                                            int Tmax) {
+  if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || N < 1 || Tmax < 0) return 256;
+  const sv::PrefillPlan p = sv::prefill_plan(B, Tq, Hq, Hkv, N, Tmax);
+  return align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float)) +
+         align256((size_t)B * p.NP * N * sizeof(float)) + align256((size_t)B * N * sizeof(float));
+}
+
+sv_status sv_prefill_attend_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis,
+                                     const void* v_vis, int64_t vis_bstride, int64_t vis_tstride,
+                                     int N, int Hkv, int D, const void* k_txt, const void* v_txt,
+                                     int64_t txt_bstride, int64_t txt_tstride,
+                                     const int32_t* txt_len, int Tmax, sv_dtype dtype,
+                                     float scale, int k, float* out, int32_t* idx_out,
+                                     float* scores_out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  const char* fn = "sv_prefill_attend_retrieve";
+  if (!q || !k_vis || !v_vis || !out || !workspace)
+    return fail(SV_EINVAL, "%s: NULL q, k_vis, v_vis, out or workspace", fn);
+  if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || N < 1 || Tmax < 0)
+    return fail(SV_EINVAL, "%s: bad sizes B=%d Tq=%d Hq=%d Hkv=%d N=%d Tmax=%d", fn, B, Tq, Hq,
+                Hkv, N, Tmax);
+  if (k < 0 || k > N) return fail(SV_EINVAL, "%s: k=%d outside [0, N=%d]", fn, k, N);
+  if (k > 0 && !idx_out) return fail(SV_EINVAL, "%s: NULL idx_out", fn);
+  if (Tmax > 0 && (!k_txt || !v_txt || !txt_len))
+    return fail(SV_EINVAL, "%s: NULL k_txt, v_txt or txt_len", fn);
+  if (Hq % Hkv) return fail(SV_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (dtype != SV_BF16) return fail(SV_EUNSUPPORTED, "%s: dtype %d (bf16 only)", fn, (int)dtype);
+  if (D != 64 && D != 128) return fail(SV_EUNSUPPORTED, "%s: D=%d (64 or 128)", fn, D);
+  const int64_t R = (int64_t)Hkv * D;
+  if (vis_tstride < R || vis_bstride < 0 || vis_tstride % 8 || vis_bstride % 8)
+    return fail(SV_EINVAL, "%s: visual strides must be >= row and multiples of 8", fn);
+  if (Tmax > 0 && (txt_tstride < R || txt_bstride < 0 || txt_tstride % 8 || txt_bstride % 8))
+    return fail(SV_EINVAL, "%s: text strides must be >= row and multiples of 8", fn);
+  if (!aligned16(q) || !aligned16(k_vis) || !aligned16(v_vis) ||
+      (Tmax > 0 && (!aligned16(k_txt) || !aligned16(v_txt))))
+    return fail(SV_EINVAL, "%s: q and caches must be 16-byte aligned", fn);
+  if ((int64_t)Tq * (Hq / Hkv) > (1 << 20))
+    return fail(SV_EUNSUPPORTED, "%s: Tq * Hq / Hkv query rows per KV head above 2^20", fn);
+  const sv::PrefillPlan p = sv::prefill_plan(B, Tq, Hq, Hkv, N, Tmax);
+  if ((int64_t)B * Hkv * p.RC * (p.CV + p.CT) > 2147483647LL ||
+      (int64_t)B * Hkv * p.RC * p.W * 32 > 2147483647LL)
+    return fail(SV_EUNSUPPORTED, "%s: too many workgroups", fn);
+  const size_t need = sv_prefill_attend_retrieve_workspace(B, Tq, Hq, Hkv, D, N, Tmax);
+  if (workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  char* ws = (char*)workspace;
+  sv::PrefillArgs a{};
+  a.q = (const sv::bf16_t*)q;
+  a.kv = (const sv::bf16_t*)k_vis;
+  a.vv = (const sv::bf16_t*)v_vis;
+  a.kt = (const sv::bf16_t*)k_txt;
+  a.vt = (const sv::bf16_t*)v_txt;
+  a.vbs = vis_bstride;
+  a.vts = vis_tstride;
+  a.tbs = txt_bstride;
+  a.tts = txt_tstride;
+  a.txt_len = Tmax > 0 ? txt_len : nullptr;
+  a.B = B;
+  a.Tq = Tq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.D = D;
+  a.N = N;
+  a.Tmax = Tmax;
+  a.c2 = (scale > 0.f ? scale : 1.0f / std::sqrt((float)D)) * 1.4426950408889634f;
+  a.rows = p.rows;
+  a.W = p.W;
+  a.RC = p.RC;
+  a.E = p.E;
+  a.CV = p.CV;
+  a.CT = p.CT;
+  a.NP = p.NP;
+  a.part = (float*)ws;
+  ws += align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float));
+  a.pscore = (float*)ws;
+  ws += align256((size_t)B * p.NP * N * sizeof(float));
+  a.out = out;
+  float* scores = scores_out ? scores_out : (float*)ws;
+  return hip_status(sv::launch_prefill(a, scores, k, idx_out, (hipStream_t)stream), fn);
 }

@@ -1,0 +1,374 @@
+// Prefill attention of a question chunk with the query-aware retrieval fused
+// into it.
+//
+// SparseVILA velog summary, Sec. 3.2 (query-aware token selection, its
+// implementation note): the retrieval salience of the question is computed
+// alongside the question's ordinary (FlashAttention) prefill attention; the
+// kernel table (Sec. 3.3) credits the retrieval-salience kernel with its
+// speedup.  Both need the same logits q . K of every question token against
+// every visual key: the attention turns them into a causal softmax over the
+// whole context, the retrieval sums them (raw) over the question's tokens and
+// the query heads of each KV head.  Here one pass over the caches does both.
+//
+// Item (b, g, rc, c): KV head g of sequence b, row chunk rc of the question's
+// Tq * G query rows of that head (row = tau * G + h % G), key split c (visual
+// splits first, then text splits; E keys each).  W waves per workgroup, 32
+// query rows per wave (two 16-row blocks).  Keys stream through LDS in
+// stages of 32 (double-buffered): K fragment-major (direct global -> LDS
+// loads), V row-major with a padded row stride.
+//
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K tile, B = Q^T, fp32 acc;
+//                  lane (li, lg) holds keys 4 lg + r of row li)
+//   retrieval:    raw S^T summed over the wave's rows (DPP over the 16 lanes
+//                 of a key group) -> partial score of each visual key
+//   softmax:      online, per row; x = S scale log2(e), masked (keys past the
+//                 split, text rows past the token's position) to -inf
+//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16: B = P^T straight from the S^T
+//                  registers, as bf16 high part + bf16 residual; A = V^T read
+//                  with ds_read_tr16_b64, which transposes 4 x 16-bit per lane)
+//
+// Partials (m, l, O) of each split go to the workspace; a combine kernel
+// merges them per row by max-rescaling, and a third kernel sums the partial
+// retrieval scores in a fixed order (deterministic) before the top-k select.
+#include "common.h"
+#include "prefill.h"
+
+namespace sv {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPfStage = 32;       // keys per LDS stage (two 16-key tiles)
+constexpr int kPfRowsPerWave = 32;
+constexpr int kPfVPad = 32;        // bytes of padding per V row in LDS
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row16_add(float v) {
+  v += dpp_row<0xB1>(v);
+  v += dpp_row<0x4E>(v);
+  v += dpp_row<0x141>(v);
+  v += dpp_row<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int D, int W>
+struct PfShape {
+  static constexpr int KS = D / 32;                        // 32-wide k-steps of Q K^T
+  static constexpr int DB = D / 16;                        // 16-dim blocks of P V
+  static constexpr int KBYTES = 2 * KS * 1024;             // K fragments of one stage
+  static constexpr int VSTR = D * 2 + kPfVPad;             // V row stride in LDS (bytes)
+  static constexpr int VBYTES = kPfStage * VSTR;
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int VCH = kPfStage * D / 8;             // 16-byte V chunks per stage
+  static constexpr int VPT = VCH / (W * kWave);            // ... per thread
+  static_assert(VCH % (W * kWave) == 0, "V stage split evenly");
+};
+
+template <int D, int W>
+__global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
+  using S = PfShape<D, W>;
+  constexpr int KS = S::KS, DB = S::DB;
+  __shared__ __align__(16) char lds[2 * S::BUF];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const int C = a.CV + a.CT;
+
+  int x = blockIdx.x;
+  const int c = x % C;
+  x /= C;
+  const int rc = x % a.RC;
+  x /= a.RC;
+  const int g = x % a.Hkv;
+  const int b = x / a.Hkv;
+
+  int tl = a.txt_len ? a.txt_len[b] : 0;
+  tl = tl < 0 ? 0 : (tl > a.Tmax ? a.Tmax : tl);
+  const bool visual = c < a.CV;
+  const int e0 = (visual ? c : c - a.CV) * a.E;
+  int e1 = e0 + a.E;
+  const int lim = visual ? a.N : tl;
+  e1 = e1 < lim ? e1 : lim;
+  const int nkeys = e1 > e0 ? e1 - e0 : 0;
+  const bf16_t* kbase = visual ? a.kv + (int64_t)b * a.vbs : a.kt + (int64_t)b * a.tbs;
+  const bf16_t* vbase = visual ? a.vv + (int64_t)b * a.vbs : a.vt + (int64_t)b * a.tbs;
+  const int64_t ts = visual ? a.vts : a.tts;
+  const int Hkv = a.Hkv;
+
+  // Q^T fragments (B operand) of this wave's two row blocks; the text
+  // position of each of this lane's rows (16 rb + li).
+  bf16x8_t qf[2][KS];
+  int pos[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rc * (W * kPfRowsPerWave) + wave * kPfRowsPerWave + 16 * rb + li;
+    const bool ok = row < a.rows;
+    const int tau = ok ? row / a.G : 0, hh = ok ? row - tau * a.G : 0;
+    pos[rb] = ok ? tl - a.Tq + tau : -1;
+    const bf16_t* qr = a.q + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 u = ok ? *reinterpret_cast<const uint4*>(qr + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qf[rb][s] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+
+  // Stage loads: K fragments (tile t, step s: lane (li, lg) -> key 16 t + li,
+  // dims 32 s + 8 lg) directly into LDS; V rows into registers, then LDS.
+  // Keys past the split read the split's first key (masked later).
+  const int nst = (nkeys + kPfStage - 1) / kPfStage;
+  auto key_row = [&](int k) -> int64_t { return (int64_t)(e0 + (k < nkeys ? k : 0)) * ts + g * D; };
+  auto load_k = [&](int st, char* buf) {
+    for (int f = wave; f < 2 * KS; f += W) {
+      const int t = f / KS, s = f - t * KS;
+      const bf16_t* src = kbase + key_row(st * kPfStage + 16 * t + li) + 32 * s + 8 * lg;
+      char* dst = buf + f * 1024;
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
+  };
+  u32x4 vreg[S::VPT];
+  auto load_v = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < S::VPT; ++i) {
+      const int ch = i * (W * kWave) + tid;
+      const int key = ch / (D / 8), d8 = ch - key * (D / 8);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + key_row(st * kPfStage + key) + 8 * d8);
+    }
+  };
+  auto store_v = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < S::VPT; ++i) {
+      const int ch = i * (W * kWave) + tid;
+      const int key = ch / (D / 8), d8 = ch - key * (D / 8);
+      *reinterpret_cast<u32x4*>(buf + S::KBYTES + key * S::VSTR + d8 * 16) = vreg[i];
+    }
+  };
+
+  float m[2], l[2];
+  f32x4_t acc[2][DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float* pscore = visual ? a.pscore + ((int64_t)b * a.NP + (g * a.RC + rc) * W + wave) * a.N : nullptr;
+
+  if (nst > 0) {
+    load_k(0, lds);
+    load_v(0);
+    store_v(lds);
+  }
+  wait_stores_complete();  // direct LDS loads landed (vmcnt = 0)
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    char* cur = lds + (st & 1) * S::BUF;
+    char* nxt = lds + ((st + 1) & 1) * S::BUF;
+    const bool more = st + 1 < nst;
+    if (more) {
+      load_k(st + 1, nxt);
+      load_v(st + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8_t kf[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8_t*>(cur + ((t * KS + s) * kWave + lane) * 16);
+      f32x4_t St[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[rb][s], z, 0, 0, 0);
+        St[rb] = z;  // St[rb][r] = S[row 16 rb + li][key 16 t + 4 lg + r]
+      }
+      const int kb = st * kPfStage + 16 * t + 4 * lg;  // split-relative key of r = 0
+      if (visual) {
+        // Retrieval: raw logits of the key summed over this wave's rows.
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = row16_add(St[0][r] + St[1][r]);
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb + r < nkeys) pscore[e0 + kb + r] = sc[r];
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float xv[4], tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int k = kb + r;
+          const bool ok = k < nkeys && (visual || e0 + k <= pos[rb]);
+          xv[r] = ok ? St[rb][r] * a.c2 : -INFINITY;
+          tmax = fmaxf(tmax, xv[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float mn = fmaxf(m[rb], tmax);
+        const float al = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = xv[r] == -INFINITY ? 0.f : fast_exp2(xv[r] - mn);
+          ps += p[r];
+        }
+        l[rb] = l[rb] * al + ps;
+        m[rb] = mn;
+        // P^T as the B operand: high bf16 part and the bf16 residual.
+        s16x4 ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t h = bf16_rne(p[r]);
+          ph[r] = (short)h;
+          pl[r] = (short)bf16_rne(p[r] - __uint_as_float((uint32_t)h << 16));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          // V^T fragment: lane (li, lg) gets dim 16 db + li of keys 16 t + 4 lg .. + 3.
+          const int vkey = 16 * t + 4 * lg + (li >> 2);
+          const char* va = cur + S::KBYTES + vkey * S::VSTR + (16 * db + 4 * (li & 3)) * 2;
+          const s16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(va));
+          f32x4_t o = acc[rb][db] * al;
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, ph, o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl, o, 0, 0, 0);
+          acc[rb][db] = o;  // acc[rb][db][r] = O[row 16 rb + li][dim 16 db + 4 lg + r]
+        }
+      }
+    }
+    if (more) store_v(nxt);
+    wait_stores_complete();
+    __syncthreads();
+  }
+
+  // Partial of split c for this wave's rows: O (unnormalised), m, l.
+  float* part = a.part + (((int64_t)(b * Hkv + g) * a.RC + rc) * C + c) * (W * kPfRowsPerWave) *
+                              (D + 4);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float lt = l[rb];
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int rl = wave * kPfRowsPerWave + 16 * rb + li;
+    float* pr = part + (int64_t)rl * (D + 4);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
+    if (lg == 0) {
+      pr[D] = m[rb];
+      pr[D + 1] = lt;
+    }
+  }
+}
+
+// Merge the C splits of every row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+template <int D>
+__global__ __launch_bounds__(D) void prefill_combine_kernel(PrefillArgs a) {
+  const int RCH = a.W * kPfRowsPerWave;
+  int x = blockIdx.x;
+  const int rl = x % RCH;
+  x /= RCH;
+  const int rc = x % a.RC;
+  x /= a.RC;
+  const int g = x % a.Hkv;
+  const int b = x / a.Hkv;
+  const int row = rc * RCH + rl;
+  if (row >= a.rows) return;
+  const int C = a.CV + a.CT;
+  const float* p = a.part + ((int64_t)(b * a.Hkv + g) * a.RC + rc) * C * RCH * (D + 4) +
+                   (int64_t)rl * (D + 4);
+  const int64_t cs = (int64_t)RCH * (D + 4);
+  float M = -INFINITY;
+  for (int c = 0; c < C; ++c) M = fmaxf(M, p[c * cs + D]);
+  float num = 0.f, den = 0.f;
+  const int d = threadIdx.x;
+  for (int c = 0; c < C; ++c) {
+    const float mc = p[c * cs + D];
+    const float w = mc == -INFINITY ? 0.f : fast_exp2(mc - M);
+    num = fmaf(w, p[c * cs + d], num);
+    den = fmaf(w, p[c * cs + D + 1], den);
+  }
+  const int tau = row / a.G, hh = row - tau * a.G;
+  a.out[(((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + d] = den > 0.f ? num / den : 0.f;
+}
+
+// scores[b][t] = sum over the NP partials (fixed order).
+__global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillArgs a, float* scores) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.N) return;
+  const int b = (int)(i / a.N), t = (int)(i - (int64_t)b * a.N);
+  const float* p = a.pscore + (int64_t)b * a.NP * a.N + t;
+  float s = 0.f;
+  for (int j = 0; j < a.NP; ++j) s += p[(int64_t)j * a.N];
+  scores[i] = s;
+}
+
+template <int D>
+hipError_t prefill_go(const PrefillArgs& a, hipStream_t st) {
+  const int64_t items = (int64_t)a.B * a.Hkv * a.RC * (a.CV + a.CT);
+  switch (a.W) {
+    case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), dim3((unsigned)items), dim3(kWave), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), dim3((unsigned)items), dim3(2 * kWave), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), dim3((unsigned)items), dim3(4 * kWave), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.RC * a.W * kPfRowsPerWave;
+  hipLaunchKernelGGL((prefill_combine_kernel<D>), dim3((unsigned)rows), dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax) {
+  PrefillPlan p{};
+  p.rows = Tq * (Hq / Hkv);
+  p.W = p.rows <= 32 ? 1 : (p.rows <= 64 ? 2 : 4);
+  p.RC = (p.rows + p.W * kPfRowsPerWave - 1) / (p.W * kPfRowsPerWave);
+  const int64_t heads = (int64_t)B * Hkv * p.RC;
+  const int64_t ctarget = heads >= 512 ? 1 : (512 + heads - 1) / heads;
+  int64_t E = ((int64_t)N + Tmax + ctarget - 1) / ctarget;
+  E = (E + kPfStage - 1) / kPfStage * kPfStage;
+  if (E < 64) E = 64;
+  p.E = (int)E;
+  p.CV = (int)((N + E - 1) / E);
+  p.CT = (int)((Tmax + E - 1) / E);
+  p.NP = Hkv * p.RC * p.W;
+  return p;
+}
+
+size_t prefill_part_floats(int B, int Hkv, int D, const PrefillPlan& p) {
+  return (size_t)B * Hkv * p.RC * (p.CV + p.CT) * p.W * kPfRowsPerWave * (D + 4);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, float* scores, int k, int32_t* idx,
+                          hipStream_t st) {
+  hipError_t e = a.D == 128 ? prefill_go<128>(a, st) : prefill_go<64>(a, st);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)a.B * a.N;
+  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a,
+                     scores);
+  e = hipGetLastError();
+  if (e != hipSuccess || k <= 0) return e;
+  return launch_topk_rows(scores, a.B, a.N, a.N, k, idx, st);
+}
+
+}  // namespace sv
