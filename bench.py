@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--pack-only", action="store_true",
                    help="time only the per-question pack and the decode over packed rows "
                         "(profiling runs); prints its object")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="time only the question prefill with fused retrieval (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget of each CPU oracle sample")
     p.add_argument("--seed", type=int, default=0)
@@ -248,6 +250,10 @@ def main():
     if a.profile_traffic:
         profile_traffic(a, dev, w)
         return
+    if a.prefill_only:
+        layers = make_layers(a, dev, w)
+        print(json.dumps({"prefill_retrieve": bench_prefill(a, dev, stream, w, layers)}), flush=True)
+        return
 
     # ------------------------------------------------------------ headline decode workload
     layers = make_layers(a, dev, w)
@@ -278,6 +284,10 @@ def main():
         res["packed"] = bench_packed(a, dev, stream, w, layers)
         res["packed"]["decode_speedup_vs_fused_step"] = round(
             res["packed"]["decode"]["steps_per_s"] / res["value"], 3)
+
+    # ------------------------------------------------------------ question prefill + fused retrieval
+    if not a.no_pack and w.name != "multiturn_128k":
+        res["prefill_retrieve"] = bench_prefill(a, dev, stream, w, layers)
 
     # ------------------------------------------------------------ CPU oracle, headline workload
     if not a.no_cpu_baseline:
@@ -573,6 +583,92 @@ def bench_packed(a, dev, stream, w, layers):
                        "hbm_gbs_algorithmic": round(step_gbs, 1),
                        "hbm_frac_algorithmic": round(step_gbs / HBM_PEAK_GBS, 4),
                        "launch": "hipgraph" if g_step is not None else "eager"}}
+
+
+def bench_prefill(a, dev, stream, w, layers, Tq=32):
+    """A question of Tq tokens through every layer: causal prefill attention over the
+    visual cache and the text (whose last Tq rows are the question's), with the
+    query-aware retrieval of k tokens fused in (sv_prefill_attend_retrieve, one
+    launch per layer plus its combine / select launches).  Next to it, the
+    retrieval alone as a separate pass (sv_retrieve with the same Tq)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    import visual_token_sparsity_amd as sv
+    gq = torch.Generator(device=dev).manual_seed(synthetic.stream_seed(a.seed, w.name, "prefill_q"))
+    qs = [torch.randn((w.B, Tq, w.Hq, w.D), generator=gq, device=dev).to(w.dtype) for _ in layers]
+    ws = sv.new_workspace(sv.prefill_attend_retrieve_workspace_bytes(w.B, Tq, w.Hq, w.Hkv, w.D, w.N,
+                                                                     w.Tmax), dev)
+    ws_r = sv.new_workspace(sv.retrieve_workspace_bytes(w.B, w.N, w.k), dev)
+    out = [torch.empty((w.B, Tq, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in layers]
+    idx = [torch.empty((w.B, w.k), dtype=torch.int32, device=dev) for _ in layers]
+
+    def fused():
+        for l, d in enumerate(layers):
+            sv.prefill_attend_retrieve(qs[l], d["k_vis"], d["v_vis"], d["k_txt"], d["v_txt"],
+                                       d["txt_len"], w.k, workspace=ws, out=out[l], idx_out=idx[l])
+
+    def retrieval_only():
+        for l, d in enumerate(layers):
+            sv.retrieve(qs[l], d["k_vis"], w.k, workspace=ws_r, out=idx[l])
+
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            fused()
+            retrieval_only()
+        g1 = None if a.no_graph else capture(fused, stream)
+        g2 = None if a.no_graph else capture(retrieval_only, stream)
+        r1 = g1.replay if g1 is not None else fused
+        r2 = g2.replay if g2 is not None else retrieval_only
+        for _ in range(2):
+            r1()
+            r2()
+        reps = max(5, a.steps // 10)
+        t_fused = gpu_time(r1, reps, stream) / reps
+        t_ret = gpu_time(r2, reps, stream) / reps
+    e = 2 if w.dtype.itemsize == 2 else 4
+    row = w.Hkv * w.D * e
+    per_layer = w.B * ((w.N + w.T) * 2 * row + Tq * w.Hq * w.D * (e + 4) + w.N * 4 + w.k * 4)
+    flops = 4.0 * w.B * Tq * w.Hq * (w.N + w.T) * w.D * len(layers)
+    gbs = per_layer * len(layers) / t_fused / 1e9
+    res = {"question_tokens": Tq, "layers": len(layers), "k": w.k,
+           "ms_per_question": round(t_fused * 1e3, 4),
+           "tokens_per_s": round(w.B * Tq / t_fused, 1),
+           "roofline": {"kernel": "prefill_attn_kernel + combine + score sum + top-k, every layer",
+                        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "bytes_per_layer": per_layer,
+                        "mfma_tflops": round(flops / t_fused / 1e12, 2)},
+           "retrieval_alone_ms": round(t_ret * 1e3, 4),
+           "what": "attention of the question (causal over the text, all visual tokens) and its "
+                   "top-k retrieval from one pass; retrieval_alone is sv_retrieve with the same "
+                   "question tokens (a separate pass over the visual keys)"}
+    if not a.no_cpu_baseline:
+        import oracle
+        ncores, model = cpu_info()
+        done, spent = 0, 0.0
+        for l, d in enumerate(layers):
+            for b in range(w.B):
+                h = {n: d[n][b:b + 1].cpu() for n in ("k_vis", "v_vis", "k_txt", "v_txt")}
+                qb = qs[l][b:b + 1].cpu()
+                tl = d["txt_len"][b:b + 1].cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.prefill_attention(qb, h["k_vis"], h["v_vis"], h["k_txt"], h["v_txt"], tl)
+                oracle.retrieve(qb, h["k_vis"], w.k)
+                spent += time.perf_counter() - t0
+                done += 1
+                if spent >= a.cpu_seconds:
+                    break
+            if spent >= a.cpu_seconds:
+                break
+        per_q = spent / done * w.B * len(layers)
+        res["cpu_baseline"] = {"value": round(w.B * Tq / per_q, 2), "unit": "tokens/s",
+                               "cores": blas_threads(), "host_cores_visible": ncores,
+                               "cpu_model": model, "kind": "oracle",
+                               "sample": f"{done} (layer, sequence) units of {w.B * len(layers)} "
+                                         f"(prefill attention + retrieval, fp64), {spent:.1f} s"}
+    return res
 
 
 def bench_summary(a, dev, stream):
