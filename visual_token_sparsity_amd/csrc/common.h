@@ -105,6 +105,45 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum over aligned groups of Width lanes (a power of two up to 64), the total
+// in every lane of the group.  Inside a 16-lane row the steps are DPP moves
+// (quad xor 1, quad xor 2, half-row mirror, row mirror: VALU, no LDS trip);
+// wider groups add cross-row shuffles.  Every lane adds the same two partial
+// sums at each step, so all lanes of a group get bit-identical totals, equal
+// to the xor-butterfly's.
+// The value of lane (lane ^ OFF), OFF a power of two below 64, without an
+// LDS trip: a DPP row rotation for 8; for 16 and 32 the row-swap moves
+// (v_permlane16_swap / v_permlane32_swap) applied to v and itself return
+// both halves of each pair, and the lane keeps the other one.
+template <int OFF>
+__device__ __forceinline__ float xor_partner(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if constexpr (OFF == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  } else {
+    return __shfl_xor(v, OFF, kWave);
+  }
+}
+
+template <int Width>
+__device__ __forceinline__ float lane_group_sum(float v) {
+#define SV_DPP_ADD(ctrl) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false))
+  if constexpr (Width >= 2) SV_DPP_ADD(0xB1);   // quad_perm [1,0,3,2]
+  if constexpr (Width >= 4) SV_DPP_ADD(0x4E);   // quad_perm [2,3,0,1]
+  if constexpr (Width >= 8) SV_DPP_ADD(0x141);  // row_half_mirror
+  if constexpr (Width >= 16) SV_DPP_ADD(0x140); // row_mirror
+#undef SV_DPP_ADD
+  if constexpr (Width >= 32) v += xor_partner<16>(v);
+  if constexpr (Width >= 64) v += xor_partner<32>(v);
+  return v;
+}
+
 // Whole-wave inclusive prefix sum (all 64 lanes active), DPP only: row
 // shifts build 16-lane scans, then row broadcasts carry the row totals.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

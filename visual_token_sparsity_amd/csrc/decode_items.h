@@ -27,6 +27,8 @@
 // arrive merges them by max-rescaling and writes the output.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "select.h"
 
@@ -105,8 +107,15 @@ __host__ inline void scan_geometry(int C, int* nseg, int* LPR) {
 }
 
 __device__ __forceinline__ float sum_lanes_rt(float v, int width) {
-  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  switch (width) {  // wave-uniform
+    case 1: return v;
+    case 2: return lane_group_sum<2>(v);
+    case 4: return lane_group_sum<4>(v);
+    case 8: return lane_group_sum<8>(v);
+    case 16: return lane_group_sum<16>(v);
+    case 32: return lane_group_sum<32>(v);
+    default: return lane_group_sum<64>(v);
+  }
 }
 
 // One scan item: rows [item*rows_per_item, ...) of sequence b.  Returns true
@@ -571,7 +580,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
       float s = 0.f;
 #pragma unroll
       for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
-      z[i] = group_sum<LPE>(s);
+      z[i] = lane_group_sum<LPE>(s);
     }
     if (off[j] != kBufOob) {
 #pragma unroll
@@ -587,25 +596,29 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     }
   }
 
-  // Merge the EPW lane groups of this wave.
-#pragma unroll
-  for (int off = LPE; off < kWave; off <<= 1) {
+  // Merge the EPW lane groups of this wave (partner values by DPP and
+  // row-swap moves, no LDS trips).
+  auto merge_groups = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const float mo = __shfl_xor(m[i], off, kWave);
-      const float lo = __shfl_xor(l[i], off, kWave);
+      const float mo = xor_partner<OFF>(m[i]);
+      const float lo = xor_partner<OFF>(l[i]);
       const float mn = fmaxf(m[i], mo);
       const float al = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
       const float bo = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
       l[i] = l[i] * al + lo * bo;
 #pragma unroll
       for (int v = 0; v < VE; ++v) {
-        const float ao = __shfl_xor(acc[i][v], off, kWave);
+        const float ao = xor_partner<OFF>(acc[i][v]);
         acc[i][v] = acc[i][v] * al + ao * bo;
       }
       m[i] = mn;
     }
-  }
+  };
+  if constexpr (LPE <= 8) merge_groups(std::integral_constant<int, 8>{});
+  if constexpr (LPE <= 16) merge_groups(std::integral_constant<int, 16>{});
+  if constexpr (LPE <= 32) merge_groups(std::integral_constant<int, 32>{});
 
   // Merge the waves through LDS: per wave and head, acc[D] then (m, l).
   float* s_w = reinterpret_cast<float*>(smem);
