@@ -416,7 +416,8 @@ sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F,
  *  workspace  at least sv_prefill_attend_retrieve_workspace(...) bytes,
  *             256-byte aligned; no zero-fill needed.
  * Supported: dtype SV_BF16; D in {64, 128}; Hq % Hkv == 0;
- * Tq * Hq / Hkv <= 2^20.
+ * Tq * Hq / Hkv <= 2^20; (N + 32) * vis_tstride and (Tmax + 32) * txt_tstride
+ * elements below 2^30 (one sequence's cache under 2 GiB).
  * Errors: SV_EINVAL (bad sizes or k, NULL required pointer, strides smaller
  * than a row or not multiples of 8 elements, misalignment),
  * SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.

@@ -606,6 +606,9 @@ sv_status sv_prefill_attend_retrieve(const void* q, int B, int Tq, int Hq, const
     return fail(SV_EINVAL, "%s: q and caches must be 16-byte aligned", fn);
   if ((int64_t)Tq * (Hq / Hkv) > (1 << 20))
     return fail(SV_EUNSUPPORTED, "%s: Tq * Hq / Hkv query rows per KV head above 2^20", fn);
+  if (((int64_t)N + 32) * vis_tstride * 2 >= (1LL << 31) ||
+      ((int64_t)Tmax + 32) * txt_tstride * 2 >= (1LL << 31))
+    return fail(SV_EUNSUPPORTED, "%s: one sequence's visual or text cache spans 2 GiB or more", fn);
   const sv::PrefillPlan p = sv::prefill_plan(B, Tq, Hq, Hkv, N, Tmax);
   if ((int64_t)B * Hkv * p.RC * (p.CV + p.CT) > 2147483647LL ||
       (int64_t)B * Hkv * p.RC * p.W * 32 > 2147483647LL)
@@ -641,6 +644,7 @@ sv_status sv_prefill_attend_retrieve(const void* q, int B, int Tq, int Hq, const
   a.CV = p.CV;
   a.CT = p.CT;
   a.NP = p.NP;
+  a.KW = p.KW;
   a.part = (float*)ws;
   ws += align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float));
   a.pscore = (float*)ws;

@@ -9,8 +9,11 @@ namespace sv {
 // Work plan: rows = Tq * G query rows per KV head, W waves of 32 rows per
 // workgroup, RC row chunks of 32 W rows, key splits of E keys (CV visual, CT
 // text), NP = Hkv * RC * W partial retrieval scores per token.
+// KW > 1 (rows <= 32): one 32-row block per item and KW waves that split the
+// item's keys; the CV splits of E keys run over the sequence's keys in one
+// list (visual, then text), CT = 0.
 struct PrefillPlan {
-  int rows, W, RC, E, CV, CT, NP;
+  int rows, W, RC, E, CV, CT, NP, KW;
 };
 PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax);
 size_t prefill_part_floats(int B, int Hkv, int D, const PrefillPlan& p);
@@ -23,7 +26,7 @@ struct PrefillArgs {
   const int32_t* txt_len;          // [B]
   int B, Tq, Hq, Hkv, G, D, N, Tmax;
   float c2;                        // scale * log2(e)
-  int rows, W, RC, E, CV, CT, NP;  // the plan
+  int rows, W, RC, E, CV, CT, NP, KW;  // the plan
   float* part;                     // split partials [B][Hkv][RC][C][32 W][D + 4]
   float* pscore;                   // partial retrieval scores [B][NP][N]
   float* out;                      // [B][Tq][Hq][D]

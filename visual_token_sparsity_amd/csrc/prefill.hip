@@ -30,6 +30,17 @@
 // Partials (m, l, O) of each split go to the workspace; a combine kernel
 // merges them per row by max-rescaling, and a third kernel sums the partial
 // retrieval scores in a fixed order (deterministic) before the top-k select.
+//
+// Up to 32 query rows per KV head (one row block: a short question, or few
+// query heads per KV head): four waves share the item's row block and split
+// its keys (wave w takes stages w, w + 4, ...), so an item has four waves'
+// worth of loads in flight and one partial.  Each lane loads the K fragments
+// of its key straight into registers: lane group lg holds a contiguous run of
+// D/4 dims, taken 8 per k-step (the query fragments use the same dim order,
+// which leaves the dot products unchanged).  V rows go through a private LDS
+// buffer per wave.  The splits run over the sequence's keys as one list
+// (visual, then text).  At the end the waves' (m, l, O) meet in LDS in a
+// fixed order (waves 2, 3 into 0, 1, then 1 into 0).
 #include "common.h"
 #include "prefill.h"
 
@@ -278,6 +289,289 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
   }
 }
 
+constexpr int kPfKW = 4;  // key-split waves of the one-row-block path
+
+template <int D>
+struct PfKwShape {
+  static constexpr int KS = D / 32;                          // 32-wide k-steps of Q K^T
+  static constexpr int DB = D / 16;                          // 16-dim blocks of P V
+  static constexpr int DL = D / 4;                           // dims of one lane group's run
+  static constexpr int VSTR = D * 2 + kPfVPad;               // V row stride in LDS (bytes)
+  static constexpr int VBYTES = kPfStage * VSTR;             // one wave's V stage
+  static constexpr int VPL = kPfStage * D / 8 / kWave;       // 16-byte V chunks per lane
+  static constexpr int MSTR = D + 4;                         // floats per row of a merge slot
+  static constexpr int MBYTES = kPfRowsPerWave * MSTR * 4;   // one merge slot
+  static constexpr int QBYTES = 2 * KS * kWave * 16;          // Q^T fragments of the row block
+  static constexpr int LDS = (kPfKW * VBYTES > 2 * MBYTES ? kPfKW * VBYTES : 2 * MBYTES) + QBYTES;
+  static_assert(VPL * kWave * 8 == kPfStage * D, "V stage split evenly over a wave");
+};
+
+template <int D>
+__global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(PrefillArgs a) {
+  using S = PfKwShape<D>;
+  constexpr int KS = S::KS, DB = S::DB, DL = S::DL;
+  __shared__ __align__(16) char lds[S::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const int C = a.CV;
+
+  int x = blockIdx.x;
+  const int c = x % C;
+  x /= C;
+  const int g = x % a.Hkv;
+  const int b = x / a.Hkv;
+
+  int tl = a.txt_len ? a.txt_len[b] : 0;
+  tl = tl < 0 ? 0 : (tl > a.Tmax ? a.Tmax : tl);
+  const int N = a.N;
+  // Keys of the sequence as one list: e < N visual tokens, N <= e < Np
+  // padding (masked), e >= Np text rows e - Np; Np = N rounded up to a stage,
+  // so every stage is all visual or all text.
+  const int Np = (N + kPfStage - 1) / kPfStage * kPfStage;
+  const int e0 = c * a.E;
+  int e1 = e0 + a.E;
+  e1 = e1 < Np + tl ? e1 : Np + tl;
+  const int nkeys = e1 > e0 ? e1 - e0 : 0;
+  const int nst = (nkeys + kPfStage - 1) / kPfStage;
+
+  // Q^T fragments of the row block (rows li and 16 + li) in LDS, shared by
+  // the waves, in the lanes' dim order (fragment (rb, s) of lane l at
+  // ((rb * KS + s) * 64 + l) * 16 bytes); the text position of each of this
+  // lane's rows.
+  char* qbuf = lds + S::LDS - S::QBYTES;
+  int pos[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = 16 * rb + li;
+    const bool ok = row < a.rows;
+    const int tau = ok ? row / a.G : 0, hh = ok ? row - tau * a.G : 0;
+    pos[rb] = ok ? tl - a.Tq + tau : -1;
+    const bf16_t* qr = a.q + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + lg * DL;
+    for (int s = wave; s < KS; s += kPfKW) {
+      const uint4 u = ok ? *reinterpret_cast<const uint4*>(qr + 8 * s) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(qbuf + ((rb * KS + s) * kWave + lane) * 16) = u;
+    }
+  }
+  __syncthreads();
+  auto qfrag = [&](int rb, int s) {
+    return *reinterpret_cast<const bf16x8_t*>(qbuf + ((rb * KS + s) * kWave + lane) * 16);
+  };
+
+  // Each cache of (b, g) as one buffer: rows past the cache (and past the
+  // text length) read as zeros, the rows of other splits are read and masked.
+  const BufRsrc rkv = make_rsrc(a.kv + (int64_t)b * a.vbs + g * D,
+                                (uint32_t)((int64_t)(N - 1) * a.vts * 2 + D * 2));
+  const BufRsrc rvv = make_rsrc(a.vv + (int64_t)b * a.vbs + g * D,
+                                (uint32_t)((int64_t)(N - 1) * a.vts * 2 + D * 2));
+  const uint32_t text_ext = tl > 0 ? (uint32_t)((int64_t)(tl - 1) * a.tts * 2 + D * 2) : 0u;
+  const BufRsrc rkt = make_rsrc(tl > 0 ? a.kt + (int64_t)b * a.tbs + g * D : a.kv, text_ext);
+  const BufRsrc rvt = make_rsrc(tl > 0 ? a.vt + (int64_t)b * a.tbs + g * D : a.vv, text_ext);
+  // K fragments of stage st: tile t, step s -> key 16 t + li, dims lg*DL + 8 s.
+  // V chunk i of a lane: key (64 i + lane) / (D / 8), 16 bytes at dim
+  // 8 ((64 i + lane) % (D / 8)).
+  constexpr int VKPI = kWave / (D / 8);  // V keys per chunk index
+  u32x4 kr[2][KS];
+  u32x4 vr[S::VPL];
+  struct StageSrc {
+    BufRsrc rk, rv;
+    uint32_t rs, row0;
+  };
+  auto stage_src = [&](int st) {
+    const int ks = e0 + st * kPfStage;  // uniform
+    const bool vis = ks < Np;
+    return StageSrc{vis ? rkv : rkt, vis ? rvv : rvt, (uint32_t)((vis ? a.vts : a.tts) * 2),
+                    (uint32_t)(vis ? ks : ks - Np)};
+  };
+  auto load_k = [&](int st) {
+    const StageSrc ss = stage_src(st);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t vo = (ss.row0 + 16 * t + li) * ss.rs + lg * DL * 2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kr[t][s] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rk, vo + 16 * s, 0, kCacheStream));
+    }
+  };
+  auto load_v = [&](int st) {
+    const StageSrc ss = stage_src(st);
+    const uint32_t vo = (ss.row0 + lane / (D / 8)) * ss.rs + (lane % (D / 8)) * 16;
+#pragma unroll
+    for (int i = 0; i < S::VPL; ++i)
+      vr[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rv, vo, i * VKPI * ss.rs, kCacheStream));
+  };
+  char* vbuf = lds + wave * S::VBYTES;
+
+  float m[2], l[2];
+  f32x4_t acc[2][DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float* pscore = a.pscore + ((int64_t)b * a.NP + g) * N;
+
+  if (wave < nst) {
+    load_k(wave);
+    load_v(wave);
+  }
+  for (int st = wave; st < nst; st += kPfKW) {
+    // This stage's V rows to the wave's own LDS buffer (its reads of the
+    // previous stage were issued before these writes), then the next V
+    // stage's loads; the next K stage's loads go out once this stage's
+    // logits are done.
+    const bool more = st + kPfKW < nst;
+#pragma unroll
+    for (int i = 0; i < S::VPL; ++i) {
+      const int ch = i * kWave + lane;
+      const int key = ch / (D / 8), d8 = ch - key * (D / 8);
+      *reinterpret_cast<u32x4*>(vbuf + key * S::VSTR + d8 * 16) = vr[i];
+    }
+    if (more) load_v(st + kPfKW);
+    f32x4_t Sall[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[t][s]),
+                                                      qfrag(rb, s), z, 0, 0, 0);
+        Sall[t][rb] = z;  // Sall[t][rb][r] = S[row 16 rb + li][key 16 t + 4 lg + r]
+      }
+    if (more) load_k(st + kPfKW);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x4_t* St = Sall[t];
+      const int kb = st * kPfStage + 16 * t + 4 * lg;  // split-relative key of r = 0
+      if (e0 + kb < N) {
+        // Retrieval: raw logits of each visual key summed over the row block.
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = row16_add(St[0][r] + St[1][r]);
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb + r < nkeys && e0 + kb + r < N) pscore[e0 + kb + r] = sc[r];
+        }
+      }
+      s16x4 ph[2], pl[2];
+      float al[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float xv[4], tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int k = kb + r, e = e0 + k;
+          const bool ok = k < nkeys && (e < N || (e >= Np && e - Np <= pos[rb]));
+          xv[r] = ok ? St[rb][r] * a.c2 : -INFINITY;
+          tmax = fmaxf(tmax, xv[r]);
+        }
+        tmax = fmaxf(tmax, xor_partner<16>(tmax));
+        tmax = fmaxf(tmax, xor_partner<32>(tmax));
+        const float mn = fmaxf(m[rb], tmax);
+        al[rb] = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = xv[r] == -INFINITY ? 0.f : fast_exp2(xv[r] - mn);
+          ps += p[r];
+        }
+        l[rb] = l[rb] * al[rb] + ps;
+        m[rb] = mn;
+        // Rescale the output rows whose maximum rose (rare after the first
+        // tiles; the branch is taken by the whole wave or not at all).
+        if (__builtin_amdgcn_ballot_w64(al[rb] != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[rb][db] *= al[rb];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t h = bf16_rne(p[r]);
+          ph[rb][r] = (short)h;
+          pl[rb][r] = (short)bf16_rne(p[r] - __uint_as_float((uint32_t)h << 16));
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int vkey = 16 * t + 4 * lg + (li >> 2);
+        const char* va = vbuf + vkey * S::VSTR + (16 * db + 4 * (li & 3)) * 2;
+        const s16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4_t o = acc[rb][db];
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, ph[rb], o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl[rb], o, 0, 0, 0);
+          acc[rb][db] = o;  // acc[rb][db][r] = O[row 16 rb + li][dim 16 db + 4 lg + r]
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    l[rb] += xor_partner<16>(l[rb]);
+    l[rb] += xor_partner<32>(l[rb]);
+  }
+
+  // Merge the waves: slot rows [32][D + 4] = O, m, l.
+  auto slot = [&](int i) { return reinterpret_cast<float*>(lds) + i * kPfRowsPerWave * S::MSTR; };
+  auto put = [&](int i) {
+    float* sp = slot(i);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float* pr = sp + (16 * rb + li) * S::MSTR;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
+      if (lg == 0) {
+        pr[D] = m[rb];
+        pr[D + 1] = l[rb];
+      }
+    }
+  };
+  auto take = [&](int i) {
+    const float* sp = slot(i);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float* pr = sp + (16 * rb + li) * S::MSTR;
+      const float mo = pr[D], lo = pr[D + 1];
+      const float mn = fmaxf(m[rb], mo);
+      const float al = m[rb] == -INFINITY ? 0.f : fast_exp2(m[rb] - mn);
+      const float bo = mo == -INFINITY ? 0.f : fast_exp2(mo - mn);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[rb][db] = acc[rb][db] * al + *reinterpret_cast<const f32x4_t*>(pr + 16 * db + 4 * lg) * bo;
+      l[rb] = l[rb] * al + lo * bo;
+      m[rb] = mn;
+    }
+  };
+  __syncthreads();  // every wave is past its V buffer
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave != 0) return;
+  take(0);
+  float* part = a.part + ((int64_t)(b * a.Hkv + g) * C + c) * kPfRowsPerWave * (D + 4);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float* pr = part + (int64_t)(16 * rb + li) * (D + 4);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
+    if (lg == 0) {
+      pr[D] = m[rb];
+      pr[D + 1] = l[rb];
+    }
+  }
+}
+
 // Merge the C splits of every row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
 template <int D>
 __global__ __launch_bounds__(D) void prefill_combine_kernel(PrefillArgs a) {
@@ -323,12 +617,15 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillArgs a, floa
 template <int D>
 hipError_t prefill_go(const PrefillArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.B * a.Hkv * a.RC * (a.CV + a.CT);
-  switch (a.W) {
-    case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), dim3((unsigned)items), dim3(kWave), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), dim3((unsigned)items), dim3(2 * kWave), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), dim3((unsigned)items), dim3(4 * kWave), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.KW > 1)
+    hipLaunchKernelGGL((prefill_attn_kw_kernel<D>), dim3((unsigned)items), dim3(kPfKW * kWave), 0,
+                       st, a);
+  else if (a.W == 2)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), dim3((unsigned)items), dim3(2 * kWave), 0, st, a);
+  else if (a.W == 4)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), dim3((unsigned)items), dim3(4 * kWave), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.Hkv * a.RC * a.W * kPfRowsPerWave;
@@ -341,7 +638,26 @@ hipError_t prefill_go(const PrefillArgs& a, hipStream_t st) {
 PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax) {
   PrefillPlan p{};
   p.rows = Tq * (Hq / Hkv);
-  p.W = p.rows <= 32 ? 1 : (p.rows <= 64 ? 2 : 4);
+  if (p.rows <= kPfRowsPerWave) {
+    // About 512 items (two per compute unit), splits of whole stages per wave.
+    p.W = 1;
+    p.RC = 1;
+    p.KW = kPfKW;
+    const int64_t heads = (int64_t)B * Hkv;
+    int64_t C = (512 + heads / 2) / heads;
+    if (C < 1) C = 1;
+    const int64_t tot = ((int64_t)N + kPfStage - 1) / kPfStage * kPfStage + Tmax;  // visual keys padded to a stage, then text
+    const int64_t unit = (int64_t)kPfKW * kPfStage;
+    int64_t E = (tot + C - 1) / C;
+    E = (E + unit - 1) / unit * unit;
+    p.E = (int)E;
+    p.CV = (int)((tot + E - 1) / E);
+    p.CT = 0;
+    p.NP = Hkv;
+    return p;
+  }
+  p.KW = 1;
+  p.W = p.rows <= 64 ? 2 : 4;
   p.RC = (p.rows + p.W * kPfRowsPerWave - 1) / (p.W * kPfRowsPerWave);
   const int64_t heads = (int64_t)B * Hkv * p.RC;
   const int64_t ctarget = heads >= 512 ? 1 : (512 + heads - 1) / heads;
