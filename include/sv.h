@@ -414,7 +414,12 @@ sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F,
  *  idx_out    [B][k] int32, ascending (may be NULL if k == 0).
  *  scores_out optional [B][N] fp32 retrieval scores (NULL: workspace).
  *  workspace  at least sv_prefill_attend_retrieve_workspace(...) bytes,
- *             256-byte aligned; no zero-fill needed.
+ *             256-byte aligned, ZERO-FILLED before its first use.  It holds
+ *             one completion counter per sequence (the last workgroup of a
+ *             sequence runs its retrieval), the split partials and the
+ *             partial scores; every call returns the counters to zero, so
+ *             the workspace can be reused without clearing.  Two calls that
+ *             share a workspace must not run concurrently.
  * Supported: dtype SV_BF16; D in {64, 128}; Hq % Hkv == 0;
  * Tq * Hq / Hkv <= 2^20; (N + 32) * vis_tstride and (Tmax + 32) * txt_tstride
  * elements below 2^30 (one sequence's cache under 2 GiB).

@@ -566,12 +566,16 @@ sv_status sv_summary_salience_prune(const void* vis_q, const void* vis_k, int F,
 }
 
 // ---------------------------------------------------------------- prefill attention + retrieval
-// Workspace: [split partials][partial retrieval scores B*NP*N][scores B*N].
+// Workspace: [completion counters 2B lines][long-row select (rows of more
+// than 2048 tokens)][split partials][partial retrieval scores B*NP*N]
+// [scores B*N].
 size_t sv_prefill_attend_retrieve_workspace(int B, int Tq, int Hq, int Hkv, int D, int N,
                                             int Tmax) {
   if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || N < 1 || Tmax < 0) return 256;
   const sv::PrefillPlan p = sv::prefill_plan(B, Tq, Hq, Hkv, N, Tmax);
-  return align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float)) +
+  return align256((size_t)2 * B * sv::kCtrStride * sizeof(uint32_t)) +
+         sv::prefill_long_select_bytes(B, N) +
+         align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float)) +
          align256((size_t)B * p.NP * N * sizeof(float)) + align256((size_t)B * N * sizeof(float));
 }
 
@@ -645,11 +649,18 @@ sv_status sv_prefill_attend_retrieve(const void* q, int B, int Tq, int Hq, const
   a.CT = p.CT;
   a.NP = p.NP;
   a.KW = p.KW;
+  a.ctl = (uint32_t*)ws;
+  ws += align256((size_t)2 * B * sv::kCtrStride * sizeof(uint32_t));
+  a.long_ws = sv::prefill_long_select_bytes(B, N) ? ws : nullptr;
+  ws += sv::prefill_long_select_bytes(B, N);
   a.part = (float*)ws;
   ws += align256(sv::prefill_part_floats(B, Hkv, D, p) * sizeof(float));
   a.pscore = (float*)ws;
   ws += align256((size_t)B * p.NP * N * sizeof(float));
   a.out = out;
   float* scores = scores_out ? scores_out : (float*)ws;
+  a.scores = scores;
+  a.k = k;
+  a.idx = idx_out;
   return hip_status(sv::launch_prefill(a, scores, k, idx_out, (hipStream_t)stream), fn);
 }

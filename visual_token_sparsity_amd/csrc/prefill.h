@@ -30,7 +30,17 @@ struct PrefillArgs {
   float* part;                     // split partials [B][Hkv][RC][C][32 W][D + 4]
   float* pscore;                   // partial retrieval scores [B][NP][N]
   float* out;                      // [B][Tq][Hq][D]
+  float* scores;                   // [B][N] retrieval scores
+  int k;                           // tokens selected per sequence (0: none)
+  int32_t* idx;                    // [B][k]
+  uint32_t* ctl;                   // [2B] completion counters (stride kCtrStride), zero between calls
+  void* long_ws;                   // rows of more than 2048 tokens: the parallel select's
+                                   // workspace (prefill_long_select_bytes), else null
 };
+
+// Workspace of the parallel select of rows of more than 2048 tokens (0 for
+// shorter rows); zero between calls.
+size_t prefill_long_select_bytes(int B, int N);
 
 // Attention + combine, retrieval scores into `scores` [B][N], then (k > 0)
 // the top-k per sequence into idx [B][k].

@@ -32,16 +32,25 @@
 // retrieval scores in a fixed order (deterministic) before the top-k select.
 //
 // Up to 32 query rows per KV head (one row block: a short question, or few
-// query heads per KV head): four waves share the item's row block and split
-// its keys (wave w takes stages w, w + 4, ...), so an item has four waves'
-// worth of loads in flight and one partial.  Each lane loads the K fragments
-// of its key straight into registers: lane group lg holds a contiguous run of
-// D/4 dims, taken 8 per k-step (the query fragments use the same dim order,
-// which leaves the dot products unchanged).  V rows go through a private LDS
-// buffer per wave.  The splits run over the sequence's keys as one list
+// query heads per KV head): eight waves share the item's row block and split
+// its keys (wave w takes stages w, w + 8, ...), so an item has eight waves'
+// worth of loads in flight and one partial.  K fragments go from memory
+// straight into registers; V rows go through a private LDS buffer per wave.  The splits run over the sequence's keys as one list
 // (visual, then text).  At the end the waves' (m, l, O) meet in LDS in a
-// fixed order (waves 2, 3 into 0, 1, then 1 into 0).
+// fixed order (halving: waves 4..7 into 0..3, 2, 3 into 0, 1, then 1 into 0).
+// With one split per (b, g) the item writes the normalised output itself.
+// The last item of a sequence to finish (a completion counter) sums the
+// partial retrieval scores of its sequence in a fixed order and selects the
+// top k, so no further launch is needed for the retrieval.
+//
+// Rows of more than 2048 visual tokens are selected by many workgroups
+// instead (the parallel select of long_select.h, one launch after the
+// attention): sum items add up the partial scores of one 2048-token chunk
+// each (same fixed order) and histogram their top key digits, then the
+// candidate, threshold and compaction items of the decode path run on the
+// summed row.
 #include "common.h"
+#include "long_select.h"
 #include "prefill.h"
 
 namespace sv {
@@ -289,27 +298,83 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
   }
 }
 
-constexpr int kPfKW = 4;  // key-split waves of the one-row-block path
+constexpr int kPfKW = 8;  // key-split waves of the one-row-block path
+
+// Retrieval of sequence b by one workgroup of NW waves once every partial
+// score row of b is written: s[t] = sum_j pscore[b][j][t] (j = 0..NP-1 in
+// order), stored to the scores row, then the top-k of the row into idx[b].
+template <int NW, int KPT>
+__device__ __forceinline__ void select_sequence(const PrefillArgs& a, int b, char* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int N = a.N;
+  const float* ps = a.pscore + (int64_t)b * a.NP * N;
+  float* srow = a.scores + (int64_t)b * N;
+  // The select's element layout: wave w owns [w*seg, (w+1)*seg), lane l
+  // elements w*seg + 64 i + l.
+  const int seg = ((N + NW * kWave - 1) / (NW * kWave)) * kWave;
+  const int chunks = seg / kWave;
+  const int base = wave * seg + lane;
+  uint32_t key[KPT];
+  for (int i0 = 0; i0 < chunks; i0 += KPT) {
+    float sum[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) sum[i] = 0.f;
+    for (int j0 = 0; j0 < a.NP; j0 += 8) {
+      float v[8][KPT];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          const int e = base + (i0 + i) * kWave;
+          v[j][i] = (j0 + j < a.NP && i0 + i < chunks && e < N)
+                        ? load_shared_dev(ps + (int64_t)(j0 + j) * N + e) : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) sum[i] += v[j][i];
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = base + (i0 + i) * kWave;
+      if (i0 + i < chunks && e < N) store_shared_dev(srow + e, sum[i]);
+      if (i0 == 0) key[i] = float_key(sum[i]);
+    }
+  }
+  SelectSmem<NW>& sm = *reinterpret_cast<SelectSmem<NW>*>(smem);
+  int32_t* out = a.idx + (int64_t)b * a.k;
+  if (chunks <= KPT) {
+    block_topk<NW, KPT, false, true>(nullptr, N, a.k, out, sm, key);
+  } else {
+    wait_stores_complete();  // the row just stored is read back by the select's passes
+    __syncthreads();
+    block_topk<NW, KPT, true, false>(srow, N, a.k, out, sm);
+  }
+}
 
 template <int D>
 struct PfKwShape {
   static constexpr int KS = D / 32;                          // 32-wide k-steps of Q K^T
   static constexpr int DB = D / 16;                          // 16-dim blocks of P V
-  static constexpr int DL = D / 4;                           // dims of one lane group's run
   static constexpr int VSTR = D * 2 + kPfVPad;               // V row stride in LDS (bytes)
   static constexpr int VBYTES = kPfStage * VSTR;             // one wave's V stage
   static constexpr int VPL = kPfStage * D / 8 / kWave;       // 16-byte V chunks per lane
   static constexpr int MSTR = D + 4;                         // floats per row of a merge slot
   static constexpr int MBYTES = kPfRowsPerWave * MSTR * 4;   // one merge slot
   static constexpr int QBYTES = 2 * KS * kWave * 16;          // Q^T fragments of the row block
-  static constexpr int LDS = (kPfKW * VBYTES > 2 * MBYTES ? kPfKW * VBYTES : 2 * MBYTES) + QBYTES;
+  static constexpr int SBYTES = sizeof(SelectSmem<kPfKW>);
+  static constexpr int MAIN0 = kPfKW * VBYTES > kPfKW / 2 * MBYTES ? kPfKW * VBYTES : kPfKW / 2 * MBYTES;
+  static constexpr int MAIN = MAIN0 > SBYTES ? MAIN0 : SBYTES;  // V buffers, merge slots, select
+  static constexpr int LDS = MAIN + QBYTES;
+  static constexpr int SKPT = 4;  // keys per thread kept in registers by the select (rows <= 2048)
   static_assert(VPL * kWave * 8 == kPfStage * D, "V stage split evenly over a wave");
 };
 
 template <int D>
 __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(PrefillArgs a) {
   using S = PfKwShape<D>;
-  constexpr int KS = S::KS, DB = S::DB, DL = S::DL;
+  constexpr int KS = S::KS, DB = S::DB;
   __shared__ __align__(16) char lds[S::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -347,9 +412,9 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
     const bool ok = row < a.rows;
     const int tau = ok ? row / a.G : 0, hh = ok ? row - tau * a.G : 0;
     pos[rb] = ok ? tl - a.Tq + tau : -1;
-    const bf16_t* qr = a.q + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + lg * DL;
+    const bf16_t* qr = a.q + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + 8 * lg;
     for (int s = wave; s < KS; s += kPfKW) {
-      const uint4 u = ok ? *reinterpret_cast<const uint4*>(qr + 8 * s) : make_uint4(0, 0, 0, 0);
+      const uint4 u = ok ? *reinterpret_cast<const uint4*>(qr + 32 * s) : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(qbuf + ((rb * KS + s) * kWave + lane) * 16) = u;
     }
   }
@@ -367,7 +432,8 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
   const uint32_t text_ext = tl > 0 ? (uint32_t)((int64_t)(tl - 1) * a.tts * 2 + D * 2) : 0u;
   const BufRsrc rkt = make_rsrc(tl > 0 ? a.kt + (int64_t)b * a.tbs + g * D : a.kv, text_ext);
   const BufRsrc rvt = make_rsrc(tl > 0 ? a.vt + (int64_t)b * a.tbs + g * D : a.vv, text_ext);
-  // K fragments of stage st: tile t, step s -> key 16 t + li, dims lg*DL + 8 s.
+  // K fragments of stage st: tile t, step s -> key 16 t + li, dims 32 s + 8 lg
+  // (each load: 64 contiguous bytes of each of 16 rows).
   // V chunk i of a lane: key (64 i + lane) / (D / 8), 16 bytes at dim
   // 8 ((64 i + lane) % (D / 8)).
   constexpr int VKPI = kWave / (D / 8);  // V keys per chunk index
@@ -387,11 +453,11 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
     const StageSrc ss = stage_src(st);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t vo = (ss.row0 + 16 * t + li) * ss.rs + lg * DL * 2;
+      const uint32_t vo = (ss.row0 + 16 * t + li) * ss.rs + lg * 16;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         kr[t][s] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rk, vo + 16 * s, 0, kCacheStream));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rk, vo + 64 * s, 0, kCacheStream));
     }
   };
   auto load_v = [&](int st) {
@@ -457,7 +523,7 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
         if (li == 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (kb + r < nkeys && e0 + kb + r < N) pscore[e0 + kb + r] = sc[r];
+            if (kb + r < nkeys && e0 + kb + r < N) store_shared_dev(pscore + e0 + kb + r, sc[r]);
         }
       }
       s16x4 ph[2], pl[2];
@@ -550,26 +616,161 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
       m[rb] = mn;
     }
   };
-  __syncthreads();  // every wave is past its V buffer
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave != 0) return;
-  take(0);
-  float* part = a.part + ((int64_t)(b * a.Hkv + g) * C + c) * kPfRowsPerWave * (D + 4);
+  // Halving merge: waves [h, 2h) put, waves [0, h) take (fixed order).
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float* pr = part + (int64_t)(16 * rb + li) * (D + 4);
+  for (int h = kPfKW / 2; h >= 1; h /= 2) {
+    __syncthreads();  // every wave is past its V buffer / the previous level
+    if (wave >= h && wave < 2 * h) put(wave - h);
+    __syncthreads();
+    if (wave < h) take(wave);
+  }
+  if (wave == 0) {
+    if (C == 1) {
+      // The only split: normalised output rows.
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
-    if (lg == 0) {
-      pr[D] = m[rb];
-      pr[D + 1] = l[rb];
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = 16 * rb + li;
+        if (row < a.rows) {
+          const int tau = row / a.G, hh = row - tau * a.G;
+          float* o = a.out + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D;
+          const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<f32x4_t*>(o + 16 * db + 4 * lg) = acc[rb][db] * inv;
+        }
+      }
+    } else {
+      float* part = a.part + ((int64_t)(b * a.Hkv + g) * C + c) * kPfRowsPerWave * (D + 4);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float* pr = part + (int64_t)(16 * rb + li) * (D + 4);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
+        if (lg == 0) {
+          pr[D] = m[rb];
+          pr[D + 1] = l[rb];
+        }
+      }
     }
   }
+  if (a.k <= 0 || a.long_ws) return;  // long rows: the parallel select runs after
+
+  // The last item of sequence b: retrieval scores and the top-k.
+  __shared__ uint32_t s_last;
+  wait_stores_complete();  // this item's partial scores are out (device-coherent)
+  __syncthreads();
+  uint32_t* ctr = a.ctl + (int64_t)b * kCtrStride;
+  if (tid == 0) s_last = counter_add(ctr, 1u) == (uint32_t)(a.Hkv * C) - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  select_sequence<kPfKW, S::SKPT>(a, b, lds);
+  if (tid == 0) counter_reset(ctr);
+}
+
+// ---------------------------------------------------------------- long rows
+// Sum item (b, p): chunk p of sequence b's scores (the element layout of
+// the long-row select: p*2048 + wave*512 + 64 i + lane), stored
+// device-coherent; their top 11 key bits go to a local histogram, flushed
+// to replica p % kLsReps of hist1; then seq_ctr[b] += 1.
+__device__ __forceinline__ void pf_sum_item(const PrefillArgs& pa, const ScanArgs& sa,
+                                            const LongSelArgs& ls, int b, int p, char* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int N = pa.N;
+  uint32_t* lh = reinterpret_cast<uint32_t*>(smem);
+  for (int i = tid; i < kLsBins; i += kItemThreads) lh[i] = 0u;
+  __syncthreads();
+  const int e0 = p * kLsChunk + wave * (kLsChunk / kItemWaves) + lane;
+  const float* ps = pa.pscore + (int64_t)b * pa.NP * N;
+  float sum[kSelKpt];
+#pragma unroll
+  for (int i = 0; i < kSelKpt; ++i) sum[i] = 0.f;
+  for (int j0 = 0; j0 < pa.NP; j0 += 4) {
+    float v[4][kSelKpt];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < kSelKpt; ++i) {
+        const int e = e0 + i * kWave;
+        v[j][i] = (j0 + j < pa.NP && e < N) ? ps[(int64_t)(j0 + j) * N + e] : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < kSelKpt; ++i) sum[i] += v[j][i];
+  }
+  float* srow = sa.scores + (int64_t)b * N;
+#pragma unroll
+  for (int i = 0; i < kSelKpt; ++i) {
+    const int e = e0 + i * kWave;
+    if (e < N) {
+      store_shared_dev(srow + e, sum[i]);
+      atomicAdd(&lh[digit1(float_key(sum[i]))], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ls.hist1 + ((int64_t)b * kLsReps + (p & (kLsReps - 1))) * kLsBins;
+  for (int i = tid; i < kLsBins; i += kItemThreads) {
+    const uint32_t v = lh[i];
+    if (v) __hip_atomic_fetch_add(gh + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_stores_complete();
+  __syncthreads();
+  if (tid == 0) counter_add(&sa.seq_ctr[b * kCtrStride], 1u);
+}
+
+// Items in phase order: B*P sum items, B*P candidate items, B threshold
+// items, B*P compaction items (each waits only on items before it).
+__global__ __launch_bounds__(kItemThreads) void prefill_long_select_kernel(PrefillArgs pa,
+                                                                           ScanArgs sa,
+                                                                           LongSelArgs ls) {
+  extern __shared__ __align__(16) char smem[];
+  const uint32_t B = (uint32_t)pa.B, P = (uint32_t)ls.P;
+  uint32_t u = blockIdx.x;
+  if (u < B * P) {
+    pf_sum_item(pa, sa, ls, u / P, u % P, smem);
+  } else if ((u -= B * P) < B * P) {
+    cand_item(sa, ls, u / P, u % P, smem);
+  } else if ((u -= B * P) < B) {
+    thr_item(sa, ls, u, smem);
+  } else {
+    u -= B;
+    compact_item(sa, ls, u / P, u % P, smem);
+  }
+}
+
+hipError_t launch_prefill_long_select(const PrefillArgs& a, hipStream_t st) {
+  const int P = (a.N + kLsChunk - 1) / kLsChunk;
+  char* w = static_cast<char*>(a.long_ws);
+  auto take = [&](size_t n) {
+    char* r = w;
+    w += (n + 255) & ~(size_t)255;
+    return r;
+  };
+  LongSelArgs ls{};
+  ls.P = P;
+  ls.ctl = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsCtlLines * kCtrStride * 4));
+  ls.hist1 = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsReps * kLsBins * 4));
+  ls.hist2 = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsBins * 4));
+  ls.cand = reinterpret_cast<uint64_t*>(take((size_t)a.B * kLsCandCap * 8));
+  ls.chunk_hi = reinterpret_cast<uint32_t*>(take((size_t)a.B * P * 4));
+  ls.offs = reinterpret_cast<uint32_t*>(take((size_t)a.B * P * 4));
+  ScanArgs sa{};
+  sa.N = a.N;
+  sa.k = a.k;
+  sa.idx = a.idx;
+  sa.scores = a.scores;
+  sa.items_per_seq = P;
+  sa.seq_ctr = a.ctl + (size_t)a.B * kCtrStride;
+  sa.hist1 = ls.hist1;
+  sa.spin_limit = kSpinLimit;
+  size_t lds = (size_t)kLsBins * 4;
+  if (cand_smem_bytes() > lds) lds = cand_smem_bytes();
+  if (thr_smem_bytes(P) > lds) lds = thr_smem_bytes(P);
+  if (sizeof(SelectSmem<kItemWaves>) > lds) lds = sizeof(SelectSmem<kItemWaves>);
+  const unsigned items = (unsigned)(3 * a.B * P + a.B);
+  hipLaunchKernelGGL(prefill_long_select_kernel, dim3(items), dim3(kItemThreads), lds, st, a, sa, ls);
+  return hipGetLastError();
 }
 
 // Merge the C splits of every row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
@@ -589,15 +790,32 @@ __global__ __launch_bounds__(D) void prefill_combine_kernel(PrefillArgs a) {
   const float* p = a.part + ((int64_t)(b * a.Hkv + g) * a.RC + rc) * C * RCH * (D + 4) +
                    (int64_t)rl * (D + 4);
   const int64_t cs = (int64_t)RCH * (D + 4);
-  float M = -INFINITY;
-  for (int c = 0; c < C; ++c) M = fmaxf(M, p[c * cs + D]);
-  float num = 0.f, den = 0.f;
   const int d = threadIdx.x;
-  for (int c = 0; c < C; ++c) {
-    const float mc = p[c * cs + D];
-    const float w = mc == -INFINITY ? 0.f : fast_exp2(mc - M);
-    num = fmaf(w, p[c * cs + d], num);
-    den = fmaf(w, p[c * cs + D + 1], den);
+  // Batches of 8 splits: their loads go out together.
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < C; c0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mv[j] = c0 + j < C ? p[(c0 + j) * cs + D] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);
+  }
+  float num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < C; c0 += 8) {
+    float mv[8], ov[8], lv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = c0 + j < C;
+      mv[j] = ok ? p[(c0 + j) * cs + D] : -INFINITY;
+      ov[j] = ok ? p[(c0 + j) * cs + d] : 0.f;
+      lv[j] = ok ? p[(c0 + j) * cs + D + 1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - M);
+      num = fmaf(w, ov[j], num);
+      den = fmaf(w, lv[j], den);
+    }
   }
   const int tau = row / a.G, hh = row - tau * a.G;
   a.out[(((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + d] = den > 0.f ? num / den : 0.f;
@@ -610,17 +828,29 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillArgs a, floa
   const int b = (int)(i / a.N), t = (int)(i - (int64_t)b * a.N);
   const float* p = a.pscore + (int64_t)b * a.NP * a.N + t;
   float s = 0.f;
-  for (int j = 0; j < a.NP; ++j) s += p[(int64_t)j * a.N];
+  for (int j0 = 0; j0 < a.NP; j0 += 8) {  // batches of 8 loads in flight, summed in order
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = j0 + j < a.NP ? p[(int64_t)(j0 + j) * a.N] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
   scores[i] = s;
 }
 
 template <int D>
 hipError_t prefill_go(const PrefillArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.B * a.Hkv * a.RC * (a.CV + a.CT);
-  if (a.KW > 1)
+  if (a.KW > 1) {
     hipLaunchKernelGGL((prefill_attn_kw_kernel<D>), dim3((unsigned)items), dim3(kPfKW * kWave), 0,
                        st, a);
-  else if (a.W == 2)
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.CV + a.CT == 1) return e;
+    const int64_t rows = (int64_t)a.B * a.Hkv * kPfRowsPerWave;
+    hipLaunchKernelGGL((prefill_combine_kernel<D>), dim3((unsigned)rows), dim3(D), 0, st, a);
+    return hipGetLastError();
+  }
+  if (a.W == 2)
     hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), dim3((unsigned)items), dim3(2 * kWave), 0, st, a);
   else if (a.W == 4)
     hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), dim3((unsigned)items), dim3(4 * kWave), 0, st, a);
@@ -639,12 +869,12 @@ PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax) {
   PrefillPlan p{};
   p.rows = Tq * (Hq / Hkv);
   if (p.rows <= kPfRowsPerWave) {
-    // About 512 items (two per compute unit), splits of whole stages per wave.
+    // About 256 items (one per compute unit), splits of whole stages per wave.
     p.W = 1;
     p.RC = 1;
     p.KW = kPfKW;
     const int64_t heads = (int64_t)B * Hkv;
-    int64_t C = (512 + heads / 2) / heads;
+    int64_t C = (256 + heads / 2) / heads;
     if (C < 1) C = 1;
     const int64_t tot = ((int64_t)N + kPfStage - 1) / kPfStage * kPfStage + Tmax;  // visual keys padded to a stage, then text
     const int64_t unit = (int64_t)kPfKW * kPfStage;
@@ -671,6 +901,14 @@ PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax) {
   return p;
 }
 
+size_t prefill_long_select_bytes(int B, int N) {
+  if (N <= kItemThreads * kSelKpt) return 0;
+  const size_t P = (size_t)(N + kLsChunk - 1) / kLsChunk;
+  auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  return al((size_t)B * kLsCtlLines * kCtrStride * 4) + al((size_t)B * kLsReps * kLsBins * 4) +
+         al((size_t)B * kLsBins * 4) + al((size_t)B * kLsCandCap * 8) + 2 * al((size_t)B * P * 4);
+}
+
 size_t prefill_part_floats(int B, int Hkv, int D, const PrefillPlan& p) {
   return (size_t)B * Hkv * p.RC * (p.CV + p.CT) * p.W * kPfRowsPerWave * (D + 4);
 }
@@ -679,6 +917,8 @@ hipError_t launch_prefill(const PrefillArgs& a, float* scores, int k, int32_t* i
                           hipStream_t st) {
   hipError_t e = a.D == 128 ? prefill_go<128>(a, st) : prefill_go<64>(a, st);
   if (e != hipSuccess) return e;
+  if (a.long_ws) return k > 0 ? launch_prefill_long_select(a, st) : hipSuccess;
+  if (a.KW > 1) return e;  // the key-split path selects in the attention launch
   const int64_t n = (int64_t)a.B * a.N;
   hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a,
                      scores);
