@@ -25,6 +25,15 @@
 // softmax runs in base 2 on a query pre-scaled by scale*log2(e).  Partials
 // (m, l, acc) go out with device-coherent stores; the last split of (b, g) to
 // arrive merges them by max-rescaling and writes the output.
+//
+// bf16 caches with G >= 2 query heads per KV head take matrix cores instead:
+// a wave owns tiles of 16 entries; S^T = K Q^T (v_mfma_f32_16x16x32_bf16, the
+// G query heads as columns of a 16-wide B operand; each lane loads 16-byte
+// slices of one entry's K row straight into the A operand), an online softmax
+// per head column, then O^T += V^T P^T (v_mfma_f32_16x16x16_bf16 with P^T as
+// a bf16 high part plus the bf16 residual, so the product keeps fp32 accuracy;
+// V^T comes from the tile's V rows staged in the wave's LDS buffer and read
+// with ds_read_tr16_b64).  The same splits, partials and combine.
 #pragma once
 
 #include <type_traits>
@@ -432,11 +441,18 @@ struct AttnShape {
 // combine for the weights and l of up to kMaxCombineSplits splits per head,
 // G denominators and one float4 per thread.
 constexpr int kMaxCombineSplits = 256;
+constexpr int kAttnVPad = 32;  // bytes of padding per V row in the MFMA item's LDS buffer
+template <int D>
+__host__ __device__ constexpr size_t attn_mfma_vbuf_bytes() {
+  return (size_t)16 * (2 * D + kAttnVPad);  // one 16-entry tile of V rows (bf16)
+}
 template <int D, int G>
 __host__ __device__ constexpr size_t attn_smem_bytes() {
   const size_t w = (size_t)kItemWaves * G * (D + 2);
   const size_t c = (size_t)G * kMaxCombineSplits * 2 + 8 + (size_t)kItemThreads * 4;
-  return (w > c ? w : c) * sizeof(float);
+  const size_t f = (w > c ? w : c) * sizeof(float);
+  const size_t v = G >= 2 ? kItemWaves * attn_mfma_vbuf_bytes<D>() : 0;  // bf16 matrix-core item
+  return f > v ? f : v;
 }
 
 // Float4 columns of the combine and the number of thread groups that split
@@ -447,6 +463,195 @@ __host__ __device__ constexpr int combine_groups() {
   int s = 1;
   while (s < 16 && 2 * s * V <= kItemThreads) s *= 2;
   return s;
+}
+
+typedef __attribute__((ext_vector_type(8))) __bf16 attn_bf16x8;
+typedef __attribute__((ext_vector_type(4))) float attn_f32x4;
+typedef short attn_s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t attn_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Matrix-core front of a bf16 item with G >= 2 (see the header): entries
+// [e0, e0 + n_ent) of the split, SE of them at most; writes each wave's
+// (acc, m, l) per head into its LDS slot slot(w, i) = smem + (w*G + i)*(D+2)
+// floats, as the vector front does.
+template <int D, int G, int SE>
+__device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g, bool text,
+                                                int e0, int n_ent, bool wait, char* smem) {
+  static_assert(G >= 2 && G <= 16, "query heads as the columns of one 16-wide tile");
+  constexpr int KS = D / 32, DB = D / 16;
+  constexpr int TPW = (SE + 16 * kItemWaves - 1) / (16 * kItemWaves);  // tiles per wave
+  constexpr int VSTR = 2 * D + kAttnVPad;
+  constexpr int VCH = D / 8;               // 16-byte chunks per V row
+  constexpr int VLD = 16 * VCH / kWave;    // V loads per lane per tile
+  constexpr int VEPL = kWave / VCH;        // entries per V load instruction
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
+
+  // Q^T (B operand): lane (li, lg) holds head g*G + li (zero past G), dims
+  // 32 s + 8 lg.
+  attn_bf16x8 qf[KS];
+  {
+    const bf16_t* qh = q + ((int64_t)b * a.Hq + g * G + (li < G ? li : 0)) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 u = li < G ? *reinterpret_cast<const uint4*>(qh + 32 * s) : make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(attn_bf16x8, u);
+    }
+  }
+
+  // The sequence's cache as one buffer (as in the vector front).
+  const int64_t ts = text ? a.tts : a.vts;
+  BufRsrc krs, vrs;
+  {
+    const int64_t rows = text ? (a.Tmax > 0 ? a.Tmax : 1) : (a.N > 0 ? a.N : 1);
+    const uint32_t ext = (uint32_t)(((int64_t)(rows - 1) * ts + (int64_t)a.Hkv * D) * 2);
+    const char* kb = reinterpret_cast<const char*>(text ? a.kt : a.kv) + (int64_t)b * (text ? a.tbs : a.vbs) * 2;
+    const char* vb = reinterpret_cast<const char*>(text ? a.vt : a.vv) + (int64_t)b * (text ? a.tbs : a.vbs) * 2;
+    krs = make_rsrc(kb, ext);
+    vrs = make_rsrc(vb, ext);
+  }
+  const uint32_t head_off = (uint32_t)(g * D * 2);
+
+  // Token of entry li of each tile (-1: none), polled when the indices come
+  // from this kernel.
+  int tok[TPW];
+  auto entry_of = [&](int tt, int r) { return (tt * kItemWaves + wave) * 16 + r; };
+  if (text) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int e = entry_of(tt, li);
+      tok[tt] = e < n_ent ? e0 + e : -1;
+    }
+  } else if (wait) {
+    const uint32_t* ib = a.idx_enc + (int64_t)b * a.k + e0;
+    for (uint32_t n = 0;; ++n) {
+      bool missing = false;
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int e = entry_of(tt, li);
+        const uint32_t w = e < n_ent ? load_flag(ib + e) : 0u;
+        tok[tt] = e < n_ent ? (int)w - 1 : -1;
+        missing |= e < n_ent && w == 0u;
+      }
+      if (!__syncthreads_or(missing)) break;
+      if (n + 1 >= a.spin_limit) {
+        if (tid == 0) report_giveup(a.status, kGiveUpIndices);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  } else {
+    const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int e = entry_of(tt, li);
+      tok[tt] = e < n_ent ? ib[e] : -1;
+    }
+  }
+  const int lim = text ? a.Tmax : a.N;  // tokens outside [0, lim) are skipped
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+    if (tok[tt] < 0 || tok[tt] >= lim) tok[tt] = -1;
+
+  // All loads in flight: K slices (A operand: entry li, dims 32 s + 8 lg)
+  // and V rows (entry VEPL*i + lane / VCH, 16 bytes at chunk lane % VCH).
+  u32x4 kr[TPW][KS], vr[TPW][VLD];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const uint32_t ko = tok[tt] >= 0 ? (uint32_t)(tok[tt] * ts * 2) + head_off + 16 * lg : kBufOob;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kr[tt][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ko + (ko == kBufOob ? 0 : 64 * s), 0, kCacheDefault));
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int vt = __shfl(tok[tt], VEPL * i + lane / VCH, kWave);
+      const uint32_t vo = vt >= 0 ? (uint32_t)(vt * ts * 2) + head_off + 16 * (lane % VCH) : kBufOob;
+      vr[tt][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, kCacheDefault));
+    }
+  }
+
+  char* vbuf = smem + wave * attn_mfma_vbuf_bytes<D>();
+  float m = -INFINITY, l = 0.f;  // head li
+  attn_f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    // Entries of this tile that count (bit r: entry r).
+    const uint32_t valid = (uint32_t)__ballot(tok[tt] >= 0) & 0xFFFFu;
+    if (!__builtin_amdgcn_readfirstlane(valid)) continue;  // uniform
+#pragma unroll
+    for (int i = 0; i < VLD; ++i)
+      *reinterpret_cast<u32x4*>(vbuf + (VEPL * i + lane / VCH) * VSTR + 16 * (lane % VCH)) = vr[tt][i];
+    attn_f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8, kr[tt][s]), qf[s], st, 0, 0, 0);
+    // st[r] = S[head li][entry 4 lg + r]
+    float x[4], tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = (valid >> (4 * lg + r)) & 1u ? st[r] * a.qscale : -INFINITY;
+      tmax = fmaxf(tmax, x[r]);
+    }
+    tmax = fmaxf(tmax, xor_partner<16>(tmax));
+    tmax = fmaxf(tmax, xor_partner<32>(tmax));
+    const float mn = fmaxf(m, tmax);
+    const float al = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = x[r] == -INFINITY ? 0.f : fast_exp2(x[r] - mn);
+      ps += pr[r];
+    }
+    l = l * al + ps;
+    m = mn;
+    if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= al;
+    }
+    attn_s16x4 ph, pl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t h = attn_bf16_rne(pr[r]);
+      ph[r] = (short)h;
+      pl[r] = (short)attn_bf16_rne(pr[r] - __uint_as_float((uint32_t)h << 16));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      // V^T fragment: lane (li, lg) gets dim 16 db + li of entries 4 lg .. 4 lg + 3.
+      const char* va = vbuf + (4 * lg + (li >> 2)) * VSTR + (16 * db + 4 * (li & 3)) * 2;
+      const attn_s16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) attn_s16x4*)(va));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, ph, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl, acc[db], 0, 0, 0);
+      // acc[db][r] = O[head li][dim 16 db + 4 lg + r]
+    }
+  }
+  l += xor_partner<16>(l);
+  l += xor_partner<32>(l);
+
+  // Slots of the vector front's cross-wave merge (the V buffers are done).
+  __syncthreads();
+  float* s_w = reinterpret_cast<float*>(smem);
+  if (li < G) {
+    float* sp = s_w + ((int64_t)wave * G + li) * (D + 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sp[16 * db + 4 * lg + r] = acc[db][r];
+    if (lg == 0) {
+      sp[D] = m;
+      sp[D + 1] = l;
+    }
+  }
 }
 
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
@@ -478,160 +683,164 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   }
   n_ent = n_ent < 0 ? 0 : (n_ent > SE ? SE : n_ent);
 
-  Vec<T> qx[G];
-#pragma unroll
-  for (int i = 0; i < G; ++i) qx[i].load(q + ((int64_t)b * a.Hq + g * G + i) * D + d0);
-
-  // The sequence's text or visual cache as one buffer; entry j of this lane
-  // is the head-g row of one token, at a 32-bit byte offset (kBufOob: none).
-  constexpr int ES = (int)sizeof(T);
-  const int64_t row_elems = (int64_t)a.Hkv * D;
-  BufRsrc krs, vrs;
-  int64_t ts;
-  if (text) {
-    ts = a.tts;
-    const uint32_t ext = (uint32_t)(((int64_t)(a.Tmax > 0 ? a.Tmax - 1 : 0) * ts + row_elems) * ES);
-    krs = make_rsrc(reinterpret_cast<const char*>(a.kt) + (int64_t)b * a.tbs * ES, ext);
-    vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + (int64_t)b * a.tbs * ES, ext);
-  } else {
-    ts = a.vts;
-    const uint32_t ext = (uint32_t)(((int64_t)(a.N > 0 ? a.N - 1 : 0) * ts + row_elems) * ES);
-    krs = make_rsrc(reinterpret_cast<const char*>(a.kv) + (int64_t)b * a.vbs * ES, ext);
-    vrs = make_rsrc(reinterpret_cast<const char*>(a.vv) + (int64_t)b * a.vbs * ES, ext);
-  }
-  const uint32_t head_off = (uint32_t)((g * D + d0) * ES);
-  uint32_t off[EPL];
-  if (text) {
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = (j * kItemWaves + wave) * EPW + eg;
-      off[j] = e < n_ent ? (uint32_t)((e0 + e) * ts * ES) + head_off : kBufOob;
-    }
-  } else {
-    int tok[EPL];
-    if (wait) {
-      // The indices are produced by this kernel: poll this split's words of
-      // the encoded copy until every one is written (bounded); the read that
-      // finds them complete is the one that loads them.
-      const uint32_t* ib = a.idx_enc + (int64_t)b * a.k + e0;
-      for (uint32_t n = 0;; ++n) {
-        bool missing = false;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          const int e = (j * kItemWaves + wave) * EPW + eg;
-          const uint32_t w = e < n_ent ? load_flag(ib + e) : 0u;
-          tok[j] = e < n_ent ? (int)w - 1 : -1;  // -1: no entry
-          missing |= e < n_ent && w == 0u;
-        }
-        if (!__syncthreads_or(missing)) break;
-        if (n + 1 >= a.spin_limit) {
-          if (tid == 0) report_giveup(a.status, kGiveUpIndices);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    } else {
-      const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = (j * kItemWaves + wave) * EPW + eg;
-        tok[j] = e < n_ent ? ib[e] : -1;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int t = tok[j];  // indices outside [0, N) are skipped
-      off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
-    }
-  }
-
-  Vec<T> kx[EPL], vx[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    kx[j].template load_buf<kCacheDefault>(krs, off[j], 0u);
-    vx[j].template load_buf<kCacheDefault>(vrs, off[j], 0u);
-  }
-
-  float qv[G][VE];
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    qx[i].to_f32(qv[i]);
-#pragma unroll
-    for (int v = 0; v < VE; ++v) qv[i][v] *= a.qscale;
-  }
-
-  float m[G], l[G], acc[G][VE];
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-#pragma unroll
-    for (int v = 0; v < VE; ++v) acc[i][v] = 0.f;
-  }
-
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    float kf[VE], vf[VE];
-    kx[j].to_f32(kf);
-    vx[j].to_f32(vf);
-    float z[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
-      z[i] = lane_group_sum<LPE>(s);
-    }
-    if (off[j] != kBufOob) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float mn = fmaxf(m[i], z[i]);
-        const float al = fast_exp2(m[i] - mn);  // m = -inf -> 0
-        const float p = fast_exp2(z[i] - mn);
-        l[i] = l[i] * al + p;
-#pragma unroll
-        for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
-        m[i] = mn;
-      }
-    }
-  }
-
-  // Merge the EPW lane groups of this wave (partner values by DPP and
-  // row-swap moves, no LDS trips).
-  auto merge_groups = [&](auto off_tag) {
-    constexpr int OFF = decltype(off_tag)::value;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float mo = xor_partner<OFF>(m[i]);
-      const float lo = xor_partner<OFF>(l[i]);
-      const float mn = fmaxf(m[i], mo);
-      const float al = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
-      const float bo = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
-      l[i] = l[i] * al + lo * bo;
-#pragma unroll
-      for (int v = 0; v < VE; ++v) {
-        const float ao = xor_partner<OFF>(acc[i][v]);
-        acc[i][v] = acc[i][v] * al + ao * bo;
-      }
-      m[i] = mn;
-    }
-  };
-  if constexpr (LPE <= 8) merge_groups(std::integral_constant<int, 8>{});
-  if constexpr (LPE <= 16) merge_groups(std::integral_constant<int, 16>{});
-  if constexpr (LPE <= 32) merge_groups(std::integral_constant<int, 32>{});
-
-  // Merge the waves through LDS: per wave and head, acc[D] then (m, l).
   float* s_w = reinterpret_cast<float*>(smem);
   auto slot = [&](int w, int i) { return s_w + ((int64_t)w * G + i) * (D + 2); };
-  if (eg == 0) {
-#pragma unroll
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value && G >= 2;
+  if constexpr (kMfma) {
+    attn_front_mfma<D, G, SE>(a, b, g, text, e0, n_ent, wait, smem);
+  } else {
+    Vec<T> qx[G];
+  #pragma unroll
+    for (int i = 0; i < G; ++i) qx[i].load(q + ((int64_t)b * a.Hq + g * G + i) * D + d0);
+
+    // The sequence's text or visual cache as one buffer; entry j of this lane
+    // is the head-g row of one token, at a 32-bit byte offset (kBufOob: none).
+    constexpr int ES = (int)sizeof(T);
+    const int64_t row_elems = (int64_t)a.Hkv * D;
+    BufRsrc krs, vrs;
+    int64_t ts;
+    if (text) {
+      ts = a.tts;
+      const uint32_t ext = (uint32_t)(((int64_t)(a.Tmax > 0 ? a.Tmax - 1 : 0) * ts + row_elems) * ES);
+      krs = make_rsrc(reinterpret_cast<const char*>(a.kt) + (int64_t)b * a.tbs * ES, ext);
+      vrs = make_rsrc(reinterpret_cast<const char*>(a.vt) + (int64_t)b * a.tbs * ES, ext);
+    } else {
+      ts = a.vts;
+      const uint32_t ext = (uint32_t)(((int64_t)(a.N > 0 ? a.N - 1 : 0) * ts + row_elems) * ES);
+      krs = make_rsrc(reinterpret_cast<const char*>(a.kv) + (int64_t)b * a.vbs * ES, ext);
+      vrs = make_rsrc(reinterpret_cast<const char*>(a.vv) + (int64_t)b * a.vbs * ES, ext);
+    }
+    const uint32_t head_off = (uint32_t)((g * D + d0) * ES);
+    uint32_t off[EPL];
+    if (text) {
+  #pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = (j * kItemWaves + wave) * EPW + eg;
+        off[j] = e < n_ent ? (uint32_t)((e0 + e) * ts * ES) + head_off : kBufOob;
+      }
+    } else {
+      int tok[EPL];
+      if (wait) {
+        // The indices are produced by this kernel: poll this split's words of
+        // the encoded copy until every one is written (bounded); the read that
+        // finds them complete is the one that loads them.
+        const uint32_t* ib = a.idx_enc + (int64_t)b * a.k + e0;
+        for (uint32_t n = 0;; ++n) {
+          bool missing = false;
+  #pragma unroll
+          for (int j = 0; j < EPL; ++j) {
+            const int e = (j * kItemWaves + wave) * EPW + eg;
+            const uint32_t w = e < n_ent ? load_flag(ib + e) : 0u;
+            tok[j] = e < n_ent ? (int)w - 1 : -1;  // -1: no entry
+            missing |= e < n_ent && w == 0u;
+          }
+          if (!__syncthreads_or(missing)) break;
+          if (n + 1 >= a.spin_limit) {
+            if (tid == 0) report_giveup(a.status, kGiveUpIndices);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      } else {
+        const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
+  #pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = (j * kItemWaves + wave) * EPW + eg;
+          tok[j] = e < n_ent ? ib[e] : -1;
+        }
+      }
+  #pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int t = tok[j];  // indices outside [0, N) are skipped
+        off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
+      }
+    }
+
+    Vec<T> kx[EPL], vx[EPL];
+  #pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      kx[j].template load_buf<kCacheDefault>(krs, off[j], 0u);
+      vx[j].template load_buf<kCacheDefault>(vrs, off[j], 0u);
+    }
+
+    float qv[G][VE];
+  #pragma unroll
     for (int i = 0; i < G; ++i) {
-      float* sp = slot(wave, i);
+      qx[i].to_f32(qv[i]);
+  #pragma unroll
+      for (int v = 0; v < VE; ++v) qv[i][v] *= a.qscale;
+    }
+
+    float m[G], l[G], acc[G][VE];
+  #pragma unroll
+    for (int i = 0; i < G; ++i) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+  #pragma unroll
+      for (int v = 0; v < VE; ++v) acc[i][v] = 0.f;
+    }
+
+  #pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      float kf[VE], vf[VE];
+      kx[j].to_f32(kf);
+      vx[j].to_f32(vf);
+      float z[G];
+  #pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float s = 0.f;
+  #pragma unroll
+        for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
+        z[i] = lane_group_sum<LPE>(s);
+      }
+      if (off[j] != kBufOob) {
+  #pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const float mn = fmaxf(m[i], z[i]);
+          const float al = fast_exp2(m[i] - mn);  // m = -inf -> 0
+          const float p = fast_exp2(z[i] - mn);
+          l[i] = l[i] * al + p;
+  #pragma unroll
+          for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
+          m[i] = mn;
+        }
+      }
+    }
+
+    // Merge the EPW lane groups of this wave (partner values by DPP and
+    // row-swap moves, no LDS trips).
+    auto merge_groups = [&](auto off_tag) {
+      constexpr int OFF = decltype(off_tag)::value;
+  #pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float mo = xor_partner<OFF>(m[i]);
+        const float lo = xor_partner<OFF>(l[i]);
+        const float mn = fmaxf(m[i], mo);
+        const float al = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
+        const float bo = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
+        l[i] = l[i] * al + lo * bo;
+  #pragma unroll
+        for (int v = 0; v < VE; ++v) {
+          const float ao = xor_partner<OFF>(acc[i][v]);
+          acc[i][v] = acc[i][v] * al + ao * bo;
+        }
+        m[i] = mn;
+      }
+    };
+    if constexpr (LPE <= 8) merge_groups(std::integral_constant<int, 8>{});
+    if constexpr (LPE <= 16) merge_groups(std::integral_constant<int, 16>{});
+    if constexpr (LPE <= 32) merge_groups(std::integral_constant<int, 32>{});
+    // Merge the waves through LDS: per wave and head, acc[D] then (m, l).
+    if (eg == 0) {
 #pragma unroll
-      for (int v = 0; v < VE; ++v) sp[d0 + v] = acc[i][v];
-      if (sub == 0) {
-        sp[D] = m[i];
-        sp[D + 1] = l[i];
+      for (int i = 0; i < G; ++i) {
+        float* sp = slot(wave, i);
+#pragma unroll
+        for (int v = 0; v < VE; ++v) sp[d0 + v] = acc[i][v];
+        if (sub == 0) {
+          sp[D] = m[i];
+          sp[D + 1] = l[i];
+        }
       }
     }
   }
