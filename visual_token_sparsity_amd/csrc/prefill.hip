@@ -791,30 +791,40 @@ __global__ __launch_bounds__(D) void prefill_combine_kernel(PrefillArgs a) {
                    (int64_t)rl * (D + 4);
   const int64_t cs = (int64_t)RCH * (D + 4);
   const int d = threadIdx.x;
-  // Batches of 8 splits: their loads go out together.
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < C; c0 += 8) {
-    float mv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mv[j] = c0 + j < C ? p[(c0 + j) * cs + D] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);
-  }
-  float num = 0.f, den = 0.f;
-  for (int c0 = 0; c0 < C; c0 += 8) {
-    float mv[8], ov[8], lv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = c0 + j < C;
-      mv[j] = ok ? p[(c0 + j) * cs + D] : -INFINITY;
-      ov[j] = ok ? p[(c0 + j) * cs + d] : 0.f;
-      lv[j] = ok ? p[(c0 + j) * cs + D + 1] : 0.f;
+  // Batches of up to kCh splits: their (m, l) pairs go to LDS in one round
+  // trip, then every thread adds its dim of 16 splits per round trip; the
+  // running maximum rescales the sums between batches.
+  constexpr int kCh = 128;
+  __shared__ float s_m[kCh], s_l[kCh];
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < C; c0 += kCh) {
+    const int n = C - c0 < kCh ? C - c0 : kCh;
+    __syncthreads();  // the previous batch is read
+    for (int j = d; j < n; j += D) {
+      s_m[j] = p[(c0 + j) * cs + D];
+      s_l[j] = p[(c0 + j) * cs + D + 1];
     }
+    __syncthreads();
+    float bm = -INFINITY;
+    for (int j = 0; j < n; ++j) bm = fmaxf(bm, s_m[j]);
+    const float mn = fmaxf(M, bm);
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+    num *= sc;
+    den *= sc;
+    M = mn;
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      float ov[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - M);
-      num = fmaf(w, ov[j], num);
-      den = fmaf(w, lv[j], den);
+      for (int j = 0; j < 16; ++j) ov[j] = j0 + j < n ? p[(c0 + j0 + j) * cs + d] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j0 + j < n) {
+          const float mc = s_m[j0 + j];
+          const float w = mc == -INFINITY ? 0.f : fast_exp2(mc - M);
+          num = fmaf(w, ov[j], num);
+          den = fmaf(w, s_l[j0 + j], den);
+        }
+      }
     }
   }
   const int tau = row / a.G, hh = row - tau * a.G;
@@ -889,11 +899,16 @@ PrefillPlan prefill_plan(int B, int Tq, int Hq, int Hkv, int N, int Tmax) {
   p.KW = 1;
   p.W = p.rows <= 64 ? 2 : 4;
   p.RC = (p.rows + p.W * kPfRowsPerWave - 1) / (p.W * kPfRowsPerWave);
+  // At most about 512 items (two per compute unit at this kernel's
+  // occupancy) so that they run in one round: a second, nearly empty round
+  // would double the time.
   const int64_t heads = (int64_t)B * Hkv * p.RC;
-  const int64_t ctarget = heads >= 512 ? 1 : (512 + heads - 1) / heads;
-  int64_t E = ((int64_t)N + Tmax + ctarget - 1) / ctarget;
+  const int64_t cmax = heads >= 256 ? 2 : 512 / heads;
+  int64_t E = ((int64_t)N + Tmax + cmax - 2) / (cmax > 2 ? cmax - 1 : 1);
   E = (E + kPfStage - 1) / kPfStage * kPfStage;
   if (E < 64) E = 64;
+  while (((int64_t)N + E - 1) / E + ((int64_t)Tmax + E - 1) / E > cmax && E < (int64_t)N + Tmax)
+    E += kPfStage;
   p.E = (int)E;
   p.CV = (int)((N + E - 1) / E);
   p.CT = (int)((Tmax + E - 1) / E);
