@@ -97,8 +97,9 @@ def decode_bytes(w, T=None):
 
 # Sources of the one-launch decode layer's kernel (their hash keys the
 # committed counter summaries).
-FUSED_SOURCES = ("fused.hip", "fused_kernel.h", "fused_bf16.hip", "fused_f32.hip",
-                 "decode_items.h", "long_select.h", "select.h", "common.h")
+FUSED_SOURCES = ("fused.hip", "fused_kernel.h", "fused_bf16.hip", "fused_bf16_long.hip",
+                 "fused_f32.hip", "fused_f32_long.hip", "decode_items.h", "long_select.h",
+                 "select.h", "common.h")
 
 
 # Sources of the dense-packing kernel.

@@ -20,9 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsv.so")
 
-SOURCES = ["api.cpp", "retrieve.hip", "attn.hip", "fused.hip", "fused_bf16.hip", "fused_f32.hip",
-           "salience.hip", "salience_stream.hip", "pack.hip", "summary.hip",
-           "prefill.hip"]
+SOURCES = ["api.cpp", "retrieve.hip", "attn.hip", "fused.hip", "fused_bf16.hip",
+           "fused_bf16_long.hip", "fused_f32.hip", "fused_f32_long.hip", "salience.hip",
+           "salience_stream.hip", "pack.hip", "summary.hip", "prefill.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

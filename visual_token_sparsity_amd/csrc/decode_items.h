@@ -10,8 +10,9 @@
 // logits.  qhat lives in LDS (two planes of four floats per 16-byte chunk, so
 // a wave's reads are conflict-free); registers hold only two rows of keys in
 // flight per lane.  A row of C 16-byte chunks is split into segments of at
-// most 512 chunks; LPR lanes (a power of two) cover one segment with up to 8
-// chunks each.  Chunks past the row end read a clamped in-row address and
+// most 64*CPL chunks; LPR lanes (a power of two) cover one segment with up to
+// CPL chunks each (CPL = 8; 4 in the fused kernel's short-row scans, which
+// keeps that kernel at five waves per SIMD).  Chunks past the row end read a clamped in-row address and
 // meet a zero in qhat, so every load is unconditional.
 //
 // Select (same passage): when the last scan item of a sequence finishes, its
@@ -45,8 +46,8 @@ namespace sv {
 
 constexpr int kItemWaves = 4;
 constexpr int kItemThreads = kItemWaves * kWave;
-constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment
-constexpr int kScanSegChunks = 512;
+constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment (default)
+constexpr int kScanCplShort = 4;   // the fused kernel's short-row scans: half the registers
 constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
 
 // Bits of the sticky status word (the first word of a workspace whose kernels
@@ -98,18 +99,20 @@ struct ScanArgs {
 };
 
 // Chunks of qhat kept in LDS (zero past C).
-__host__ __device__ inline int scan_padded_chunks(int nseg, int LPR) {
-  return nseg > 1 ? nseg * kScanSegChunks : LPR * kScanCpl;
+// A segment is cpl * 64 chunks (each lane cpl of them).
+__host__ __device__ inline int scan_padded_chunks(int nseg, int LPR, int cpl = kScanCpl) {
+  return nseg > 1 ? nseg * cpl * kWave : LPR * cpl;
 }
 
-__host__ inline void scan_geometry(int C, int* nseg, int* LPR) {
-  if (C > kScanSegChunks) {
-    *nseg = (C + kScanSegChunks - 1) / kScanSegChunks;
+__host__ inline void scan_geometry(int C, int* nseg, int* LPR, int cpl = kScanCpl) {
+  const int seg = cpl * kWave;
+  if (C > seg) {
+    *nseg = (C + seg - 1) / seg;
     *LPR = kWave;
     return;
   }
   *nseg = 1;
-  const int need = (C + kScanCpl - 1) / kScanCpl;
+  const int need = (C + cpl - 1) / cpl;
   int l = 1;
   while (l < need) l <<= 1;
   *LPR = l;
@@ -130,7 +133,7 @@ __device__ __forceinline__ float sum_lanes_rt(float v, int width) {
 // One scan item: rows [item*rows_per_item, ...) of sequence b.  Returns true
 // in every thread of the workgroup that must run the select for b.  q_of is
 // the sequence whose qhat LDS holds (-1: none); it is reused when it matches.
-template <typename T>
+template <typename T, int CPL = kScanCpl>
 __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, char* smem,
                                           int& q_of) {
   constexpr int VE = Vec<T>::kElems;
@@ -143,7 +146,8 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   const int RPS = kWave / LPR;  // units per wave step
   const int sub = lane & (LPR - 1);
   const int rsub = lane / LPR;
-  const int CP = scan_padded_chunks(nseg, LPR);
+  constexpr int SEG = CPL * kWave;  // chunks per segment
+  const int CP = scan_padded_chunks(nseg, LPR, CPL);
   float* qh = reinterpret_cast<float*>(smem);  // [NP][CP][4]
 
   const int r0 = item * a.rows_per_item;
@@ -181,15 +185,15 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   auto unit_off = [&](int u) -> uint32_t {
     const int row = unit_row(u);
     if (u >= nunits || row >= nrows) return kBufOob;
-    return (uint32_t)row * row_bytes + (uint32_t)(unit_seg(u) * kScanSegChunks + sub) * 16u;
+    return (uint32_t)row * row_bytes + (uint32_t)(unit_seg(u) * SEG + sub) * 16u;
   };
   // Chunk j of a unit is chunk sub + j*LPR of its segment; chunks past the
   // segment are not loaded (uniform) or, where a segment is ragged, zeroed.
   auto load_unit = [&](int u, Vec<T>* dst) {
-    const int slen = min(kScanSegChunks, a.C - unit_seg(u < nunits ? u : 0) * kScanSegChunks);
+    const int slen = min(SEG, a.C - unit_seg(u < nunits ? u : 0) * SEG);
     const uint32_t off = unit_off(u);
 #pragma unroll
-    for (int j = 0; j < kScanCpl; ++j) {
+    for (int j = 0; j < CPL; ++j) {
       if (j * LPR < slen)
         dst[j].template load_buf<kCacheStream>(rs, off, (uint32_t)(j * LPR * 16));
       else
@@ -197,16 +201,16 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
     }
   };
   auto mask_ragged = [&](int u, Vec<T>* v) {
-    const int slen = min(kScanSegChunks, a.C - unit_seg(u) * kScanSegChunks);
+    const int slen = min(SEG, a.C - unit_seg(u) * SEG);
     if (slen % LPR == 0) return;  // uniform
 #pragma unroll
-    for (int j = 0; j < kScanCpl; ++j)
+    for (int j = 0; j < CPL; ++j)
       if (sub + j * LPR >= slen) v[j].zero();
   };
 
   // The wave's first two units of keys in flight before the query is summed
   // (units past the wave's run read nothing).
-  Vec<T> va[kScanCpl], vb[kScanCpl];
+  Vec<T> va[CPL], vb[CPL];
   load_unit(rsub, va);
   load_unit(RPS + rsub, vb);
 
@@ -256,8 +260,8 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
     const int seg = unit_seg(u);
     mask_ragged(u, cur);
 #pragma unroll
-    for (int j = 0; j < kScanCpl; ++j) {
-      const int ch = seg * kScanSegChunks + sub + j * LPR;
+    for (int j = 0; j < CPL; ++j) {
+      const int ch = seg * SEG + sub + j * LPR;
       float f[VE];
       cur[j].to_f32(f);
 #pragma unroll
@@ -396,8 +400,9 @@ __device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float
   }
 }
 
-__host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE, bool hist = false) {
-  const size_t q = (size_t)scan_padded_chunks(nseg, LPR) * VE * sizeof(float) +
+__host__ __device__ inline size_t scan_smem_bytes(int nseg, int LPR, int VE, bool hist = false,
+                                                  int cpl = kScanCpl) {
+  const size_t q = (size_t)scan_padded_chunks(nseg, LPR, cpl) * VE * sizeof(float) +
                    (hist ? (size_t)kLsBins * sizeof(uint32_t) : 0);
   const size_t s = sizeof(SelectSmem<kItemWaves>);
   return q > s ? q : s;

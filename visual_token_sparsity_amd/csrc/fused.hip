@@ -5,13 +5,16 @@
 
 namespace sv {
 
-// Defined in fused_bf16.hip and fused_f32.hip.
-extern template hipError_t launch_fused_typed<bf16_t>(int, int, int, const ScanArgs&,
-                                                      const AttnArgs&, const FusedCtl&,
-                                                      const LongSelArgs&, hipStream_t);
-extern template hipError_t launch_fused_typed<float>(int, int, int, const ScanArgs&,
-                                                     const AttnArgs&, const FusedCtl&,
-                                                     const LongSelArgs&, hipStream_t);
+// Defined in fused_bf16.hip, fused_bf16_long.hip, fused_f32.hip and fused_f32_long.hip.
+#define SV_FUSED_EXTERN(T, LONG)                                                          \
+  extern template hipError_t launch_fused_typed<T, LONG>(int, int, int, const ScanArgs&,   \
+                                                        const AttnArgs&, const FusedCtl&, \
+                                                        const LongSelArgs&, hipStream_t)
+SV_FUSED_EXTERN(bf16_t, false);
+SV_FUSED_EXTERN(bf16_t, true);
+SV_FUSED_EXTERN(float, false);
+SV_FUSED_EXTERN(float, true);
+#undef SV_FUSED_EXTERN
 
 // Long-row select workspace, per launch:
 //   [ctl B*kLsCtlLines lines][hist1 B*kLsReps*kLsBins][hist2 B*kLsBins]  (zero between launches)
@@ -48,7 +51,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.N = f.N;
   sa.D = f.D;
   sa.C = f.Hkv * f.D / VE;
-  scan_geometry(sa.C, &sa.nseg, &sa.LPR);
+  scan_geometry(sa.C, &sa.nseg, &sa.LPR, long_rows(f.N) ? kScanCpl : kScanCplShort);
   // Rows that fit the select's registers: small scan items (more of them
   // than resident workgroups, so the sequences finish one after another),
   // complemented scores and a polling select item per sequence.  Longer
@@ -132,8 +135,12 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   ctl.text_end = ctl.seq_end + (uint32_t)p.CT * f.Hkv * f.B;
   ctl.total = ctl.text_end + (uint32_t)p.CV * f.Hkv * f.B;
   if (f.retrieve_only) ctl.text_end = ctl.total = ctl.seq_end;
-  if (f.dtype == 1) return launch_fused_typed<bf16_t>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
-  return launch_fused_typed<float>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
+  const bool lng = sa.hist1 != nullptr;
+  if (f.dtype == 1)
+    return lng ? launch_fused_typed<bf16_t, true>(f.D, G, p.EPL, sa, aa, ctl, ls, st)
+               : launch_fused_typed<bf16_t, false>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
+  return lng ? launch_fused_typed<float, true>(f.D, G, p.EPL, sa, aa, ctl, ls, st)
+             : launch_fused_typed<float, false>(f.D, G, p.EPL, sa, aa, ctl, ls, st);
 }
 
 }  // namespace sv

@@ -1,0 +1,13 @@
+// Instantiations of the one-launch decode layer for bf16_t caches,
+// rows of more than 2048 tokens (the parallel
+// select): a translation unit of their own, so the dtype and row-mode
+// variants compile in parallel.
+#include "fused_kernel.h"
+
+namespace sv {
+
+template hipError_t launch_fused_typed<bf16_t, true>(int, int, int, const ScanArgs&,
+                                                       const AttnArgs&, const FusedCtl&,
+                                                       const LongSelArgs&, hipStream_t);
+
+}  // namespace sv

@@ -1,11 +1,13 @@
-// Instantiations of the one-launch decode layer for float caches (their own
-// translation unit, so the two dtypes compile in parallel).
+// Instantiations of the one-launch decode layer for fp32 caches,
+// rows of at most 2048 tokens (one select workgroup
+// per sequence): a translation unit of their own, so the dtype and row-mode
+// variants compile in parallel.
 #include "fused_kernel.h"
 
 namespace sv {
 
-template hipError_t launch_fused_typed<float>(int, int, int, const ScanArgs&, const AttnArgs&,
-                                           const FusedCtl&, const LongSelArgs&,
-                                           hipStream_t);
+template hipError_t launch_fused_typed<float, false>(int, int, int, const ScanArgs&,
+                                                       const AttnArgs&, const FusedCtl&,
+                                                       const LongSelArgs&, hipStream_t);
 
 }  // namespace sv

@@ -48,18 +48,20 @@ struct FusedCtl {
   float* scores_out;   // decoded scores (polling mode), may be null
 };
 
-template <typename T, int D, int G, int EPL>
+// LONG: rows of more than 2048 tokens (the parallel select); each mode is
+// its own instantiation, so neither carries the other's registers.
+template <typename T, int D, int G, int EPL, bool LONG>
 __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnArgs aa,
                                                              FusedCtl ctl, LongSelArgs ls) {
   extern __shared__ __align__(16) char smem[];
   const uint32_t t = blockIdx.x;
   if (t < ctl.seq_end) {
     int q_of = -1;
-    if (!sa.hist1) {
+    if constexpr (!LONG) {
       const int b = t / ctl.per_seq;
       const int j = t % ctl.per_seq;
       if (j < sa.items_per_seq) {
-        if (scan_item<T>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+        if (scan_item<T, kScanCplShort>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
       } else {
         select_poll_item(sa, b, ctl.scores_out, smem);
       }
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
     const uint32_t S = (uint32_t)sa.items_per_seq, P = (uint32_t)ls.P;
     uint32_t u = t;
     if (u < ctl.B * S) {
-      scan_item<T>(sa, u / S, u % S, smem, q_of);
+      scan_item<T, kScanCpl>(sa, u / S, u % S, smem, q_of);
     } else if ((u -= ctl.B * S) < ctl.B * P) {
       cand_item(sa, ls, u / P, u % P, smem);
     } else if ((u -= ctl.B * P) < ctl.B) {
@@ -101,11 +103,11 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   }
 }
 
-template <typename T, int D, int G, int EPL>
+template <typename T, int D, int G, int EPL, bool LONG>
 static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
                            const LongSelArgs& ls, hipStream_t st) {
   const int VE = Vec<T>::kElems;
-  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE, sa.hist1 != nullptr);
+  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE, LONG, LONG ? kScanCpl : kScanCplShort);
   if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
   if (sa.hist1) {
     if (cand_smem_bytes() > lds) lds = cand_smem_bytes();
@@ -114,7 +116,7 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
   if (lds > 48 * 1024) {
     static bool raised = false;  // per instantiation; the attribute is per function
     if (!raised) {
-      const hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<T, D, G, EPL>,
+      const hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<T, D, G, EPL, LONG>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                96 * 1024);
       if (e != hipSuccess) return e;
@@ -129,7 +131,7 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
     // once (a second, partly filled round would leave the memory system
     // idle at its end).
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<T, D, G, EPL>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<T, D, G, EPL, LONG>,
                                                      kItemThreads, lds) == hipSuccess &&
         per_cu > 0) {
       const uint32_t attn_items = ctl.total - ctl.seq_end, text_items = ctl.text_end - ctl.seq_end;
@@ -143,43 +145,44 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
       c.total = c.seq_end + attn_items;
     }
   }
-  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL>), dim3(c.total), dim3(kItemThreads), lds, st,
+  hipLaunchKernelGGL((fused_kernel<T, D, G, EPL, LONG>), dim3(c.total), dim3(kItemThreads), lds, st,
                      s, aa, c, ls);
   return hipGetLastError();
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool LONG>
 static hipError_t fused_epl(int epl, const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
                             const LongSelArgs& ls, hipStream_t st) {
   switch (epl) {  // the fused launch plans 4 or 8 entries per lane
-    case 4: return fused_go<T, D, G, 4>(sa, aa, ctl, ls, st);
-    case 8: return fused_go<T, D, G, 8>(sa, aa, ctl, ls, st);
+    case 4: return fused_go<T, D, G, 4, LONG>(sa, aa, ctl, ls, st);
+    case 8: return fused_go<T, D, G, 8, LONG>(sa, aa, ctl, ls, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool LONG>
 static hipError_t fused_g(int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
                           const FusedCtl& ctl, const LongSelArgs& ls, hipStream_t st) {
   switch (G) {
-    case 1: return fused_epl<T, D, 1>(epl, sa, aa, ctl, ls, st);
-    case 2: return fused_epl<T, D, 2>(epl, sa, aa, ctl, ls, st);
-    case 3: return fused_epl<T, D, 3>(epl, sa, aa, ctl, ls, st);
-    case 4: return fused_epl<T, D, 4>(epl, sa, aa, ctl, ls, st);
-    case 5: return fused_epl<T, D, 5>(epl, sa, aa, ctl, ls, st);
-    case 6: return fused_epl<T, D, 6>(epl, sa, aa, ctl, ls, st);
-    case 7: return fused_epl<T, D, 7>(epl, sa, aa, ctl, ls, st);
-    case 8: return fused_epl<T, D, 8>(epl, sa, aa, ctl, ls, st);
+    case 1: return fused_epl<T, D, 1, LONG>(epl, sa, aa, ctl, ls, st);
+    case 2: return fused_epl<T, D, 2, LONG>(epl, sa, aa, ctl, ls, st);
+    case 3: return fused_epl<T, D, 3, LONG>(epl, sa, aa, ctl, ls, st);
+    case 4: return fused_epl<T, D, 4, LONG>(epl, sa, aa, ctl, ls, st);
+    case 5: return fused_epl<T, D, 5, LONG>(epl, sa, aa, ctl, ls, st);
+    case 6: return fused_epl<T, D, 6, LONG>(epl, sa, aa, ctl, ls, st);
+    case 7: return fused_epl<T, D, 7, LONG>(epl, sa, aa, ctl, ls, st);
+    case 8: return fused_epl<T, D, 8, LONG>(epl, sa, aa, ctl, ls, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// One dtype's instantiations (compiled in their own translation unit).
-template <typename T>
+// One (dtype, row mode)'s instantiations, each compiled in a translation unit
+// of its own so that they build in parallel.
+template <typename T, bool LONG>
 hipError_t launch_fused_typed(int D, int G, int epl, const ScanArgs& sa, const AttnArgs& aa,
                               const FusedCtl& ctl, const LongSelArgs& ls, hipStream_t st) {
-  return D == 128 ? fused_g<T, 128>(G, epl, sa, aa, ctl, ls, st)
-                  : fused_g<T, 64>(G, epl, sa, aa, ctl, ls, st);
+  return D == 128 ? fused_g<T, 128, LONG>(G, epl, sa, aa, ctl, ls, st)
+                  : fused_g<T, 64, LONG>(G, epl, sa, aa, ctl, ls, st);
 }
 
 }  // namespace sv
