@@ -44,6 +44,7 @@ constexpr int kStrThreads = kStrWaves * kWave;
 constexpr int kStrTiles = 4;               // 16-wide tiles per wave (rows or keys)
 constexpr int kStrBlock = kStrWaves * kStrTiles * 16;   // 256 rows / keys per workgroup
 constexpr int kStrStage = kStrTiles * 16;  // 64 keys / rows per LDS stage
+constexpr float kLag = 8.f;                // pass 1: most the shift may trail the row maximum
 
 __device__ __forceinline__ bf16x8_t ld_frag(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
@@ -146,26 +147,53 @@ __global__ __launch_bounds__(kStrThreads) void salience_rowstat_kernel(
     }
     // Columns past N do not exist (the tail stage only).
     const int kcol = st * kStrStage + li;
-    bool valid[kStrTiles];
+    if (st + 1 < nst || N % kStrStage == 0) {
+      // Every column counts.  The shift m lags the running maximum by at most
+      // kLag (log2 units): it moves only when a stage's maximum rises past
+      // m + kLag, so most stages take one max, one fma, one exp and one add
+      // per element (terms stay below 2^kLag, and none underflows earlier
+      // than with the exact running maximum).
 #pragma unroll
-    for (int t = 0; t < kStrTiles; ++t) valid[t] = kcol + 16 * t < N;
+      for (int rb = 0; rb < kStrTiles; ++rb) {
 #pragma unroll
-    for (int rb = 0; rb < kStrTiles; ++rb) {
+        for (int r = 0; r < 4; ++r) {
+          float smax = S[0][rb][r];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x[kStrTiles];
-        float mx = m[rb][r];
+          for (int t = 1; t < kStrTiles; ++t) smax = fmaxf(smax, S[t][rb][r]);
+          const float xm = smax * c2;
+          float mm = m[rb][r], ll = l[rb][r];
+          if (xm > mm + kLag) {  // also the first stage (m = -inf)
+            ll = mm == -INFINITY ? 0.f : ll * fast_exp2(mm - xm);
+            mm = xm;
+          }
 #pragma unroll
-        for (int t = 0; t < kStrTiles; ++t) {
-          x[t] = valid[t] ? S[t][rb][r] * c2 : -INFINITY;
-          mx = fmaxf(mx, x[t]);
+          for (int t = 0; t < kStrTiles; ++t) ll += fast_exp2(fmaf(S[t][rb][r], c2, -mm));
+          l[rb][r] = ll;
+          m[rb][r] = mm;
         }
-        if (mx != -INFINITY) {
-          float sum = l[rb][r] * fast_exp2(m[rb][r] - mx);  // m = -inf -> 0
+      }
+    } else {
+      bool valid[kStrTiles];
 #pragma unroll
-          for (int t = 0; t < kStrTiles; ++t) sum += fast_exp2(x[t] - mx);
-          l[rb][r] = sum;
-          m[rb][r] = mx;
+      for (int t = 0; t < kStrTiles; ++t) valid[t] = kcol + 16 * t < N;
+#pragma unroll
+      for (int rb = 0; rb < kStrTiles; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x[kStrTiles];
+          float mx = m[rb][r];
+#pragma unroll
+          for (int t = 0; t < kStrTiles; ++t) {
+            x[t] = valid[t] ? S[t][rb][r] * c2 : -INFINITY;
+            mx = fmaxf(mx, x[t]);
+          }
+          if (mx != -INFINITY) {
+            float sum = l[rb][r] * fast_exp2(m[rb][r] - mx);  // m = -inf -> 0
+#pragma unroll
+            for (int t = 0; t < kStrTiles; ++t) sum += fast_exp2(x[t] - mx);
+            l[rb][r] = sum;
+            m[rb][r] = mx;
+          }
         }
       }
     }
