@@ -11,8 +11,8 @@
 // a wave's reads are conflict-free); registers hold only two rows of keys in
 // flight per lane.  A row of C 16-byte chunks is split into segments of at
 // most 64*CPL chunks; LPR lanes (a power of two) cover one segment with up to
-// CPL chunks each (CPL = 8; 4 in the fused kernel's short-row scans, which
-// keeps that kernel at five waves per SIMD).  Chunks past the row end read a clamped in-row address and
+// CPL chunks each (CPL = 8; 4 in the bf16 short-row scans, which keeps the
+// fused kernel's short-row mode at five waves per SIMD).  Chunks past the row end read a clamped in-row address and
 // meet a zero in qhat, so every load is unconditional.
 //
 // Select (same passage): when the last scan item of a sequence finishes, its
@@ -47,7 +47,11 @@ namespace sv {
 constexpr int kItemWaves = 4;
 constexpr int kItemThreads = kItemWaves * kWave;
 constexpr int kScanCpl = 8;        // 16-byte chunks per lane per segment (default)
-constexpr int kScanCplShort = 4;   // the fused kernel's short-row scans: half the registers
+constexpr int kScanCplShort = 4;   // bf16 short-row scans (fused and standalone): half the registers
+// Chunks per lane per unit of the short-row scans of a dtype (1: bf16).
+template <typename T>
+__host__ __device__ constexpr int short_scan_cpl() { return sizeof(T) == 2 ? kScanCplShort : kScanCpl; }
+__host__ inline int short_scan_cpl(int dtype) { return dtype == 1 ? kScanCplShort : kScanCpl; }
 constexpr int kSelKpt = 8;         // keys per thread kept in registers by the select
 
 // Bits of the sticky status word (the first word of a workspace whose kernels

@@ -51,7 +51,7 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
   sa.N = f.N;
   sa.D = f.D;
   sa.C = f.Hkv * f.D / VE;
-  scan_geometry(sa.C, &sa.nseg, &sa.LPR, long_rows(f.N) ? kScanCpl : kScanCplShort);
+  scan_geometry(sa.C, &sa.nseg, &sa.LPR, long_rows(f.N) ? kScanCpl : short_scan_cpl(f.dtype));
   // Rows that fit the select's registers: small scan items (more of them
   // than resident workgroups, so the sequences finish one after another),
   // complemented scores and a polling select item per sequence.  Longer

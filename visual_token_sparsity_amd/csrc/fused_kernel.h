@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
       const int b = t / ctl.per_seq;
       const int j = t % ctl.per_seq;
       if (j < sa.items_per_seq) {
-        if (scan_item<T, kScanCplShort>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+        if (scan_item<T, short_scan_cpl<T>()>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
       } else {
         select_poll_item(sa, b, ctl.scores_out, smem);
       }
@@ -107,7 +107,7 @@ template <typename T, int D, int G, int EPL, bool LONG>
 static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCtl& ctl,
                            const LongSelArgs& ls, hipStream_t st) {
   const int VE = Vec<T>::kElems;
-  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE, LONG, LONG ? kScanCpl : kScanCplShort);
+  size_t lds = scan_smem_bytes(sa.nseg, sa.LPR, VE, LONG, LONG ? kScanCpl : short_scan_cpl<T>());
   if (attn_smem_bytes<D, G>() > lds) lds = attn_smem_bytes<D, G>();
   if (sa.hist1) {
     if (cand_smem_bytes() > lds) lds = cand_smem_bytes();

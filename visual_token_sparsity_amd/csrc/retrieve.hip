@@ -16,7 +16,7 @@ __global__ __launch_bounds__(kItemThreads) void scan_select_kernel(ScanArgs a) {
   extern __shared__ __align__(16) char smem[];
   int q_of = -1;
   const int b = blockIdx.y;
-  if (scan_item<T, kScanCplShort>(a, b, blockIdx.x, smem, q_of)) select_item(a, b, smem, q_of);
+  if (scan_item<T, short_scan_cpl<T>()>(a, b, blockIdx.x, smem, q_of)) select_item(a, b, smem, q_of);
 }
 
 int scan_rows_per_item(int B, int N, int LPR, int nseg) {
@@ -54,7 +54,7 @@ hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv,
   a.D = D;
   a.C = Hkv * D / VE;
   // The fused kernel's short-row unit size: both paths sum in the same order.
-  scan_geometry(a.C, &a.nseg, &a.LPR, kScanCplShort);
+  scan_geometry(a.C, &a.nseg, &a.LPR, short_scan_cpl(dtype));
   a.rows_per_item = rows_per_item > 0 ? rows_per_item : scan_rows_per_item(B, N, a.LPR, a.nseg);
   a.items_per_seq = (N + a.rows_per_item - 1) / a.rows_per_item;
   a.scores = scores;
@@ -62,7 +62,7 @@ hipError_t launch_retrieve(const void* q, int B, int Tq, int Hq, const void* kv,
   a.idx = idx_out;
   a.seq_ctr = counters;
   a.ready = nullptr;
-  const size_t lds = scan_smem_bytes(a.nseg, a.LPR, VE, false, kScanCplShort);
+  const size_t lds = scan_smem_bytes(a.nseg, a.LPR, VE, false, short_scan_cpl(dtype));
   const dim3 grid(a.items_per_seq, B);
   if (dtype == 1)
     hipLaunchKernelGGL(scan_select_kernel<bf16_t>, grid, dim3(kItemThreads), lds, stream, a);
