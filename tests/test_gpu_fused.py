@@ -56,6 +56,11 @@ FUSED_CASES = [
     ("fp32_rows_two_segments", "image576_fp32", dict(N=130, k=30, T=10, Tmax=12, planted=0)),
     ("bf16_rows_two_segments", "llava_next_7b", dict(B=2, N=130, k=30, Hq=64, Hkv=64, T=10,
                                                      Tmax=12, planted=0)),
+    # Matrix-core attention items in both row modes, D = 64.
+    ("gqa8_d64_short_rows", "qwen2_7b_video", dict(B=2, Hq=32, Hkv=4, D=64, N=1500, k=300, T=50,
+                                                   Tmax=64)),
+    ("gqa2_d64_long_rows", "qwen2_7b_video", dict(Hq=4, Hkv=2, D=64, N=5000, k=700, T=20,
+                                                  Tmax=24)),
 ]
 
 

@@ -229,6 +229,11 @@ ATTN_CASES = [
     ("text_only", "llava_next_7b", dict(B=2, N=50, k=0, planted=0)),
     ("visual_only", "llava_next_7b", dict(B=2, N=300, k=40, T=0, Tmax=0, planted=0)),
     ("ragged_small", "qwen2_7b_video", dict(N=37, k=5, T=3, Tmax=9)),
+    # bf16 grouped-query heads on matrix cores: 2 and 8 query heads per KV
+    # head at D = 64 (up to four 16-entry tiles per wave), 4 at D = 128.
+    ("gqa2_d64", "qwen2_7b_video", dict(Hq=8, Hkv=4, D=64, N=700, k=200, T=40, Tmax=48)),
+    ("gqa8_d64", "qwen2_7b_video", dict(Hq=32, Hkv=4, D=64, N=3000, k=1000, T=70, Tmax=80)),
+    ("gqa4_d128_b3", "qwen2_7b_video", dict(B=3, Hq=16, Hkv=4, N=900, k=250, T=33, Tmax=40)),
 ]
 
 
