@@ -37,6 +37,9 @@ CASES = [
     ("one_token", 3, 1, 8, 8, 128, 500, 40, [40, 1, 0], 64),
     ("long_rows_select", 1, 4, 8, 8, 128, 5000, 16, [16], 700),
     ("k_equals_n", 1, 3, 4, 4, 64, 90, 10, [10], 90),
+    # 192 (sequence, KV head) items: one key split each, normalised output
+    # written by the attention items themselves (no combine).
+    ("one_split_direct_output", 6, 4, 32, 32, 128, 300, 40, [40, 33, 4, 40, 0, 17], 100),
 ]
 
 
