@@ -894,8 +894,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   const float* pb = a.part + head0 * C * PS;  // this (b, g): [G][C][PS]
   if (C <= kMaxCombineSplits) {
     // Thread (v, s) sums float4 column v over splits s, s+S, ...; its first
-    // 16 loads go out together with the (m, l) loads of every split (to
-    // LDS), so the merge costs one round trip.  Then one wave per head turns
+    // 8 loads go out together with the (m, l) loads of every split (to LDS),
+    // so up to 8 S splits merge in one round trip (8, not more: the batch's
+    // registers set the fused kernel's occupancy).  Then one wave per head turns
     // m into the weight 2^(m - M) and sums the denominator, and the S groups
     // of a column meet in LDS.
     float* s_f = reinterpret_cast<float*>(smem);  // [G][C]
@@ -911,9 +912,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
       return __builtin_bit_cast(
           f32x4v, load4_dev(pr, (s < S && cc < C) ? col + (uint32_t)(cc * PS * 4) : kBufOob));
     };
-    f32x4v x[16];
+    f32x4v x[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = col_load(s + j * S);
+    for (int j = 0; j < 8; ++j) x[j] = col_load(s + j * S);
     for (int t = tid; t < G * C; t += kItemThreads) {
       s_f[t] = load_shared_dev(pb + (int64_t)t * PS + D);
       s_l[t] = load_shared_dev(pb + (int64_t)t * PS + D + 1);
@@ -936,15 +937,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     __syncthreads();
     f32x4v num = {0.f, 0.f, 0.f, 0.f};
     const float* fw = s_f + i * C;
-    for (int c0 = s;; c0 += 16 * S) {
+    for (int c0 = s;; c0 += 8 * S) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 8; ++j) {
         const int cc = c0 + j * S;
         num += (s < S && cc < C ? fw[cc] : 0.f) * x[j];
       }
-      if (c0 + 16 * S >= C) break;  // no barrier inside: per-thread exit is fine
+      if (c0 + 8 * S >= C) break;  // no barrier inside: per-thread exit is fine
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = col_load(c0 + 16 * S + j * S);
+      for (int j = 0; j < 8; ++j) x[j] = col_load(c0 + 8 * S + j * S);
     }
     if constexpr (S > 1) {
       s_red[tid] = num;

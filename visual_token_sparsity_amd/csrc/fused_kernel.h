@@ -61,7 +61,9 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
       const int b = t / ctl.per_seq;
       const int j = t % ctl.per_seq;
       if (j < sa.items_per_seq) {
-        if (scan_item<T, short_scan_cpl<T>()>(sa, b, j, smem, q_of)) select_item(sa, b, smem, q_of);
+        // Scores stored complemented (encode): the scan item never selects,
+        // the select item below does.
+        scan_item<T, short_scan_cpl<T>()>(sa, b, j, smem, q_of);
       } else {
         select_poll_item(sa, b, ctl.scores_out, smem);
       }
