@@ -229,6 +229,7 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
             if (kb + r < nkeys) pscore[e0 + kb + r] = sc[r];
         }
       }
+      s16x4 ph[2], pl[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float xv[4], tmax = -INFINITY;
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
           xv[r] = ok ? St[rb][r] * a.c2 : -INFINITY;
           tmax = fmaxf(tmax, xv[r]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        tmax = fmaxf(tmax, xor_partner<16>(tmax));
+        tmax = fmaxf(tmax, xor_partner<32>(tmax));
         const float mn = fmaxf(m[rb], tmax);
         const float al = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
         float p[4], ps = 0.f;
@@ -251,24 +252,31 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
         }
         l[rb] = l[rb] * al + ps;
         m[rb] = mn;
+        // Rescale the output rows whose maximum rose (the whole wave or none).
+        if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[rb][db] *= al;
+        }
         // P^T as the B operand: high bf16 part and the bf16 residual.
-        s16x4 ph, pl;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint16_t h = bf16_rne(p[r]);
-          ph[r] = (short)h;
-          pl[r] = (short)bf16_rne(p[r] - __uint_as_float((uint32_t)h << 16));
+          ph[rb][r] = (short)h;
+          pl[rb][r] = (short)bf16_rne(p[r] - __uint_as_float((uint32_t)h << 16));
         }
+      }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          // V^T fragment: lane (li, lg) gets dim 16 db + li of keys 16 t + 4 lg .. + 3.
-          const int vkey = 16 * t + 4 * lg + (li >> 2);
-          const char* va = cur + S::KBYTES + vkey * S::VSTR + (16 * db + 4 * (li & 3)) * 2;
-          const s16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(va));
-          f32x4_t o = acc[rb][db] * al;
-          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, ph, o, 0, 0, 0);
-          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl, o, 0, 0, 0);
+      for (int db = 0; db < DB; ++db) {
+        // V^T fragment: lane (li, lg) gets dim 16 db + li of keys 16 t + 4 lg .. + 3.
+        const int vkey = 16 * t + 4 * lg + (li >> 2);
+        const char* va = cur + S::KBYTES + vkey * S::VSTR + (16 * db + 4 * (li & 3)) * 2;
+        const s16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4_t o = acc[rb][db];
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, ph[rb], o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl[rb], o, 0, 0, 0);
           acc[rb][db] = o;  // acc[rb][db][r] = O[row 16 rb + li][dim 16 db + 4 lg + r]
         }
       }
@@ -284,8 +292,8 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float lt = l[rb];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    lt += xor_partner<16>(lt);
+    lt += xor_partner<32>(lt);
     const int rl = wave * kPfRowsPerWave + 16 * rb + li;
     float* pr = part + (int64_t)rl * (D + 4);
 #pragma unroll
