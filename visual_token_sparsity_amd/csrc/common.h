@@ -259,7 +259,7 @@ __host__ __device__ constexpr int attn_part_stride(int D) { return D + 4; }
 struct AttnPlan {
   int EPL, SE, CT, CV;
 };
-constexpr long kAttnTargetItems = 1024;       // standalone attention launch
+constexpr long kAttnTargetItems = 2048;       // standalone attention launch
 constexpr long kFusedAttnTargetItems = 2048;  // fused layer: smaller splits start sooner
 AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_items);
 // The fused launch's plan: attn_plan with kFusedAttnTargetItems, 4 or 8 entries per lane.
