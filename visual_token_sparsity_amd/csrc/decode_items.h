@@ -85,7 +85,13 @@ struct ScanArgs {
   float* scores;             // [B][N]
   int k;
   int32_t* idx;              // [B][k]
-  uint32_t* seq_ctr;         // [B] (stride kCtrStride) finished scan items, self-resetting
+  uint32_t* seq_ctr;         // [B << ctr_log2] (stride kCtrStride) finished scan items, self-resetting
+  // Long rows: scan item j of b counts on line (b << ctr_log2) + j % (1 << ctr_log2),
+  // and the waiting items sum the 1 << ctr_log2 lines of b.  Atomics on one
+  // address serialise (about 12 ns each), so one line per sequence would hold
+  // the last count back by several microseconds when hundreds of items
+  // finish together.  0 elsewhere (one line: the last arriver is known).
+  int ctr_log2;
   uint32_t* ready;           // [B] (stride kCtrStride) selection published (fused kernel only)
   // Fused kernel, rows that fit the select's registers: scores are stored as
   // the complement of their bits (a zero word: not written yet) and a select
@@ -315,7 +321,10 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
     }
     wait_stores_complete();
     __syncthreads();
-    if (tid == 0) counter_add(&a.seq_ctr[b * kCtrStride], 1u);
+    if (tid == 0) {
+      const int line = (b << a.ctr_log2) + (item & ((1 << a.ctr_log2) - 1));
+      counter_add(&a.seq_ctr[line * kCtrStride], 1u);
+    }
     return false;
   }
   wait_stores_complete();

@@ -17,7 +17,8 @@ SV_FUSED_EXTERN(float, true);
 #undef SV_FUSED_EXTERN
 
 // Long-row select workspace, per launch:
-//   [ctl B*kLsCtlLines lines][hist1 B*kLsReps*kLsBins][hist2 B*kLsBins]  (zero between launches)
+//   [ctl B*kLsCtlLines lines][scan counts B*kLsScanCtrs lines][hist1 B*kLsReps*kLsBins]
+//   [hist2 B*kLsBins]  (zero between launches)
 //   [cand B*kLsCandCap][chunk_hi B*P][offs B*P]
 static size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
 static bool long_rows(int N) { return N > kItemThreads * kSelKpt; }
@@ -26,6 +27,7 @@ static int long_chunks(int N) { return (N + kLsChunk - 1) / kLsChunk; }
 size_t long_select_zero_bytes(int B, int N) {
   if (!long_rows(N)) return 0;
   return al256((size_t)B * kLsCtlLines * kCtrStride * 4) +
+         al256((size_t)B * kLsScanCtrs * kCtrStride * 4) +
          al256((size_t)B * kLsReps * kLsBins * 4) + al256((size_t)B * kLsBins * 4);
 }
 
@@ -78,6 +80,9 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
     ls.P = (int)P;
     ls.ctl = reinterpret_cast<uint32_t*>(w);
     w += al256((size_t)f.B * kLsCtlLines * kCtrStride * 4);
+    sa.seq_ctr = reinterpret_cast<uint32_t*>(w);  // the scan items' count lines
+    sa.ctr_log2 = kLsScanCtrLog2;
+    w += al256((size_t)f.B * kLsScanCtrs * kCtrStride * 4);
     ls.hist1 = reinterpret_cast<uint32_t*>(w);
     w += al256((size_t)f.B * kLsReps * kLsBins * 4);
     ls.hist2 = reinterpret_cast<uint32_t*>(w);

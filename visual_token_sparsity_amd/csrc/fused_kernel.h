@@ -26,8 +26,8 @@
 // atomics from thousands of workgroups serialise in the memory system.
 //
 // Control words (one 128-byte line each) are zero after every launch:
-// seq_ctr[b] is reset by the selecting workgroup (long rows: the threshold
-// item), comb_ctr[b,g] by the combining one, and vis_done[b] counts visual
+// the scan count lines of b by the selecting workgroup (long rows: the
+// threshold item), comb_ctr[b,g] by the combining one, and vis_done[b] counts visual
 // items past their wait, the last of which lowers ready[b] again and clears
 // the encoded index copy the visual items poll.
 // Complemented scores are zeroed by the select item that read them; the

@@ -11,7 +11,8 @@
 //
 //   scan items   every score's top 11 key bits (digit d1) go to a local LDS
 //                histogram, flushed with atomics to one of 8 replicas of a
-//                per-sequence histogram (hist1); then seq_ctr[b] += 1.
+//                per-sequence histogram (hist1); then one of the 16 count
+//                lines of b += 1 (kLsScanCtrs: one hot line would serialise).
 //   cand item p  (one per chunk, waits for all scan items of b) sums the
 //                replicas, finds the digit D1 holding the k-th key, counts
 //                its chunk's keys above D1 (chunk_hi[p]), appends the keys
@@ -41,6 +42,8 @@ constexpr int kLsChunk = 2048;     // scores per candidate / compaction item
 constexpr int kLsCandCap = 16384;  // keys of digit D1 kept as candidates
 constexpr int kLsFinalCap = 256;   // keys of (D1, D2) ranked by one workgroup
 constexpr int kLsCtlLines = 6;     // control lines per sequence
+constexpr int kLsScanCtrLog2 = 4;  // the scan items' count lines per sequence: 16
+constexpr int kLsScanCtrs = 1 << kLsScanCtrLog2;
 
 static_assert(kLsChunk == kItemThreads * kSelKpt, "one chunk: eight keys per thread");
 static_assert(kLsFinalCap <= kItemThreads, "one final candidate per thread");
@@ -81,6 +84,25 @@ __device__ __forceinline__ uint32_t poll_until(const uint32_t* p, uint32_t targe
   return v;
 }
 
+// The sum of the n (<= 64) counter lines at p (kCtrStride apart), polled by a
+// whole wave until it reaches `target`, at most `limit` times; otherwise as
+// poll_until.  Every lane returns the last sum read.
+__device__ __forceinline__ uint32_t wave_poll_sum_until(const uint32_t* p, int n, uint32_t target,
+                                                        uint32_t limit, uint32_t* status,
+                                                        uint32_t bit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t v = 0;
+  for (uint32_t it = 0; it < limit; ++it) {
+    // Counts stay far below 2^24, so the float sum is exact.
+    const float c = lane < n ? (float)load_flag(p + lane * kCtrStride) : 0.f;
+    v = (uint32_t)group_sum<kWave>(c);
+    if (v >= target) return v;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  if (lane == 0) report_giveup(status, bit);
+  return v;
+}
+
 // Keys of chunk p of row b, eight per thread: element
 // p*kLsChunk + wave*512 + i*64 + lane (the select's layout: each wave a
 // contiguous run, ordered compaction by ballots).  Past the row: key 0,
@@ -116,9 +138,9 @@ __device__ __forceinline__ void cand_item(const ScanArgs& a, const LongSelArgs& 
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   for (int i = tid; i < kLsBins; i += kItemThreads) sm.h2[i] = 0;
-  if (tid == 0)
-    poll_until(&a.seq_ctr[b * kCtrStride], (uint32_t)a.items_per_seq, a.spin_limit, a.status,
-               kGiveUpScanCount);
+  if (wave == 0)
+    wave_poll_sum_until(&a.seq_ctr[(b << a.ctr_log2) * kCtrStride], 1 << a.ctr_log2,
+                        (uint32_t)a.items_per_seq, a.spin_limit, a.status, kGiveUpScanCount);
   __syncthreads();
 
   uint32_t key[kSelKpt];
@@ -346,10 +368,10 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
   const BufRsrc h2 = make_rsrc(l.hist2 + (int64_t)b * kLsBins, (uint32_t)(kLsBins * 4));
   for (int i = tid; i < kLsBins / 4; i += kItemThreads) store4_dev(h2, (uint32_t)(i * 16), z);
   if (tid < 3) counter_reset(ls_line(l, b, kLsInfo1) + tid);
+  if (tid < (1 << a.ctr_log2)) counter_reset(&a.seq_ctr[((b << a.ctr_log2) + tid) * kCtrStride]);
   if (tid == 0) {
     counter_reset(ls_line(l, b, kLsCandN));
     counter_reset(ls_line(l, b, kLsCandDone));
-    counter_reset(&a.seq_ctr[b * kCtrStride]);
   }
 }
 
