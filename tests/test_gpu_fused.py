@@ -46,6 +46,10 @@ FUSED_CASES = [
     ("multiturn_b1_n131072_h8", "multiturn_128k", dict(B=1, Hq=8, Hkv=8, T=130, Tmax=256)),
     ("long_k_equals_n", "qwen2_7b_video", dict(N=4100, k=4100, T=16, Tmax=16)),
     ("long_k_one", "multiturn_128k", dict(B=3, N=2049, k=1, Hq=4, Hkv=4, T=8, Tmax=8)),
+    # Long fp32 rows of three chunks, GQA 4: the chunk attention items on the
+    # vector front.
+    ("fp32_long_rows_gqa4", "image576_fp32", dict(B=2, N=5000, k=700, Hq=16, Hkv=4, T=20,
+                                                  Tmax=24, planted=0)),
     ("visual_only", "llava_next_7b", dict(B=2, N=300, k=40, T=0, Tmax=0, planted=0)),
     ("k_one", "llava_next_7b", dict(B=3, N=77, k=1, T=5, Tmax=8, planted=0)),
     ("n_one", "llava_next_7b", dict(B=2, N=1, k=1, T=4, Tmax=4, planted=0)),

@@ -253,10 +253,10 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq, const void* k_vis, i
 // ---------------------------------------------------------------- attention
 // Workspace of sv_sparse_decode_attn: [partials B*Hq*C*(D+4) fp32][counters B*Hkv uint32].
 static size_t attn_partial_bytes(int B, int Hq, int Hkv, int D, int k, int Tmax,
-                                 bool fused = false) {
+                                 bool fused = false, int N = 0) {
   size_t best = 0;
   for (int ve = 4; ve <= 8; ve += 4) {
-    const sv::AttnPlan p = fused ? sv::fused_attn_plan(B, Hkv, D, ve, k, Tmax)
+    const sv::AttnPlan p = fused ? sv::fused_attn_plan(B, Hkv, D, ve, k, Tmax, N)
                                  : sv::attn_plan(B, Hkv, D, ve, k, Tmax, sv::kAttnTargetItems);
     const size_t bytes = (size_t)B * Hq * (p.CT + p.CV) * sv::attn_part_stride(D) * sizeof(float);
     if (bytes > best) best = bytes;
@@ -354,7 +354,7 @@ static size_t fused_enc_bytes(int B, int k) { return align256((size_t)B * k * si
 size_t sv_retrieve_attend_workspace(int B, int Hq, int Hkv, int D, int N, int k, int Tmax) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || N < 1 || k < 0 || Tmax < 0) return kStatusBytes;
   return kStatusBytes + retrieve_scores_bytes(B, N) +
-         attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true) +
+         attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true, N) +
          fused_ctl_bytes(B, Hkv) + fused_enc_bytes(B, k) + sv::long_select_bytes(B, N);
 }
 
@@ -434,7 +434,7 @@ static sv_status retrieve_attend_impl(const char* fn, bool noalloc, const void* 
   f.out = out;
   ws += retrieve_scores_bytes(B, N);
   f.part = (float*)ws;
-  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true);
+  ws += attn_partial_bytes(B, Hq, Hkv, D, k, Tmax, true, N);
   uint32_t* ctl = (uint32_t*)ws;
   f.seq_ctr = ctl;
   f.ready = f.seq_ctr + (size_t)B * sv::kCtrStride;

@@ -42,7 +42,7 @@ AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_i
   return plan(8);
 }
 
-AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax) {
+AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, int N) {
   AttnPlan p = attn_plan(B, Hkv, D, VE, k, Tmax, kFusedAttnTargetItems);
   if (p.EPL < 4) {
     p.EPL = 4;
@@ -50,6 +50,9 @@ AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax) {
     p.CT = (Tmax + p.SE - 1) / p.SE;
     p.CV = (k + p.SE - 1) / p.SE;
   }
+  // Chunk attention: one visual split per 2048-score chunk, whatever its
+  // count of selected tokens (SE per round).
+  if (fused_chunk_attn(B, Hkv, N, k)) p.CV = (N + 2047) / 2048;
   return p;
 }
 

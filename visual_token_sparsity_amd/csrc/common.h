@@ -263,7 +263,11 @@ constexpr long kAttnTargetItems = 2048;       // standalone attention launch
 constexpr long kFusedAttnTargetItems = 2048;  // fused layer: smaller splits start sooner
 AttnPlan attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, long target_items);
 // The fused launch's plan: attn_plan with kFusedAttnTargetItems, 4 or 8 entries per lane.
-AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax);
+AttnPlan fused_attn_plan(int B, int Hkv, int D, int VE, int k, int Tmax, int N);
+// Fused launch over rows longer than one select chunk (2048 scores) with few
+// (sequence, KV head, chunk) triples: the visual attention runs chunk by
+// chunk, one split per chunk, and starts before the threshold is known.
+bool fused_chunk_attn(int B, int Hkv, int N, int k);
 
 hipError_t launch_attn(const void* q, int B, int Hq, const void* kv, const void* vv,
                        int64_t vbs, int64_t vts, int N, int Hkv, int D, const int32_t* idx,

@@ -496,10 +496,14 @@ __device__ __forceinline__ uint16_t attn_bf16_rne(float f) {
 // Matrix-core front of a bf16 item with G >= 2 (see the header): entries
 // [e0, e0 + n_ent) of the split, SE of them at most; writes each wave's
 // (acc, m, l) per head into its LDS slot slot(w, i) = smem + (w*G + i)*(D+2)
-// floats, as the vector front does.
-template <int D, int G, int SE>
+// floats, as the vector front does.  LIST: the entries are the visual tokens
+// list[0 .. n) (LDS), taken SE at a time with the softmax state carried from
+// round to round; n starts at n_ent, and once those are done more() (called
+// by every thread) may append entries and returns the new n, once.
+template <int D, int G, int SE, bool LIST, class More>
 __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g, bool text,
-                                                int e0, int n_ent, bool wait, char* smem) {
+                                                int e0, int n_ent, bool wait, char* smem,
+                                                const int* list, More&& more) {
   static_assert(G >= 2 && G <= 16, "query heads as the columns of one 16-wide tile");
   constexpr int KS = D / 32, DB = D / 16;
   constexpr int TPW = (SE + 16 * kItemWaves - 1) / (16 * kItemWaves);  // tiles per wave
@@ -537,11 +541,32 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
   }
   const uint32_t head_off = (uint32_t)(g * D * 2);
 
+  char* vbuf = smem + wave * attn_mfma_vbuf_bytes<D>();
+  float m = -INFINITY, l = 0.f;  // head li
+  attn_f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
+
   // Token of entry li of each tile (-1: none), polled when the indices come
   // from this kernel.
   int tok[TPW];
   auto entry_of = [&](int tt, int r) { return (tt * kItemWaves + wave) * 16 + r; };
-  if (text) {
+  int n_have = n_ent;
+  bool more_left = LIST;
+  for (int r0 = 0;;) {
+  if constexpr (LIST) {
+    if (r0 >= n_have) {  // uniform
+      if (!more_left) break;
+      more_left = false;
+      n_have = more();
+      if (r0 >= n_have) break;
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int e = r0 + entry_of(tt, li);
+      tok[tt] = e < n_have ? list[e] : -1;
+    }
+  } else if (text) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       const int e = entry_of(tt, li);
@@ -595,11 +620,6 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
     }
   }
 
-  char* vbuf = smem + wave * attn_mfma_vbuf_bytes<D>();
-  float m = -INFINITY, l = 0.f;  // head li
-  attn_f32x4 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     // Entries of this tile that count (bit r: entry r).
@@ -653,6 +673,9 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
       // acc[db][r] = O[head li][dim 16 db + 4 lg + r]
     }
   }
+  if constexpr (!LIST) break;
+  r0 = r0 + SE < n_have ? r0 + SE : n_have;
+  }
   l += xor_partner<16>(l);
   l += xor_partner<32>(l);
 
@@ -672,11 +695,18 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
   }
 }
 
+struct NoMore {
+  __device__ int operator()() const { return 0; }
+};
+
 // Item (b, g, c).  wait: the visual indices are produced by this kernel;
-// poll their encoded copy idx_enc (bounded).
-template <typename T, int D, int G, int EPL>
+// poll their encoded copy idx_enc (bounded).  LIST: split c covers the visual
+// tokens list[0 .. n_list) (LDS) and whatever more() appends after them (see
+// attn_front_mfma), in rounds of the split's entry count.
+template <typename T, int D, int G, int EPL, bool LIST = false, class More = NoMore>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c, bool wait,
-                                          char* smem) {
+                                          char* smem, const int* list = nullptr, int n_list = 0,
+                                          More&& more = More{}) {
   using S = AttnShape<T, D>;
   constexpr int VE = S::VE, LPE = S::LPE, EPW = S::EPW;
   constexpr int SE = kItemWaves * EPW * EPL;
@@ -687,10 +717,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   const T* q = reinterpret_cast<const T*>(a.q);
   const int C = a.CT + a.CV;
 
-  const bool text = c < a.CT;
+  const bool text = !LIST && c < a.CT;
   int n_ent;  // entries of this split
   int e0;     // first entry: text row or position in idx[b]
-  if (text) {
+  if (LIST) {
+    e0 = 0;
+    n_ent = n_list;
+  } else if (text) {
     int tl = a.txt_len ? a.txt_len[b] : 0;
     tl = tl < 0 ? 0 : (tl > a.Tmax ? a.Tmax : tl);
     e0 = c * SE;
@@ -699,13 +732,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     e0 = (c - a.CT) * SE;
     n_ent = a.k - e0;
   }
-  n_ent = n_ent < 0 ? 0 : (n_ent > SE ? SE : n_ent);
+  n_ent = n_ent < 0 ? 0 : (!LIST && n_ent > SE ? SE : n_ent);
 
   float* s_w = reinterpret_cast<float*>(smem);
   auto slot = [&](int w, int i) { return s_w + ((int64_t)w * G + i) * (D + 2); };
   constexpr bool kMfma = std::is_same<T, bf16_t>::value && G >= 2;
   if constexpr (kMfma) {
-    attn_front_mfma<D, G, SE>(a, b, g, text, e0, n_ent, wait, smem);
+    attn_front_mfma<D, G, SE, LIST>(a, b, g, text, e0, n_ent, wait, smem, list, more);
   } else {
     Vec<T> qx[G];
   #pragma unroll
@@ -729,8 +762,39 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
       vrs = make_rsrc(reinterpret_cast<const char*>(a.vv) + (int64_t)b * a.vbs * ES, ext);
     }
     const uint32_t head_off = (uint32_t)((g * D + d0) * ES);
+    float qv[G][VE];
+    float m[G], l[G], acc[G][VE];
+    auto init = [&]() {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        qx[i].to_f32(qv[i]);
+#pragma unroll
+        for (int v = 0; v < VE; ++v) qv[i][v] *= a.qscale;
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+#pragma unroll
+        for (int v = 0; v < VE; ++v) acc[i][v] = 0.f;
+      }
+    };
+    if constexpr (LIST) init();
+    int n_have = n_ent;
+    bool more_left = LIST;
+    for (int r0 = 0, it = 0;; ++it) {
     uint32_t off[EPL];
-    if (text) {
+    if constexpr (LIST) {
+      if (r0 >= n_have) {  // uniform
+        if (!more_left) break;
+        more_left = false;
+        n_have = more();
+        if (r0 >= n_have) break;
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = r0 + (j * kItemWaves + wave) * EPW + eg;
+        const int t = e < n_have ? list[e] : -1;
+        off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
+      }
+    } else if (text) {
   #pragma unroll
       for (int j = 0; j < EPL; ++j) {
         const int e = (j * kItemWaves + wave) * EPW + eg;
@@ -781,22 +845,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
       vx[j].template load_buf<kCacheDefault>(vrs, off[j], 0u);
     }
 
-    float qv[G][VE];
-  #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      qx[i].to_f32(qv[i]);
-  #pragma unroll
-      for (int v = 0; v < VE; ++v) qv[i][v] *= a.qscale;
-    }
-
-    float m[G], l[G], acc[G][VE];
-  #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-  #pragma unroll
-      for (int v = 0; v < VE; ++v) acc[i][v] = 0.f;
-    }
+    if (!LIST && it == 0) init();  // after the loads are issued
 
   #pragma unroll
     for (int j = 0; j < EPL; ++j) {
@@ -823,6 +872,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
           m[i] = mn;
         }
       }
+    }
+    if constexpr (!LIST) break;
+    r0 = r0 + SE < n_have ? r0 + SE : n_have;
     }
 
     // Merge the EPW lane groups of this wave (partner values by DPP and

@@ -24,6 +24,16 @@ static size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
 static bool long_rows(int N) { return N > kItemThreads * kSelKpt; }
 static int long_chunks(int N) { return (N + kLsChunk - 1) / kLsChunk; }
 
+// Chunk attention items, B*Hkv*P of them, each reading its 2048 scores: worth
+// it where they are few (a batch-1 video layer: 52), not for 128k-token rows
+// of many heads (8192 of them, one 8 KB score read each).
+constexpr long kChunkAttnMaxItems = 1024;
+static_assert(kLsChunk == 2048, "fused_attn_plan counts chunks of 2048 scores");
+
+bool fused_chunk_attn(int B, int Hkv, int N, int k) {
+  return long_rows(N) && k > 0 && (long)B * Hkv * long_chunks(N) <= kChunkAttnMaxItems;
+}
+
 size_t long_select_zero_bytes(int B, int N) {
   if (!long_rows(N)) return 0;
   return al256((size_t)B * kLsCtlLines * kCtrStride * 4) +
@@ -93,9 +103,16 @@ hipError_t launch_fused(const FusedLaunch& f, hipStream_t st) {
     w += al256((size_t)f.B * P * 4);
     ls.offs = reinterpret_cast<uint32_t*>(w);
     sa.hist1 = ls.hist1;
+    ls.chunk_attn = !f.retrieve_only && fused_chunk_attn(f.B, f.Hkv, f.N, f.k);
+    ls.readers = (uint32_t)P * (ls.chunk_attn ? 1u + (uint32_t)f.Hkv : 1u);
+    if (ls.chunk_attn) {
+      // Neither the encoded index copy nor ready[b] is waited on.
+      sa.idx_enc = nullptr;
+      sa.ready = nullptr;
+    }
   }
 
-  AttnPlan p = fused_attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax);
+  AttnPlan p = fused_attn_plan(f.B, f.Hkv, f.D, VE, f.k, f.Tmax, f.N);
   if (f.epl > 0) {
     p.EPL = f.epl;
     p.SE = attn_split_entries(VE, f.D, f.epl);

@@ -48,6 +48,52 @@ struct FusedCtl {
   float* scores_out;   // decoded scores (polling mode), may be null
 };
 
+// LDS of a chunk attention item: the attention item's, then the chunk's token
+// list and kItemWaves + 2 words.
+template <int D, int G>
+__host__ __device__ constexpr size_t chunk_list_offset() {
+  return (attn_smem_bytes<D, G>() + 15) & ~(size_t)15;
+}
+template <int D, int G>
+__host__ __device__ constexpr size_t chunk_attn_smem_bytes() {
+  return chunk_list_offset<D, G>() + (size_t)kLsChunk * 4 + (kItemWaves + 2) * 4;
+}
+
+// Long rows, chunk attention: the item of (b, g, p) attends over the selected
+// tokens of score chunk p, the keys above D1 first (as soon as D1 is
+// published), then those of digit D1 under the threshold (once it is).  The
+// compaction items still write idx[b] but no longer gate the attention.
+template <typename T, int D, int G, int EPL>
+__device__ __forceinline__ void chunk_attn_item(const ScanArgs& sa, const AttnArgs& aa,
+                                                const LongSelArgs& ls, int b, int g, int p,
+                                                char* smem) {
+  int* list = reinterpret_cast<int*>(smem + chunk_list_offset<D, G>());
+  uint32_t* wcnt = reinterpret_cast<uint32_t*>(list + kLsChunk);
+  const int tid = threadIdx.x;
+  ChunkSel cs;
+  if (tid == 0)
+    wcnt[kItemWaves] = poll_until(ls_line(ls, b, kLsInfo1) + 3, 1u, sa.spin_limit, sa.status,
+                                  kGiveUpIndices) - 1u;
+  __syncthreads();
+  cs.D1 = wcnt[kItemWaves];
+  load_chunk_keys(sa.scores, sa.N, b, p, cs.key, cs.e0);
+  cs.cend = min(sa.N, (p + 1) * kLsChunk);
+  const int n1 = chunk_list_append(cs, list, wcnt, 0, false, 0u, 0u);
+  auto more = [&]() -> int {
+    if (tid == 0) {
+      poll_until(ls_line(ls, b, kLsThrReady), 1u, sa.spin_limit, sa.status, kGiveUpThreshold);
+      const uint32_t* info2 = ls_line(ls, b, kLsInfo2);
+      wcnt[kItemWaves] = load_flag(info2);
+      wcnt[kItemWaves + 1] = load_flag(info2 + 1);
+      threshold_read_done(ls, b);
+    }
+    __syncthreads();
+    const uint32_t tkey = wcnt[kItemWaves], tidx = wcnt[kItemWaves + 1];
+    return chunk_list_append(cs, list, wcnt, n1, true, tkey, tidx);
+  };
+  attn_item<T, D, G, EPL, true>(aa, b, g, aa.CT + p, false, smem, list, n1, more);
+}
+
 // LONG: rows of more than 2048 tokens (the parallel select); each mode is
 // its own instantiation, so neither carries the other's registers.
 template <typename T, int D, int G, int EPL, bool LONG>
@@ -85,6 +131,13 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   }
   const bool text = t < ctl.text_end;
   uint32_t u = text ? t - ctl.seq_end : t - ctl.text_end;
+  if constexpr (LONG) {
+    if (!text && ls.chunk_attn) {
+      const uint32_t P = (uint32_t)ls.P;
+      chunk_attn_item<T, D, G, EPL>(sa, aa, ls, u / (P * aa.Hkv), (u / P) % aa.Hkv, u % P, smem);
+      return;
+    }
+  }
   const int per = text ? aa.CT : aa.CV;
   const int b = u / (per * aa.Hkv);
   const int g = (u / per) % aa.Hkv;
@@ -114,6 +167,7 @@ static hipError_t fused_go(const ScanArgs& sa, const AttnArgs& aa, const FusedCt
   if (sa.hist1) {
     if (cand_smem_bytes() > lds) lds = cand_smem_bytes();
     if (thr_smem_bytes(ls.P) > lds) lds = thr_smem_bytes(ls.P);
+    if (ls.chunk_attn && chunk_attn_smem_bytes<D, G>() > lds) lds = chunk_attn_smem_bytes<D, G>();
   }
   if (lds > 48 * 1024) {
     static bool raised = false;  // per instantiation; the attribute is per function

@@ -56,9 +56,15 @@ struct LongSelArgs {
   uint32_t* offs;      // [B][P] first output position of chunk p
   // [B][kLsCtlLines] lines of kCtrStride words: cand_n, cand_done,
   // thr_ready (1: compact, 2: already selected), comp_done, info1 (D1,
-  // keys above D1, keys in D1), info2 (T, Ti).
+  // keys above D1, keys in D1, and D1 + 1 published early for the chunk
+  // attention items), info2 (T, Ti).
   uint32_t* ctl;
   int P;               // chunks per row
+  // Items that read (thr_ready, T, Ti) of a sequence: the P compaction items,
+  // plus the Hkv*P chunk attention items when the visual attention runs
+  // chunk by chunk (chunk_attn).  The last of them clears those words.
+  uint32_t readers;
+  bool chunk_attn;
 };
 
 __device__ __forceinline__ uint32_t* ls_line(const LongSelArgs& l, int b, int i) {
@@ -165,6 +171,9 @@ __device__ __forceinline__ void cand_item(const ScanArgs& a, const LongSelArgs& 
   __syncthreads();
   const uint32_t D1 = sm.d1, c1 = sm.c1;
   const bool keep = c1 <= (uint32_t)kLsCandCap;  // uniform
+  // Keys above D1 are selected whatever the threshold: the chunk attention
+  // items start on them now.
+  if (l.chunk_attn && p == 0 && tid == 0) store_flag(ls_line(l, b, kLsInfo1) + 3, D1 + 1u);
 
   uint32_t hi = 0, nc = 0;
 #pragma unroll
@@ -252,7 +261,7 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
   __builtin_amdgcn_s_setprio(3);  // every later item of b waits on this one
 
   const uint32_t* info = ls_line(l, b, kLsInfo1);
-  const uint32_t D1 = load_flag(info + 0), above1 = load_flag(info + 1), c1 = load_flag(info + 2);
+  const uint32_t above1 = load_flag(info + 1), c1 = load_flag(info + 2);
   {
     const BufRsrc hr = make_rsrc(l.hist2 + (int64_t)b * kLsBins, (uint32_t)(kLsBins * 4));
     const u32x4 s0 = load4_dev(hr, (uint32_t)(4 * tid * 4));
@@ -353,7 +362,8 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
     SelectSmem<kItemWaves>& ss = *reinterpret_cast<SelectSmem<kItemWaves>*>(smem);
     block_topk<kItemWaves, kSelKpt, true, false>(a.scores + (int64_t)b * a.N, a.N, a.k,
                                                  a.idx + (int64_t)b * a.k, ss, nullptr,
-                                                 a.idx_enc ? a.idx_enc + (int64_t)b * a.k : nullptr);
+                                                 a.idx_enc ? a.idx_enc + (int64_t)b * a.k : nullptr,
+                                                 ls_line(l, b, kLsInfo2));
   }
   wait_stores_complete();
   __syncthreads();
@@ -373,6 +383,19 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
     counter_reset(ls_line(l, b, kLsCandN));
     counter_reset(ls_line(l, b, kLsCandDone));
   }
+}
+
+// One reader of (thr_ready, T, Ti) of b is done with them (thread 0); the
+// last of l.readers clears them, and the early D1, for the next launch, and
+// returns true.
+__device__ __forceinline__ bool threshold_read_done(const LongSelArgs& l, int b) {
+  if (counter_add(ls_line(l, b, kLsCompDone), 1u) != l.readers - 1) return false;
+  counter_reset(ls_line(l, b, kLsCompDone));
+  counter_reset(ls_line(l, b, kLsThrReady));
+  counter_reset(ls_line(l, b, kLsInfo2));
+  counter_reset(ls_line(l, b, kLsInfo2) + 1);
+  if (l.chunk_attn) counter_reset(ls_line(l, b, kLsInfo1) + 3);
+  return true;
 }
 
 // ---------------------------------------------------------------- compact item
@@ -430,13 +453,58 @@ __device__ __forceinline__ void compact_item(const ScanArgs& a, const LongSelArg
   }
   wait_stores_complete();
   __syncthreads();
-  if (tid == 0 && counter_add(ls_line(l, b, kLsCompDone), 1u) == (uint32_t)l.P - 1) {
-    counter_reset(ls_line(l, b, kLsCompDone));
-    counter_reset(ls_line(l, b, kLsThrReady));
-    counter_reset(ls_line(l, b, kLsInfo2));
-    counter_reset(ls_line(l, b, kLsInfo2) + 1);
-    if (a.ready) store_flag(&a.ready[b * kCtrStride], 1u);
+  if (tid == 0 && threshold_read_done(l, b) && a.ready) store_flag(&a.ready[b * kCtrStride], 1u);
+}
+
+// ---------------------------------------------------------------- chunk attention lists
+// The selected tokens of chunk p of row b, for the attention item of (b, g, p)
+// (every thread calls): first the keys above D1 (selected whatever the
+// threshold), once D1 is published; then, through more(), the selected keys
+// of digit D1 ({key > T, or key == T and index <= Ti}, the select's rule),
+// once the threshold is.  Both lists are in ascending token order, written
+// to list (LDS, kLsChunk entries); wcnt is kItemWaves + 2 words of LDS.
+struct ChunkSel {
+  uint32_t key[kSelKpt];
+  int e0, cend;
+  uint32_t D1;
+};
+
+// Appends to list[base ..] the chunk's keys above D1 (tail false) or its
+// selected keys of digit D1 under the threshold (T, Ti) (tail true); returns
+// the new length.
+__device__ __forceinline__ int chunk_list_append(const ChunkSel& cs, int* list, uint32_t* wcnt,
+                                                 int base, bool tail, uint32_t T, uint32_t Ti) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  bool sel[kSelKpt];
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < kSelKpt; ++i) {
+    const int e = cs.e0 + i * kWave;
+    const uint32_t d = digit1(cs.key[i]);
+    sel[i] = e < cs.cend &&
+             (tail ? (d == cs.D1 && (cs.key[i] > T || (cs.key[i] == T && (uint32_t)e <= Ti)))
+                   : d > cs.D1);
+    n += (uint32_t)__popcll(__ballot(sel[i]));
   }
+  if (lane == 0) wcnt[wave] = n;
+  __syncthreads();
+  int pos = base, total = 0;
+#pragma unroll
+  for (int w = 0; w < kItemWaves; ++w) {
+    pos += w < wave ? (int)wcnt[w] : 0;
+    total += (int)wcnt[w];
+  }
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int i = 0; i < kSelKpt; ++i) {
+    const uint64_t bm = __ballot(sel[i]);
+    if (sel[i]) list[pos + __popcll(bm & lt)] = cs.e0 + i * kWave;
+    pos += __popcll(bm);
+  }
+  __syncthreads();
+  return base + total;
 }
 
 }  // namespace sv
