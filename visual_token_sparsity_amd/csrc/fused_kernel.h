@@ -81,10 +81,17 @@ __device__ __forceinline__ void chunk_attn_item(const ScanArgs& sa, const AttnAr
   const int n1 = chunk_list_append(cs, list, wcnt, 0, false, 0u, 0u);
   auto more = [&]() -> int {
     if (tid == 0) {
-      poll_until(ls_line(ls, b, kLsThrReady), 1u, sa.spin_limit, sa.status, kGiveUpThreshold);
-      const uint32_t* info2 = ls_line(ls, b, kLsInfo2);
-      wcnt[kItemWaves] = load_flag(info2);
-      wcnt[kItemWaves + 1] = load_flag(info2 + 1);
+      // The threshold element, published as one word T | (Ti + 1) << 32.
+      const uint64_t* pub = thr_pub_word(ls, b);
+      uint64_t w = 0;
+      for (uint32_t n = 0; n < sa.spin_limit; ++n) {
+        w = __hip_atomic_load(pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (w) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!w) report_giveup(sa.status, kGiveUpThreshold);
+      wcnt[kItemWaves] = (uint32_t)w;
+      wcnt[kItemWaves + 1] = (uint32_t)(w >> 32) - 1u;
       threshold_read_done(ls, b);
     }
     __syncthreads();

@@ -72,6 +72,12 @@ __device__ __forceinline__ uint32_t* ls_line(const LongSelArgs& l, int b, int i)
 }
 enum { kLsCandN = 0, kLsCandDone = 1, kLsThrReady = 2, kLsCompDone = 3, kLsInfo1 = 4, kLsInfo2 = 5 };
 
+// Chunk attention: (T, Ti) as one 64-bit word, T | (Ti + 1) << 32 (zero: not
+// published yet), in words 2-3 of the info2 line.
+__device__ __forceinline__ uint64_t* thr_pub_word(const LongSelArgs& l, int b) {
+  return reinterpret_cast<uint64_t*>(ls_line(l, b, kLsInfo2) + 2);
+}
+
 __device__ __forceinline__ uint32_t digit1(uint32_t key) { return key >> 21; }
 __device__ __forceinline__ uint32_t digit2(uint32_t key) { return (key >> 10) & (kLsBins - 1); }
 
@@ -283,33 +289,39 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
     const uint32_t D2 = sm.d2, c2 = sm.c2;
     fallback = c2 > (uint32_t)kLsFinalCap;
     if (!fallback) {
-      // Candidates of D1: those above D2 are taken; those in D2 go to LDS.
+      // Candidates of D1: those above D2 are taken (counted per chunk for the
+      // compaction offsets); those in D2 go to LDS.  With chunk attention the
+      // counting waits until the threshold is published: the attention items
+      // wait on the threshold, only the compaction items on the counts.
       const uint64_t* cl = l.cand + (int64_t)b * kLsCandCap;
-      for (uint32_t s0 = 0; s0 < c1; s0 += 8 * kItemThreads) {
-        uint64_t c[8];
+      auto cand_pass = [&](bool count, bool collect) {
+        for (uint32_t s0 = 0; s0 < c1; s0 += 8 * kItemThreads) {
+          uint64_t c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t s = s0 + (uint32_t)(j * kItemThreads + tid);
-          c[j] = s < c1 ? __hip_atomic_load(cl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-        }
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t s = s0 + (uint32_t)(j * kItemThreads + tid);
+            c[j] = s < c1 ? __hip_atomic_load(cl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+          }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t s = s0 + (uint32_t)(j * kItemThreads + tid);
-          if (s < c1) {
-            const uint32_t kk = (uint32_t)c[j], e = (uint32_t)(c[j] >> 32);
-            const uint32_t d = digit2(kk);
-            if (d > D2) {
-              atomicAdd(&sm.cnt[min(e / kLsChunk, (uint32_t)P - 1)], 1u);
-            } else if (d == D2) {
-              const uint32_t f = atomicAdd(&sm.nfin, 1u);
-              if (f < (uint32_t)kLsFinalCap) {
-                sm.fk[f] = kk;
-                sm.fi[f] = e;
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t s = s0 + (uint32_t)(j * kItemThreads + tid);
+            if (s < c1) {
+              const uint32_t kk = (uint32_t)c[j], e = (uint32_t)(c[j] >> 32);
+              const uint32_t d = digit2(kk);
+              if (d > D2) {
+                if (count) atomicAdd(&sm.cnt[min(e / kLsChunk, (uint32_t)P - 1)], 1u);
+              } else if (d == D2 && collect) {
+                const uint32_t f = atomicAdd(&sm.nfin, 1u);
+                if (f < (uint32_t)kLsFinalCap) {
+                  sm.fk[f] = kk;
+                  sm.fi[f] = e;
+                }
               }
             }
           }
         }
-      }
+      };
+      cand_pass(!l.chunk_attn, true);
       __syncthreads();
       // The rem2-th of (D1, D2) by (key descending, index ascending) is the threshold.
       const uint32_t rem2 = rem1 - sm.above2;  // 1 <= rem2 <= c2
@@ -330,6 +342,12 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
       }
       __syncthreads();
       const uint32_t T = sm.tkey, Ti = sm.tidx;
+      if (l.chunk_attn) {
+        if (tid == 0)
+          __hip_atomic_store(thr_pub_word(l, b), (uint64_t)T | ((uint64_t)(Ti + 1u) << 32),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        cand_pass(true, false);
+      }
       if (mine && (mk > T || (mk == T && mi <= Ti)))
         atomicAdd(&sm.cnt[min(mi / kLsChunk, (uint32_t)P - 1)], 1u);
       __syncthreads();
@@ -363,7 +381,7 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
     block_topk<kItemWaves, kSelKpt, true, false>(a.scores + (int64_t)b * a.N, a.N, a.k,
                                                  a.idx + (int64_t)b * a.k, ss, nullptr,
                                                  a.idx_enc ? a.idx_enc + (int64_t)b * a.k : nullptr,
-                                                 ls_line(l, b, kLsInfo2));
+                                                 l.chunk_attn ? thr_pub_word(l, b) : nullptr);
   }
   wait_stores_complete();
   __syncthreads();
@@ -394,7 +412,10 @@ __device__ __forceinline__ bool threshold_read_done(const LongSelArgs& l, int b)
   counter_reset(ls_line(l, b, kLsThrReady));
   counter_reset(ls_line(l, b, kLsInfo2));
   counter_reset(ls_line(l, b, kLsInfo2) + 1);
-  if (l.chunk_attn) counter_reset(ls_line(l, b, kLsInfo1) + 3);
+  if (l.chunk_attn) {
+    counter_reset(ls_line(l, b, kLsInfo1) + 3);
+    __hip_atomic_store(thr_pub_word(l, b), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   return true;
 }
 

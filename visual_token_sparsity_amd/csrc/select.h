@@ -92,13 +92,13 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* h, int nb, uint3
 // everything, write nothing (runs the code once, e.g. to warm the
 // instruction cache while waiting for the scores).  out_enc: also write
 // each index plus one there (device-coherent; zero means not written).
-// thr_out: also write the threshold element (T_key, T_idx) there
-// (device-coherent).
+// thr_pub: also publish the threshold element there as one device-coherent
+// 64-bit word, T_key | (T_idx + 1) << 32 (never zero).
 template <int NW, int KPT, bool Coherent, bool Cached>
 __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int32_t* __restrict__ out,
                            SelectSmem<NW>& sm, const uint32_t* pre = nullptr,
                            uint32_t* __restrict__ out_enc = nullptr,
-                           uint32_t* __restrict__ thr_out = nullptr) {
+                           uint64_t* __restrict__ thr_pub = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -282,10 +282,9 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
     thr_idx = sm.thr_idx;
   }
 
-  if (thr_out && tid == 0) {
-    __hip_atomic_store(thr_out, thr_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(thr_out + 1, thr_idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (thr_pub && tid == 0)
+    __hip_atomic_store(thr_pub, (uint64_t)thr_key | ((uint64_t)(thr_idx + 1u) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- stable compaction of {e : key_e > T_key or (key_e == T_key and e <= T_idx)}
   auto selected = [&](int e, bool valid, uint32_t kk) {
