@@ -953,7 +953,44 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
 
   // out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
   const float* pb = a.part + head0 * C * PS;  // this (b, g): [G][C][PS]
-  if (C <= kMaxCombineSplits) {
+  constexpr int V1 = G * D / 4;
+  constexpr bool kOnline = LIST && kMfma && combine_groups<D, G>() == 1;
+  constexpr int CB1 = 20;
+  if (kOnline && C <= CB1) {
+    // Chunk attention (few splits, one thread per float4 column): each thread
+    // loads its column and (m, l) of every split in one round trip and merges
+    // them online, rescaling as the maximum rises; no LDS and no barrier.
+    if (tid < V1) {
+      const int i = tid / (D / 4), d4 = tid % (D / 4);
+      const BufRsrc pr = make_rsrc(pb, (uint32_t)(G * C * PS * 4));
+      const uint32_t col = (uint32_t)(i * C * PS + 4 * d4) * 4u;
+      const float* mlp = pb + (int64_t)i * C * PS + D;
+      f32x4v x[CB1];
+      float mc[CB1], lc[CB1];
+#pragma unroll
+      for (int j = 0; j < CB1; ++j) {
+        x[j] = __builtin_bit_cast(f32x4v, load4_dev(pr, j < C ? col + (uint32_t)(j * PS * 4) : kBufOob));
+        mc[j] = j < C ? load_shared_dev(mlp + (int64_t)j * PS) : -INFINITY;
+        lc[j] = j < C ? load_shared_dev(mlp + (int64_t)j * PS + 1) : 0.f;
+      }
+      float M = -INFINITY, den = 0.f;
+      f32x4v num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < CB1; ++j) {
+        if (mc[j] != -INFINITY) {
+          const float mn = fmaxf(M, mc[j]);
+          const float a0 = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+          const float a1 = fast_exp2(mc[j] - mn);
+          num = num * a0 + a1 * x[j];
+          den = den * a0 + a1 * lc[j];
+          M = mn;
+        }
+      }
+      float* o = a.out + (head0 + i) * D + 4 * d4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = den > 0.f ? num[j] / den : 0.f;
+    }
+  } else if (C <= kMaxCombineSplits) {
     // Thread (v, s) sums float4 column v over splits s, s+S, ...; its first
     // 8 loads go out together with the (m, l) loads of every split (to LDS),
     // so up to 8 S splits merge in one round trip (8, not more: the batch's
