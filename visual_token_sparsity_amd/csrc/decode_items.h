@@ -990,6 +990,70 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = den > 0.f ? num[j] / den : 0.f;
     }
+  } else if (C <= 4 * combine_groups<D, G>()) {
+    // Up to 4 splits per thread: thread (v, s) loads column v and (m, l) of
+    // splits s, s + S, ... in one round trip and merges them online; the S
+    // groups of a column then meet once in LDS.
+    constexpr int S = combine_groups<D, G>();
+    const int v = tid % V1, s = tid / V1;
+    const int i = v / (D / 4), d4 = v % (D / 4);
+    const BufRsrc pr = make_rsrc(pb, (uint32_t)(G * C * PS * 4));
+    const uint32_t col = (uint32_t)(i * C * PS + 4 * d4) * 4u;
+    const float* mlp = pb + (int64_t)i * C * PS + D;
+    f32x4v x[4];
+    float mc[4], lc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cc = s + j * S;
+      const bool ok = s < S && cc < C;
+      x[j] = __builtin_bit_cast(f32x4v, load4_dev(pr, ok ? col + (uint32_t)(cc * PS * 4) : kBufOob));
+      mc[j] = ok ? load_shared_dev(mlp + (int64_t)cc * PS) : -INFINITY;
+      lc[j] = ok ? load_shared_dev(mlp + (int64_t)cc * PS + 1) : 0.f;
+    }
+    float M = -INFINITY, den = 0.f;
+    f32x4v num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (mc[j] != -INFINITY) {
+        const float mn = fmaxf(M, mc[j]);
+        const float a0 = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+        const float a1 = fast_exp2(mc[j] - mn);
+        num = num * a0 + a1 * x[j];
+        den = den * a0 + a1 * lc[j];
+        M = mn;
+      }
+    }
+    if constexpr (S > 1) {
+      f32x4v* s_num = reinterpret_cast<f32x4v*>(smem);  // [S][V]
+      float* s_m = reinterpret_cast<float*>(s_num + S * V1);
+      float* s_d = s_m + S * V1;
+      if (s < S) {
+        s_num[tid] = num;
+        s_m[tid] = M;
+        s_d[tid] = den;
+      }
+      __syncthreads();
+      if (s == 0) {
+        float Mt = M;
+#pragma unroll
+        for (int r = 1; r < S; ++r) Mt = fmaxf(Mt, s_m[r * V1 + v]);
+        const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - Mt);
+        num = num * f0;
+        den = den * f0;
+#pragma unroll
+        for (int r = 1; r < S; ++r) {
+          const float mr = s_m[r * V1 + v];
+          const float fr = mr == -INFINITY ? 0.f : fast_exp2(mr - Mt);
+          num += fr * s_num[r * V1 + v];
+          den += fr * s_d[r * V1 + v];
+        }
+      }
+    }
+    if (s == 0) {
+      float* o = a.out + (head0 + i) * D + 4 * d4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = den > 0.f ? num[j] / den : 0.f;
+    }
   } else if (C <= kMaxCombineSplits) {
     // Thread (v, s) sums float4 column v over splits s, s+S, ...; its first
     // 8 loads go out together with the (m, l) loads of every split (to LDS),
