@@ -117,3 +117,21 @@ def test_prefill_strided_caches_and_workspace_reuse():
     ok, err = accept.check_attention(a[0].cpu().numpy().reshape(B * Tq, Hq, D),
                                      ref.reshape(B * Tq, Hq, D))
     assert ok, err
+
+
+def test_prefill_long_rows_workspace_reuse_new_inputs():
+    """Rows over 2048 tokens take the parallel select, whose control words the
+    call leaves at zero: a second call on the same workspace with other inputs
+    selects its own top-k (stale threshold words would select the first
+    call's)."""
+    B, Tq, Hq, Hkv, D, N, Tmax, k = 1, 4, 8, 8, 128, 5000, 16, 700
+    _say("prefill long rows, workspace reuse", B, Tq, Hq, Hkv, D, N, Tmax, k)
+    ws = sv.new_workspace(sv.prefill_attend_retrieve_workspace_bytes(B, Tq, Hq, Hkv, D, N, Tmax), DEV)
+    txt = torch.tensor([16], dtype=torch.int32)
+    for seed in (11, 12, 13):
+        q, kv, vv, kt, vt = _inputs(B, Tq, Hq, Hkv, D, N, Tmax, seed=seed)
+        _, idx = sv.prefill_attend_retrieve(q.to(DEV), kv.to(DEV), vv.to(DEV), kt.to(DEV),
+                                            vt.to(DEV), txt.to(DEV), k, workspace=ws)
+        torch.cuda.synchronize()
+        ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), oracle.retrieval_scores(q, kv), k)
+        assert ok, (seed, msgs[:3])

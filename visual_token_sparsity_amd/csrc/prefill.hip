@@ -757,6 +757,7 @@ hipError_t launch_prefill_long_select(const PrefillArgs& a, hipStream_t st) {
   };
   LongSelArgs ls{};
   ls.P = P;
+  ls.readers = (uint32_t)P;  // the compaction items read the threshold
   ls.ctl = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsCtlLines * kCtrStride * 4));
   ls.hist1 = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsReps * kLsBins * 4));
   ls.hist2 = reinterpret_cast<uint32_t*>(take((size_t)a.B * kLsBins * 4));
