@@ -143,7 +143,10 @@ __device__ __forceinline__ float sum_lanes_rt(float v, int width) {
 // One scan item: rows [item*rows_per_item, ...) of sequence b.  Returns true
 // in every thread of the workgroup that must run the select for b.  q_of is
 // the sequence whose qhat LDS holds (-1: none); it is reused when it matches.
-template <typename T, int CPL = kScanCpl>
+// PAIR: one-segment rows take their two units of keys together, each qhat
+// read feeding both FMA chains (more registers, half the LDS reads and two
+// independent chains; each chain adds in the same order, so the same bits).
+template <typename T, int CPL = kScanCpl, bool PAIR = false>
 __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, char* smem,
                                           int& q_of) {
   constexpr int VE = Vec<T>::kElems;
@@ -264,6 +267,20 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   const bool coherent = a.k > 0;
   float* srow = a.scores + (int64_t)b * a.N + r0;
   float acc = 0.f;
+  // The reduced score s of unit u's row (lanes with sub == 0 store it).
+  auto store_score = [&](float s, int u) {
+    const int row = unit_row(u);
+    if (sub == 0 && u < nunits && row < nrows) {
+      if (a.encode)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + row, ~__float_as_uint(s),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (coherent) {
+        store_shared_dev(srow + row, s);  // read back by the selecting workgroup
+        if (a.hist1) atomicAdd(&lh[float_key(s) >> 21], 1u);
+      } else
+        srow[row] = s;
+    }
+  };
   // Unit u (keys in cur): the lanes' partial dot products, reduced and stored
   // at the row's last segment.
   auto consume = [&](Vec<T>* cur, int u) {
@@ -284,29 +301,54 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
       }
     }
     if (seg == nseg - 1) {
-      const float s = sum_lanes_rt(acc, LPR);
+      store_score(sum_lanes_rt(acc, LPR), u);
       acc = 0.f;
-      const int row = unit_row(u);
-      if (sub == 0 && u < nunits && row < nrows) {
-        if (a.encode)
-          __hip_atomic_store(reinterpret_cast<uint32_t*>(srow) + row, ~__float_as_uint(s),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else if (coherent) {
-          store_shared_dev(srow + row, s);  // read back by the selecting workgroup
-          if (a.hist1) atomicAdd(&lh[float_key(s) >> 21], 1u);
-        } else
-          srow[row] = s;
+    }
+  };
+  auto consume2 = [&](Vec<T>* ca, int ua, Vec<T>* cb, int ub) {
+    mask_ragged(ua, ca);
+    mask_ragged(ub, cb);
+    float xa = 0.f, xb = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int ch = sub + j * LPR;
+      float fa[VE], fb[VE];
+      ca[j].to_f32(fa);
+      cb[j].to_f32(fb);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const f32x4v w = *reinterpret_cast<const f32x4v*>(qh + ((int64_t)p * CP + ch) * 4);
+        xa = fmaf(w.x, fa[4 * p], xa);
+        xb = fmaf(w.x, fb[4 * p], xb);
+        xa = fmaf(w.y, fa[4 * p + 1], xa);
+        xb = fmaf(w.y, fb[4 * p + 1], xb);
+        xa = fmaf(w.z, fa[4 * p + 2], xa);
+        xb = fmaf(w.z, fb[4 * p + 2], xb);
+        xa = fmaf(w.w, fa[4 * p + 3], xa);
+        xb = fmaf(w.w, fb[4 * p + 3], xb);
       }
     }
+    store_score(sum_lanes_rt(xa, LPR), ua);
+    store_score(sum_lanes_rt(xb, LPR), ub);
   };
   // Two buffers, each refilled right after it is consumed, so two units per
   // lane stay in flight (steps are wave-uniform).
-  for (int u0 = 0; u0 < nunits; u0 += 2 * RPS) {
-    consume(va, u0 + rsub);
-    if (u0 + 2 * RPS < nunits) load_unit(u0 + 2 * RPS + rsub, va);
-    if (u0 + RPS < nunits) {
-      consume(vb, u0 + RPS + rsub);
+  if (PAIR && nseg == 1) {
+    int u0 = 0;
+    for (; u0 + RPS < nunits; u0 += 2 * RPS) {
+      consume2(va, u0 + rsub, vb, u0 + RPS + rsub);
+      if (u0 + 2 * RPS < nunits) load_unit(u0 + 2 * RPS + rsub, va);
       if (u0 + 3 * RPS < nunits) load_unit(u0 + 3 * RPS + rsub, vb);
+    }
+    if (u0 < nunits) consume(va, u0 + rsub);
+  } else {
+    for (int u0 = 0; u0 < nunits; u0 += 2 * RPS) {
+      consume(va, u0 + rsub);
+      if (u0 + 2 * RPS < nunits) load_unit(u0 + 2 * RPS + rsub, va);
+      if (u0 + RPS < nunits) {
+        consume(vb, u0 + RPS + rsub);
+        if (u0 + 3 * RPS < nunits) load_unit(u0 + 3 * RPS + rsub, vb);
+      }
     }
   }
 

@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
     const uint32_t S = (uint32_t)sa.items_per_seq, P = (uint32_t)ls.P;
     uint32_t u = t;
     if (u < ctl.B * S) {
-      scan_item<T, kScanCpl>(sa, u / S, u % S, smem, q_of);
+      // G >= 2: the attention items set the registers, so the scan can pair rows.
+      scan_item<T, kScanCpl, (G >= 2)>(sa, u / S, u % S, smem, q_of);
     } else if ((u -= ctl.B * S) < ctl.B * P) {
       cand_item(sa, ls, u / P, u % P, smem);
     } else if ((u -= ctl.B * P) < ctl.B) {
