@@ -265,10 +265,12 @@ def _al256(n):
 def _long_zero_span(B, N, total):
     """Byte range of the long-row control lines and histograms (zero between
     launches): the tail of the workspace is [control lines 6 per sequence]
-    [hist1 8 x 2048 words][hist2 2048 words][candidates 16384 x 8 bytes]
-    [two arrays of ceil(N / 2048) words], each part 256-byte aligned."""
+    [scan count lines 16 per sequence][hist1 8 x 2048 words][hist2 2048 words]
+    [candidates 16384 x 8 bytes][two arrays of ceil(N / 2048) words], each part
+    256-byte aligned."""
     P = (N + 2047) // 2048
-    zero = _al256(B * 6 * 128) + _al256(B * 8 * 2048 * 4) + _al256(B * 2048 * 4)
+    zero = (_al256(B * 6 * 128) + _al256(B * 16 * 128) + _al256(B * 8 * 2048 * 4) +
+            _al256(B * 2048 * 4))
     long_total = zero + _al256(B * 16384 * 8) + 2 * _al256(B * P * 4)
     start = total - long_total
     return start, start + zero
