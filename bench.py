@@ -523,7 +523,6 @@ def bench_packed(a, dev, stream, w, layers):
     question = torch.randn((w.B, 8, w.Hq, w.D), generator=gq, device=dev).to(w.dtype)
     idx = [sv.retrieve(question, d["k_vis"], w.k, workspace=ws_r) for d in layers]
     packs = [sv.pack_selected(d["k_vis"], d["v_vis"], i) for d, i in zip(layers, idx)]
-    ar = torch.arange(w.k, dtype=torch.int32, device=dev).expand(w.B, w.k).contiguous()
     out = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in layers]
     torch.cuda.synchronize()
 
@@ -546,7 +545,8 @@ def bench_packed(a, dev, stream, w, layers):
     def packed_step():
         for l, d in enumerate(layers):
             kp, vp = packs[l]
-            sv.sparse_decode_attn(d["q"], kp, vp, ar, d["k_txt"], d["v_txt"], d["txt_len"],
+            # The packed rows are the selection: no index list (rows 0..k-1).
+            sv.sparse_decode_attn(d["q"], kp, vp, w.k, d["k_txt"], d["v_txt"], d["txt_len"],
                                   workspace=ws_a, out=out[l])
 
     with torch.cuda.stream(stream):
@@ -565,7 +565,7 @@ def bench_packed(a, dev, stream, w, layers):
         pack_secs = gpu_time(run_pack, reps, stream) / (reps * len(layers))
         step_secs = gpu_time(run_step, a.steps, stream) / a.steps
     q = w.Hq * w.D * e
-    step_bytes = w.L * w.B * ((w.k + w.T) * 2 * row + q + w.k * 4 + w.Hq * w.D * 4)
+    step_bytes = w.L * w.B * ((w.k + w.T) * 2 * row + q + w.Hq * w.D * 4)
     pack_gbs = pack_bytes / pack_secs / 1e9
     step_gbs = step_bytes / step_secs / 1e9
     return {"question_tokens": 8,
@@ -578,7 +578,7 @@ def bench_packed(a, dev, stream, w, layers):
                                                                source_hash(*PACK_SOURCES))},
                      "launches_per_question": w.L,
                      "ms_per_question": round(pack_secs * w.L * 1e3, 4)},
-            "decode": {"what": "sv_sparse_decode_attn over packed rows 0..k-1 plus text, every layer",
+            "decode": {"what": "sv_sparse_decode_attn over packed rows 0..k-1 (no index list) plus text, every layer",
                        "steps_per_s": round(1.0 / step_secs, 2),
                        "ms_per_step": round(step_secs * 1e3, 4), "bytes_per_step": step_bytes,
                        "hbm_gbs_algorithmic": round(step_gbs, 1),

@@ -164,7 +164,10 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq,
  *             post-RoPE queries).
  *  k_vis,v_vis visual cache, element (b,t,g,d) at
  *             ptr[b*vis_bstride + t*vis_tstride + g*D + d].  Read only.
- *  idx        [B][k] int32 visual token indices (any order; distinct).
+ *  idx        [B][k] int32 visual token indices (any order; distinct), or
+ *             NULL: the visual entries are rows 0..k-1 of the visual cache (a
+ *             packed cache such as sv_pack_selected writes; no index list is
+ *             read).
  *  k_txt,v_txt text cache, element (b,t,g,d) at
  *             ptr[b*txt_bstride + t*txt_tstride + g*D + d], t < Tmax.
  *             May be NULL only if Tmax == 0.
@@ -178,7 +181,8 @@ sv_status sv_retrieve(const void* q, int B, int Tq, int Hq,
  *             so the workspace can be reused without clearing.
  * Supported: dtype SV_BF16 or SV_F32; D in {64, 128}; Hq/Hkv in 1..8.
  * Errors: SV_EINVAL (k < 0, k + Tmax == 0, k > N, Hq % Hkv != 0, NULL
- * required pointer, B < 1), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ * required pointer (q, out, workspace; the caches when k > 0; the text
+ * arrays when Tmax > 0), B < 1), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
  * ---------------------------------------------------------------------- */
 size_t sv_sparse_decode_attn_workspace(int B, int Hq, int Hkv, int D, int k, int Tmax);
 

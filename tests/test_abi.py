@@ -120,7 +120,7 @@ def _attn(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k=101), 1), (dict(k=-1), 1), (dict(k=0, Tmax=0), 1), (dict(Hq=30), 1),
-    (dict(idx=None), 1), (dict(kt=None), 1), (dict(tl=None), 1), (dict(out=None), 1),
+    (dict(kv=None), 1), (dict(kt=None), 1), (dict(tl=None), 1), (dict(out=None), 1),
     (dict(vts=500), 1), (dict(B=0), 1),
     (dict(Hq=36, Hkv=4), 2), (dict(D=80), 2), (dict(dt=3), 2),
     (dict(wsb=16), 3),

@@ -120,9 +120,13 @@ def test_question_retrieve_pack_then_decode_steps(wl, ov):
         q = torch.randn((w.B, w.Hq, w.D), generator=gq).to(w.dtype)
         tl = torch.tensor([w.T - step - b for b in range(w.B)], dtype=torch.int32)
         out_p = sv.sparse_decode_attn(q.to(DEV), kp, vp, ar, g["k_txt"], g["v_txt"], tl.to(DEV))
+        # No index list: the packed rows 0..k-1 themselves, the same entries in
+        # the same order, so the same bits.
+        out_r = sv.sparse_decode_attn(q.to(DEV), kp, vp, w.k, g["k_txt"], g["v_txt"], tl.to(DEV))
         out_s = sv.sparse_decode_attn(q.to(DEV), g["k_vis"], g["v_vis"], idx, g["k_txt"], g["v_txt"],
                                       tl.to(DEV))
         torch.cuda.synchronize()
+        assert torch.equal(out_r, out_p), step
         ref = oracle.sparse_decode_attn(q, d["k_vis"], d["v_vis"], idx_np, d["k_txt"], d["v_txt"], tl)
         ok, err = accept.check_attention(out_p.cpu().numpy(), ref)
         assert ok, (step, err)

@@ -270,7 +270,7 @@ def sparse_decode_attn_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, k: int
 
 
 def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor,
-                       idx: torch.Tensor, k_txt: Optional[torch.Tensor],
+                       idx: "torch.Tensor | int", k_txt: Optional[torch.Tensor],
                        v_txt: Optional[torch.Tensor], txt_len: Optional[torch.Tensor],
                        scale: Optional[float] = None, *,
                        workspace: Optional[torch.Tensor] = None,
@@ -279,7 +279,7 @@ def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor
 
     q        [B][Hq][D] (or [B][1][Hq][D])
     k_vis, v_vis  [B][N][Hkv][D] (same strides)
-    idx      int32 [B][k]
+    idx      int32 [B][k], or an int k: the visual rows 0..k-1 (a packed cache; no index list)
     k_txt, v_txt  [B][Tmax][Hkv][D] (same strides) or None
     txt_len  int32 [B] on the device (rows attended), or None when there is no text
     returns fp32 [B][Hq][D]
@@ -287,17 +287,22 @@ def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor
     lib = load()
     if q.dim() == 4:
         q = q[:, 0]
-    dev = _on_gpu(q, k_vis, v_vis, idx, k_txt, v_txt, txt_len)
+    rows = isinstance(idx, int)
+    dev = _on_gpu(q, k_vis, v_vis, None if rows else idx, k_txt, v_txt, txt_len)
     q = q.contiguous()
     B, Hq, D = q.shape
     _, N, Hkv, _ = k_vis.shape
     if k_vis.stride() != v_vis.stride() or k_vis.shape != v_vis.shape:
         raise ValueError("k_vis and v_vis must share shape and strides")
     vbs, vts = _cache_strides(k_vis, "k_vis")
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
-    idx = idx.contiguous()
-    k = idx.shape[1]
+    if rows:
+        k = idx
+        idx = None
+    else:
+        if idx.dtype != torch.int32:
+            raise TypeError("idx must be int32")
+        idx = idx.contiguous()
+        k = idx.shape[1]
     if k_txt is not None:
         if k_txt.stride() != v_txt.stride() or k_txt.shape != v_txt.shape:
             raise ValueError("k_txt and v_txt must share shape and strides")
@@ -313,7 +318,7 @@ def sparse_decode_attn(q: torch.Tensor, k_vis: torch.Tensor, v_vis: torch.Tensor
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     _check(lib.sv_sparse_decode_attn(
         q.data_ptr(), B, Hq, k_vis.data_ptr(), v_vis.data_ptr(), vbs, vts, N, Hkv, D,
-        idx.data_ptr(), k, ptr(k_txt), ptr(v_txt), tbs, tts, ptr(txt_len) if Tmax else None, Tmax,
+        ptr(idx), k, ptr(k_txt), ptr(v_txt), tbs, tts, ptr(txt_len) if Tmax else None, Tmax,
         _dtype(q), float(scale) if scale else 0.0, res.data_ptr(), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(dev)))
     return res

@@ -281,8 +281,8 @@ sv_status sv_sparse_decode_attn(const void* q, int B, int Hq, const void* k_vis,
                 B, Hq, Hkv, N, k, Tmax);
   if (k > N) return fail(SV_EINVAL, "sv_sparse_decode_attn: k=%d > N=%d", k, N);
   if (k + Tmax == 0) return fail(SV_EINVAL, "sv_sparse_decode_attn: nothing to attend (k + Tmax == 0)");
-  if (k > 0 && (!k_vis || !v_vis || !idx))
-    return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL k_vis, v_vis or idx");
+  if (k > 0 && (!k_vis || !v_vis))
+    return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL k_vis or v_vis");
   if (Tmax > 0 && (!k_txt || !v_txt || !txt_len))
     return fail(SV_EINVAL, "sv_sparse_decode_attn: NULL k_txt, v_txt or txt_len");
   if (Hq % Hkv) return fail(SV_EINVAL, "sv_sparse_decode_attn: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);

@@ -632,12 +632,18 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
       }
       __builtin_amdgcn_s_sleep(8);
     }
-  } else {
+  } else if (a.idx) {
     const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       const int e = entry_of(tt, li);
       tok[tt] = e < n_ent ? ib[e] : -1;
+    }
+  } else {  // no index list: the visual rows 0..k-1 themselves (a packed cache)
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int e = entry_of(tt, li);
+      tok[tt] = e < n_ent ? e0 + e : -1;
     }
   }
   const int lim = text ? a.Tmax : a.N;  // tokens outside [0, lim) are skipped
@@ -865,12 +871,18 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
           }
           __builtin_amdgcn_s_sleep(8);
         }
-      } else {
+      } else if (a.idx) {
         const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
   #pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = (j * kItemWaves + wave) * EPW + eg;
           tok[j] = e < n_ent ? ib[e] : -1;
+        }
+      } else {  // no index list: the visual rows 0..k-1 themselves (a packed cache)
+  #pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = (j * kItemWaves + wave) * EPW + eg;
+          tok[j] = e < n_ent ? e0 + e : -1;
         }
       }
   #pragma unroll
