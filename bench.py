@@ -215,6 +215,7 @@ def free(torch):
 
 def main():
     a = parse()
+    a.deferred = []                         # CPU baselines, run after every GPU measurement
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
@@ -232,14 +233,26 @@ def main():
     torch.cuda.set_device(dev)
     sv.load()
     stream = torch.cuda.Stream(device=dev)      # default priority
+    def flush_baselines():
+        for target, key, fn in a.deferred:
+            target[key] = fn()
+            free(torch)
+        a.deferred.clear()
+
     if a.salience_only:
-        print(json.dumps({"salience": bench_salience(a, dev, stream)}), flush=True)
+        out = {"salience": bench_salience(a, dev, stream)}
+        flush_baselines()
+        print(json.dumps(out), flush=True)
         return
     if a.summary_only:
-        print(json.dumps({"summary_salience": bench_summary(a, dev, stream)}), flush=True)
+        out = {"summary_salience": bench_summary(a, dev, stream)}
+        flush_baselines()
+        print(json.dumps(out), flush=True)
         return
     if a.salience_long_only:
-        print(json.dumps({"salience_long": bench_salience_long(a, dev, stream)}), flush=True)
+        out = {"salience_long": bench_salience_long(a, dev, stream)}
+        flush_baselines()
+        print(json.dumps(out), flush=True)
         return
     w = synthetic.DECODE[a.workload]
     if a.pack_only:
@@ -253,7 +266,11 @@ def main():
         return
     if a.prefill_only:
         layers = make_layers(a, dev, w)
-        print(json.dumps({"prefill_retrieve": bench_prefill(a, dev, stream, w, layers)}), flush=True)
+        out = {"prefill_retrieve": bench_prefill(a, dev, stream, w, layers)}
+        del layers
+        free(torch)
+        flush_baselines()
+        print(json.dumps(out), flush=True)
         return
 
     # ------------------------------------------------------------ headline decode workload
@@ -292,7 +309,7 @@ def main():
 
     # ------------------------------------------------------------ CPU oracle, headline workload
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(a, w, layers)
+        defer_baseline(a, res, "cpu_baseline", lambda: decode_baseline_fresh(a, dev, w))
     del layers
     free(torch)
 
@@ -306,7 +323,8 @@ def main():
             lx = make_layers(a, dev, wx)
             obj = bench_decode(a, dev, stream, wx, lx, two_call=False, full_schedule=True)
             if not a.no_cpu_baseline:
-                obj["cpu_baseline"] = cpu_baseline_decode(a, wx, lx)
+                defer_baseline(a, obj, "cpu_baseline",
+                               lambda wx=wx: decode_baseline_fresh(a, dev, wx))
             res["workloads"][name] = obj
             del lx
             free(torch)
@@ -323,6 +341,9 @@ def main():
         free(torch)
 
     res["hbm_measured"] = hbm_measured(dev, stream)
+
+    # ------------------------------------------------------------ CPU oracle baselines, last
+    flush_baselines()
     print(json.dumps(res), flush=True)
 
 
@@ -646,29 +667,34 @@ def bench_prefill(a, dev, stream, w, layers, Tq=32):
                    "top-k retrieval from one pass; retrieval_alone is sv_retrieve with the same "
                    "question tokens (a separate pass over the visual keys)"}
     if not a.no_cpu_baseline:
-        import oracle
-        ncores, model = cpu_info()
-        done, spent = 0, 0.0
-        for l, d in enumerate(layers):
-            for b in range(w.B):
-                h = {n: d[n][b:b + 1].cpu() for n in ("k_vis", "v_vis", "k_txt", "v_txt")}
-                qb = qs[l][b:b + 1].cpu()
-                tl = d["txt_len"][b:b + 1].cpu().numpy()
-                t0 = time.perf_counter()
-                oracle.prefill_attention(qb, h["k_vis"], h["v_vis"], h["k_txt"], h["v_txt"], tl)
-                oracle.retrieve(qb, h["k_vis"], w.k)
-                spent += time.perf_counter() - t0
-                done += 1
+        def prefill_baseline():
+            import oracle
+            lays = make_layers(a, dev, w)      # the same seeded inputs, generated again
+            ncores, model = cpu_info()
+            done, spent = 0, 0.0
+            for l, d in enumerate(lays):
+                for b in range(w.B):
+                    h = {n: d[n][b:b + 1].cpu() for n in ("k_vis", "v_vis", "k_txt", "v_txt")}
+                    qb = qs[l][b:b + 1].cpu()
+                    tl = d["txt_len"][b:b + 1].cpu().numpy()
+                    t0 = time.perf_counter()
+                    oracle.prefill_attention(qb, h["k_vis"], h["v_vis"], h["k_txt"], h["v_txt"], tl)
+                    oracle.retrieve(qb, h["k_vis"], w.k)
+                    spent += time.perf_counter() - t0
+                    done += 1
+                    if spent >= a.cpu_seconds:
+                        break
                 if spent >= a.cpu_seconds:
                     break
-            if spent >= a.cpu_seconds:
-                break
-        per_q = spent / done * w.B * len(layers)
-        res["cpu_baseline"] = {"value": round(w.B * Tq / per_q, 2), "unit": "tokens/s",
-                               "cores": blas_threads(), "host_cores_visible": ncores,
-                               "cpu_model": model, "kind": "oracle",
-                               "sample": f"{done} (layer, sequence) units of {w.B * len(layers)} "
-                                         f"(prefill attention + retrieval, fp64), {spent:.1f} s"}
+            del lays
+            per_q = spent / done * w.B * len(layers_n)
+            return {"value": round(w.B * Tq / per_q, 2), "unit": "tokens/s",
+                    "cores": blas_threads(), "host_cores_visible": ncores,
+                    "cpu_model": model, "kind": "oracle",
+                    "sample": f"{done} (layer, sequence) units of {w.B * len(layers_n)} "
+                              f"(prefill attention + retrieval, fp64), {spent:.1f} s"}
+        layers_n = list(range(len(layers)))
+        defer_baseline(a, res, "cpu_baseline", prefill_baseline)
     return res
 
 
@@ -723,9 +749,10 @@ def bench_summary(a, dev, stream):
                                   "bytes_algorithmic": nbytes}}
         if not a.no_cpu_baseline:
             import oracle
-            Q, K = sets[0]
-            res[name]["cpu_baseline"] = cpu_baseline_salience(
-                a, sw, Q, K, lambda q, k: oracle.summary_salience(q, k, S))
+            Q0, K0 = sets[0]
+            defer_baseline(a, res[name], "cpu_baseline",
+                           lambda sw=sw, Q0=Q0, K0=K0, S=S: cpu_baseline_salience(
+                               a, sw, Q0, K0, lambda q, k: oracle.summary_salience(q, k, S)))
         del sets
         free(torch)
     return res
@@ -769,7 +796,8 @@ def bench_salience(a, dev, stream):
                                             if executed else None)}}
     if not a.no_cpu_baseline:
         import oracle
-        res["cpu_baseline"] = cpu_baseline_salience(a, sw, Q, K, oracle.salience)
+        defer_baseline(a, res, "cpu_baseline",
+                       lambda: cpu_baseline_salience(a, sw, Q, K, oracle.salience))
     return res
 
 
@@ -808,24 +836,26 @@ def bench_salience_long(a, dev, stream):
                         "flops_algorithmic": flops,
                         "frac_of_two_pass_work": round(2 * tflops / BF16_PEAK_TFLOPS, 4)}}
     if not a.no_cpu_baseline:
-        import oracle
-        ncores, model = cpu_info()
-        done, spent = 0, 0.0
-        for h in range(sw.H):                # one head of the frame at a time
-            q, k = Q[:, h:h + 1].cpu(), K[:, h:h + 1].cpu()
-            t0 = time.perf_counter()
-            oracle.salience(q, k)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent >= a.cpu_seconds:
-                break
-        per_call = spent / done * sw.H
-        res["cpu_baseline"] = {"value": round(sw.F * sw.N / per_call, 1), "unit": "tokens/s",
-                               "cores": blas_threads(), "host_cores_visible": ncores,
-                               "cpu_model": model, "kind": "oracle",
-                               "ms_per_call_equivalent": round(per_call * 1e3, 1),
-                               "sample": f"{done} of {sw.H} heads of the frame (materialised "
-                                         f"fp64 softmax), {spent:.1f} s, scaled to the call"}
+        def long_baseline():
+            import oracle
+            ncores, model = cpu_info()
+            done, spent = 0, 0.0
+            for h in range(sw.H):                # one head of the frame at a time
+                q, k = Q[:, h:h + 1].cpu(), K[:, h:h + 1].cpu()
+                t0 = time.perf_counter()
+                oracle.salience(q, k)
+                spent += time.perf_counter() - t0
+                done += 1
+                if spent >= a.cpu_seconds:
+                    break
+            per_call = spent / done * sw.H
+            return {"value": round(sw.F * sw.N / per_call, 1), "unit": "tokens/s",
+                    "cores": blas_threads(), "host_cores_visible": ncores,
+                    "cpu_model": model, "kind": "oracle",
+                    "ms_per_call_equivalent": round(per_call * 1e3, 1),
+                    "sample": f"{done} of {sw.H} heads of the frame (materialised "
+                              f"fp64 softmax), {spent:.1f} s, scaled to the call"}
+        defer_baseline(a, res, "cpu_baseline", long_baseline)
     return res
 
 
@@ -851,6 +881,26 @@ def hbm_measured(dev, stream):
 
 
 # ---------------------------------------------------------------- CPU oracle baselines
+def defer_baseline(a, target, key, fn):
+    """Queue a CPU-oracle baseline for after every GPU measurement: the oracle's
+    BLAS threads would otherwise still be busy while the next workload's graph
+    replays are launched from the host, and a starved launch thread leaves the
+    GPU idle between replays."""
+    a.deferred.append((target, key, fn))
+
+
+def decode_baseline_fresh(a, dev, w):
+    """cpu_baseline_decode on the workload's inputs generated again from the same
+    seed (identical data), so no workload's caches stay resident meanwhile."""
+    import torch
+    layers = make_layers(a, dev, w)
+    try:
+        return cpu_baseline_decode(a, w, layers)
+    finally:
+        del layers
+        free(torch)
+
+
 def cpu_baseline_decode(a, w, layers):
     """The fp64 oracle on the host over whole (sequence, layer) units of the same
     decode inputs until the time budget is spent, scaled to steps/s.  Rows of the
