@@ -199,7 +199,20 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
     __syncthreads();
     const uint32_t bstar = sm.digit, above = sm.above, cnt = sm.count;
     fast = cnt <= (uint32_t)kSelMaxCand;  // uniform
-    if (fast) {
+    if (cnt == 1) {
+      // The bin holds one key (the usual case for spread values): it is the
+      // threshold element (k - above = 1), written by the thread that owns it;
+      // no candidate list and no ranking.
+      for_each([&](int e, bool valid, uint32_t kk) {
+        if (valid && bin_of(kk) == bstar) {
+          sm.thr_key = kk;
+          sm.thr_idx = (uint32_t)e;
+        }
+      });
+      __syncthreads();
+      thr_key = sm.thr_key;
+      thr_idx = sm.thr_idx;
+    } else if (fast) {
       uint32_t* cand = sm.hist[1];  // [kSelMaxCand] keys, then [kSelMaxCand] indices
       for_each([&](int e, bool valid, uint32_t kk) {
         if (valid && bin_of(kk) == bstar) {
