@@ -630,7 +630,7 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
         if (tid == 0) report_giveup(a.status, kGiveUpIndices);
         break;
       }
-      __builtin_amdgcn_s_sleep(8);
+      __builtin_amdgcn_s_sleep(24);
     }
   } else if (a.idx) {
     const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
@@ -869,7 +869,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
             if (tid == 0) report_giveup(a.status, kGiveUpIndices);
             break;
           }
-          __builtin_amdgcn_s_sleep(8);
+          __builtin_amdgcn_s_sleep(24);
         }
       } else if (a.idx) {
         const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
