@@ -217,7 +217,7 @@ def main():
     a = parse()
     a.deferred = []                         # CPU baselines, run after every GPU measurement
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
         sys.exit(2)
 
