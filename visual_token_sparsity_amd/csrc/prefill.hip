@@ -64,6 +64,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kPfStage = 32;       // keys per LDS stage (two 16-key tiles)
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfVPad = 32;        // bytes of padding per V row in LDS
+constexpr int kPfKPad = 16;        // ... per K row (key-split path)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
       load_k(st + 1, nxt);
       load_v(st + 1);
     }
+    float sck = 0.f;  // lanes li < 8: retrieval score of key 16 (li / 4) + 4 lg + li % 4
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       bf16x8_t kf[KS];
@@ -219,14 +221,12 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
       }
       const int kb = st * kPfStage + 16 * t + 4 * lg;  // split-relative key of r = 0
       if (visual) {
-        // Retrieval: raw logits of the key summed over this wave's rows.
-        float sc[4];
+        // Retrieval: raw logits of the key summed over this wave's rows
+        // (every lane of the lane group holds each sum).
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = row16_add(St[0][r] + St[1][r]);
-        if (li == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb + r < nkeys) pscore[e0 + kb + r] = sc[r];
+        for (int r = 0; r < 4; ++r) {
+          const float sc = row16_add(St[0][r] + St[1][r]);
+          sck = li == 4 * t + r ? sc : sck;
         }
       }
       s16x4 ph[2], pl[2];
@@ -280,6 +280,11 @@ __global__ __launch_bounds__(W* kWave) void prefill_attn_kernel(PrefillArgs a) {
           acc[rb][db] = o;  // acc[rb][db][r] = O[row 16 rb + li][dim 16 db + 4 lg + r]
         }
       }
+    }
+    // One 128-byte store of the stage's 32 scores (lanes li < 8 of each group).
+    if (visual && li < 8) {
+      const int k = st * kPfStage + 16 * (li >> 2) + 4 * lg + (li & 3);
+      if (k < nkeys) pscore[e0 + k] = sck;
     }
     if (more) store_v(nxt);
     wait_stores_complete();
@@ -367,16 +372,20 @@ struct PfKwShape {
   static constexpr int DB = D / 16;                          // 16-dim blocks of P V
   static constexpr int VSTR = D * 2 + kPfVPad;               // V row stride in LDS (bytes)
   static constexpr int VBYTES = kPfStage * VSTR;             // one wave's V stage
-  static constexpr int VPL = kPfStage * D / 8 / kWave;       // 16-byte V chunks per lane
+  static constexpr int KSTR = D * 2 + kPfKPad;               // K row stride in LDS (bytes)
+  static constexpr int KBYTES = kPfStage * KSTR;             // one wave's K stage
+  static constexpr int WBYTES = VBYTES + KBYTES;             // one wave's stage buffers
+  static constexpr int VPL = kPfStage * D / 8 / kWave;       // 16-byte chunks per lane (K or V)
   static constexpr int MSTR = D + 4;                         // floats per row of a merge slot
   static constexpr int MBYTES = kPfRowsPerWave * MSTR * 4;   // one merge slot
   static constexpr int QBYTES = 2 * KS * kWave * 16;          // Q^T fragments of the row block
   static constexpr int SBYTES = sizeof(SelectSmem<kPfKW>);
-  static constexpr int MAIN0 = kPfKW * VBYTES > kPfKW / 2 * MBYTES ? kPfKW * VBYTES : kPfKW / 2 * MBYTES;
-  static constexpr int MAIN = MAIN0 > SBYTES ? MAIN0 : SBYTES;  // V buffers, merge slots, select
+  static constexpr int MAIN0 = kPfKW * WBYTES > kPfKW / 2 * MBYTES ? kPfKW * WBYTES : kPfKW / 2 * MBYTES;
+  static constexpr int MAIN = MAIN0 > SBYTES ? MAIN0 : SBYTES;  // stage buffers, merge slots, select
   static constexpr int LDS = MAIN + QBYTES;
   static constexpr int SKPT = 4;  // keys per thread kept in registers by the select (rows <= 2048)
-  static_assert(VPL * kWave * 8 == kPfStage * D, "V stage split evenly over a wave");
+  static_assert(VPL * kWave * 8 == kPfStage * D, "K and V stages split evenly over a wave");
+  static_assert(LDS + 4 <= 160 * 1024, "one workgroup's LDS");
 };
 
 template <int D>
@@ -440,12 +449,12 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
   const uint32_t text_ext = tl > 0 ? (uint32_t)((int64_t)(tl - 1) * a.tts * 2 + D * 2) : 0u;
   const BufRsrc rkt = make_rsrc(tl > 0 ? a.kt + (int64_t)b * a.tbs + g * D : a.kv, text_ext);
   const BufRsrc rvt = make_rsrc(tl > 0 ? a.vt + (int64_t)b * a.tbs + g * D : a.vv, text_ext);
-  // K fragments of stage st: tile t, step s -> key 16 t + li, dims 32 s + 8 lg
-  // (each load: 64 contiguous bytes of each of 16 rows).
-  // V chunk i of a lane: key (64 i + lane) / (D / 8), 16 bytes at dim
-  // 8 ((64 i + lane) % (D / 8)).
-  constexpr int VKPI = kWave / (D / 8);  // V keys per chunk index
-  u32x4 kr[2][KS];
+  // K and V rows of a stage go through the wave's LDS buffers: chunk i of
+  // a lane is key (64 i + lane) / (D / 8), 16 bytes at dim 8 ((64 i + lane)
+  // % (D / 8)), so each load covers whole rows.  The K fragments are read
+  // back from LDS (tile t, step s -> key 16 t + li, dims 32 s + 8 lg).
+  constexpr int VKPI = kWave / (D / 8);  // keys per chunk index
+  u32x4 kr[S::VPL];
   u32x4 vr[S::VPL];
   struct StageSrc {
     BufRsrc rk, rv;
@@ -459,14 +468,11 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
   };
   auto load_k = [&](int st) {
     const StageSrc ss = stage_src(st);
+    const uint32_t vo = (ss.row0 + lane / (D / 8)) * ss.rs + (lane % (D / 8)) * 16;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t vo = (ss.row0 + 16 * t + li) * ss.rs + lg * 16;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kr[t][s] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rk, vo + 64 * s, 0, kCacheStream));
-    }
+    for (int i = 0; i < S::VPL; ++i)
+      kr[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rk, vo, i * VKPI * ss.rs, kCacheStream));
   };
   auto load_v = [&](int st) {
     const StageSrc ss = stage_src(st);
@@ -476,7 +482,8 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
       vr[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(ss.rv, vo, i * VKPI * ss.rs, kCacheStream));
   };
-  char* vbuf = lds + wave * S::VBYTES;
+  char* vbuf = lds + wave * S::WBYTES;
+  char* kbuf = vbuf + S::VBYTES;
 
   float m[2], l[2];
   f32x4_t acc[2][DB];
@@ -494,18 +501,21 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
     load_v(wave);
   }
   for (int st = wave; st < nst; st += kPfKW) {
-    // This stage's V rows to the wave's own LDS buffer (its reads of the
-    // previous stage were issued before these writes), then the next V
-    // stage's loads; the next K stage's loads go out once this stage's
-    // logits are done.
+    // This stage's K and V rows to the wave's own LDS buffers (its reads of
+    // the previous stage were issued before these writes), then the next
+    // stage's loads.
     const bool more = st + kPfKW < nst;
 #pragma unroll
     for (int i = 0; i < S::VPL; ++i) {
       const int ch = i * kWave + lane;
       const int key = ch / (D / 8), d8 = ch - key * (D / 8);
+      *reinterpret_cast<u32x4*>(kbuf + key * S::KSTR + d8 * 16) = kr[i];
       *reinterpret_cast<u32x4*>(vbuf + key * S::VSTR + d8 * 16) = vr[i];
     }
-    if (more) load_v(st + kPfKW);
+    if (more) {
+      load_k(st + kPfKW);
+      load_v(st + kPfKW);
+    }
     f32x4_t Sall[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -513,26 +523,24 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
       for (int rb = 0; rb < 2; ++rb) {
         f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[t][s]),
-                                                      qfrag(rb, s), z, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kbuf + (16 * t + li) * S::KSTR +
+                                                                 64 * s + 16 * lg);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qfrag(rb, s), z, 0, 0, 0);
+        }
         Sall[t][rb] = z;  // Sall[t][rb][r] = S[row 16 rb + li][key 16 t + 4 lg + r]
       }
-    if (more) load_k(st + kPfKW);
+    float sck = 0.f;  // lanes li < 8: retrieval score of key 16 (li / 4) + 4 lg + li % 4
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const f32x4_t* St = Sall[t];
       const int kb = st * kPfStage + 16 * t + 4 * lg;  // split-relative key of r = 0
-      if (e0 + kb < N) {
-        // Retrieval: raw logits of each visual key summed over the row block.
-        float sc[4];
+      // Retrieval: raw logits of each key summed over the row block (every
+      // lane of the lane group holds each sum).
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = row16_add(St[0][r] + St[1][r]);
-        if (li == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb + r < nkeys && e0 + kb + r < N) store_shared_dev(pscore + e0 + kb + r, sc[r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float sc = row16_add(St[0][r] + St[1][r]);
+        sck = li == 4 * t + r ? sc : sck;
       }
       s16x4 ph[2], pl[2];
       float al[2];
@@ -585,6 +593,12 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
           acc[rb][db] = o;  // acc[rb][db][r] = O[row 16 rb + li][dim 16 db + 4 lg + r]
         }
       }
+    }
+    // One 128-byte store of the stage's 32 visual scores (lanes li < 8 of
+    // each group; text keys and padding store nothing).
+    if (li < 8) {
+      const int kk = st * kPfStage + 16 * (li >> 2) + 4 * lg + (li & 3);
+      if (kk < nkeys && e0 + kk < N) store_shared_dev(pscore + e0 + kk, sck);
     }
   }
 #pragma unroll
