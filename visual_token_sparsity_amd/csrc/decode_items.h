@@ -154,7 +154,7 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   constexpr int ES = (int)sizeof(T);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   const int LPR = a.LPR, nseg = a.nseg;
   const int RPS = kWave / LPR;  // units per wave step
   const int sub = lane & (LPR - 1);
@@ -411,7 +411,7 @@ __device__ __forceinline__ void select_poll_item(const ScanArgs& a, int b, float
   constexpr int NW = kItemWaves, KPT = kSelKpt;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   const int N = a.N;
   const int seg = ((N + NW * kWave - 1) / (NW * kWave)) * kWave;
   const int chunks = seg / kWave;
@@ -554,7 +554,7 @@ __device__ __forceinline__ void attn_front_mfma(const AttnArgs& a, int b, int g,
   constexpr int VLD = 16 * VCH / kWave;    // V loads per lane per tile
   constexpr int VEPL = kWave / VCH;        // entries per V load instruction
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = tid & (kWave - 1), wave = wave_uniform(tid / kWave);
   const int li = lane & 15, lg = lane >> 4;
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
 
@@ -760,7 +760,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
   constexpr int SE = kItemWaves * EPW * EPL;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   const int eg = lane / LPE, sub = lane % LPE, d0 = sub * VE;
   const T* q = reinterpret_cast<const T*>(a.q);
   const int C = a.CT + a.CV;

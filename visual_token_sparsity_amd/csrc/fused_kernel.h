@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   if (t < ctl.seq_end) {
     int q_of = -1;
     if constexpr (!LONG) {
-      const int b = t / ctl.per_seq;
-      const int j = t % ctl.per_seq;
+      const int b = wave_uniform(t / ctl.per_seq);
+      const int j = wave_uniform(t % ctl.per_seq);
       if (j < sa.items_per_seq) {
         // Scores stored complemented (encode): the scan item never selects,
         // the select item below does.
@@ -126,14 +126,14 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
     uint32_t u = t;
     if (u < ctl.B * S) {
       // G >= 2: the attention items set the registers, so the scan can pair rows.
-      scan_item<T, kScanCpl, (G >= 2)>(sa, u / S, u % S, smem, q_of);
+      scan_item<T, kScanCpl, (G >= 2)>(sa, wave_uniform(u / S), wave_uniform(u % S), smem, q_of);
     } else if ((u -= ctl.B * S) < ctl.B * P) {
-      cand_item(sa, ls, u / P, u % P, smem);
+      cand_item(sa, ls, wave_uniform(u / P), wave_uniform(u % P), smem);
     } else if ((u -= ctl.B * P) < ctl.B) {
       thr_item(sa, ls, u, smem);
     } else {
       u -= ctl.B;
-      compact_item(sa, ls, u / P, u % P, smem);
+      compact_item(sa, ls, wave_uniform(u / P), wave_uniform(u % P), smem);
     }
     return;
   }
@@ -142,14 +142,15 @@ __global__ __launch_bounds__(kItemThreads) void fused_kernel(ScanArgs sa, AttnAr
   if constexpr (LONG) {
     if (!text && ls.chunk_attn) {
       const uint32_t P = (uint32_t)ls.P;
-      chunk_attn_item<T, D, G, EPL>(sa, aa, ls, u / (P * aa.Hkv), (u / P) % aa.Hkv, u % P, smem);
+      chunk_attn_item<T, D, G, EPL>(sa, aa, ls, wave_uniform(u / (P * aa.Hkv)),
+                                    wave_uniform((u / P) % aa.Hkv), wave_uniform(u % P), smem);
       return;
     }
   }
   const int per = text ? aa.CT : aa.CV;
-  const int b = u / (per * aa.Hkv);
-  const int g = (u / per) % aa.Hkv;
-  attn_item<T, D, G, EPL>(aa, b, g, (text ? 0 : aa.CT) + u % per, !text, smem);
+  const int b = wave_uniform(u / (per * aa.Hkv));
+  const int g = wave_uniform((u / per) % aa.Hkv);
+  attn_item<T, D, G, EPL>(aa, b, g, wave_uniform((text ? 0 : aa.CT) + u % per), !text, smem);
   if (text) return;
   // The last visual item of b (every other one has read its indices) clears
   // the encoded index copy, ready[b] and the count for the next launch.

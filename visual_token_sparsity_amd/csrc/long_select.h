@@ -122,7 +122,7 @@ __device__ __forceinline__ uint32_t wave_poll_sum_until(const uint32_t* p, int n
 __device__ __forceinline__ void load_chunk_keys(const float* scores, int N, int b, int p,
                                                 uint32_t (&key)[kSelKpt], int& e0) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_uniform(threadIdx.x / kWave);
   const int c0 = p * kLsChunk;
   const int n = min(kLsChunk, N - c0);
   const BufRsrc r = make_rsrc(scores + (int64_t)b * N + c0, (uint32_t)n * 4u);
@@ -148,7 +148,7 @@ __device__ __forceinline__ void cand_item(const ScanArgs& a, const LongSelArgs& 
   CandSmem& sm = *reinterpret_cast<CandSmem*>(smem);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   for (int i = tid; i < kLsBins; i += kItemThreads) sm.h2[i] = 0;
   if (wave == 0)
     wave_poll_sum_until(&a.seq_ctr[(b << a.ctr_log2) * kCtrStride], 1 << a.ctr_log2,
@@ -257,7 +257,7 @@ __device__ __forceinline__ void thr_item(const ScanArgs& a, const LongSelArgs& l
   ThrSmem& sm = *reinterpret_cast<ThrSmem*>(smem);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   const int P = l.P;
   if (tid == 0) {
     poll_until(ls_line(l, b, kLsCandDone), (uint32_t)P, a.spin_limit, a.status, kGiveUpCandCount);
@@ -430,7 +430,7 @@ __device__ __forceinline__ void compact_item(const ScanArgs& a, const LongSelArg
   CompactSmem& sm = *reinterpret_cast<CompactSmem*>(smem);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   if (tid == 0)
     sm.mode = poll_until(ls_line(l, b, kLsThrReady), 1u, a.spin_limit, a.status, kGiveUpThreshold);
   __syncthreads();
@@ -497,7 +497,7 @@ __device__ __forceinline__ int chunk_list_append(const ChunkSel& cs, int* list, 
                                                  int base, bool tail, uint32_t T, uint32_t Ti) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   bool sel[kSelKpt];
   uint32_t n = 0;
 #pragma unroll

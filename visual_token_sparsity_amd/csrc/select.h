@@ -30,6 +30,12 @@
 
 namespace sv {
 
+// A value the same in every lane of the wave, kept in a scalar register.  A
+// division by a kernel argument runs on the vector unit, and a buffer
+// resource or loop bound built from its result would otherwise take a
+// per-lane loop around every load that uses it.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 constexpr int kSelBins = 2048;                        // widest digit: 11 bits
 constexpr int kSelHistWords = kSelBins + kSelBins / 32;  // one pad word per 32 bins
 
@@ -101,7 +107,7 @@ __device__ __forceinline__ void block_topk(const float* vals, int N, int k, int3
                            uint64_t* __restrict__ thr_pub = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = wave_uniform(tid / kWave);
   const int seg = ((N + NW * kWave - 1) / (NW * kWave)) * kWave;  // per-wave segment
   const int chunks = seg / kWave;
   const int base = wave * seg + lane;
