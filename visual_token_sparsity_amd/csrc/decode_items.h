@@ -160,6 +160,7 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
   const int sub = lane & (LPR - 1);
   const int rsub = lane / LPR;
   constexpr int SEG = CPL * kWave;  // chunks per segment
+  constexpr int QB = PAIR ? 8 : 1;  // query rows loaded together for qhat (GQA groups)
   const int CP = scan_padded_chunks(nseg, LPR, CPL);
   float* qh = reinterpret_cast<float*>(smem);  // [NP][CP][4]
 
@@ -244,14 +245,26 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
       if (c < a.C) {
         const int e0 = c * VE;
         const int g = e0 / a.D, d0 = e0 % a.D;
-        for (int tau = 0; tau < a.Tq; ++tau) {
-          for (int i = 0; i < a.G; ++i) {
-            Vec<T> x;
-            x.load(qb + ((int64_t)(b * a.Tq + tau) * a.Hq + g * a.G + i) * a.D + d0);
-            float f[VE];
-            x.to_f32(f);
+        // Query row j = tau G + i of head group g, QB loads in flight, summed
+        // in row order (past the last row: the last row again, not added).
+        const int nq = a.Tq * a.G;
+        const T* q0 = qb + ((int64_t)b * a.Tq * a.Hq + g * a.G) * a.D + d0;
+        for (int j0 = 0; j0 < nq; j0 += QB) {
+          Vec<T> x[QB];
 #pragma unroll
-            for (int v = 0; v < VE; ++v) acc[v] += f[v];
+          for (int jj = 0; jj < QB; ++jj) {
+            const int j = j0 + jj < nq ? j0 + jj : nq - 1;
+            const int tau = j / a.G, i = j - tau * a.G;
+            x[jj].load(q0 + ((int64_t)tau * a.Hq + i) * a.D);
+          }
+#pragma unroll
+          for (int jj = 0; jj < QB; ++jj) {
+            if (j0 + jj < nq) {
+              float f[VE];
+              x[jj].to_f32(f);
+#pragma unroll
+              for (int v = 0; v < VE; ++v) acc[v] += f[v];
+            }
           }
         }
       }
