@@ -245,25 +245,37 @@ __device__ __forceinline__ bool scan_item(const ScanArgs& a, int b, int item, ch
       if (c < a.C) {
         const int e0 = c * VE;
         const int g = e0 / a.D, d0 = e0 % a.D;
-        // Query row j = tau G + i of head group g, QB loads in flight, summed
-        // in row order (past the last row: the last row again, not added).
+        // Query row j = tau G + i of head group g, summed in row order.
         const int nq = a.Tq * a.G;
         const T* q0 = qb + ((int64_t)b * a.Tq * a.Hq + g * a.G) * a.D + d0;
-        for (int j0 = 0; j0 < nq; j0 += QB) {
-          Vec<T> x[QB];
-#pragma unroll
-          for (int jj = 0; jj < QB; ++jj) {
-            const int j = j0 + jj < nq ? j0 + jj : nq - 1;
-            const int tau = j / a.G, i = j - tau * a.G;
-            x[jj].load(q0 + ((int64_t)tau * a.Hq + i) * a.D);
-          }
-#pragma unroll
-          for (int jj = 0; jj < QB; ++jj) {
-            if (j0 + jj < nq) {
+        if constexpr (QB == 1) {
+          for (int tau = 0; tau < a.Tq; ++tau)
+            for (int i = 0; i < a.G; ++i) {
+              Vec<T> x;
+              x.load(q0 + ((int64_t)tau * a.Hq + i) * a.D);
               float f[VE];
-              x[jj].to_f32(f);
+              x.to_f32(f);
 #pragma unroll
               for (int v = 0; v < VE; ++v) acc[v] += f[v];
+            }
+        } else {
+          // QB loads in flight (past the last row: the last row again, not added).
+          for (int j0 = 0; j0 < nq; j0 += QB) {
+            Vec<T> x[QB];
+#pragma unroll
+            for (int jj = 0; jj < QB; ++jj) {
+              const int j = j0 + jj < nq ? j0 + jj : nq - 1;
+              const int tau = j / a.G, i = j - tau * a.G;
+              x[jj].load(q0 + ((int64_t)tau * a.Hq + i) * a.D);
+            }
+#pragma unroll
+            for (int jj = 0; jj < QB; ++jj) {
+              if (j0 + jj < nq) {
+                float f[VE];
+                x[jj].to_f32(f);
+#pragma unroll
+                for (int v = 0; v < VE; ++v) acc[v] += f[v];
+              }
             }
           }
         }
@@ -802,7 +814,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     attn_front_mfma<D, G, SE, LIST>(a, b, g, text, e0, n_ent, wait, smem, list, more);
   } else {
     Vec<T> qx[G];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < G; ++i) qx[i].load(q + ((int64_t)b * a.Hq + g * G + i) * D + d0);
 
     // The sequence's text or visual cache as one buffer; entry j of this lane
@@ -856,7 +868,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
       }
     } else if (text) {
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < EPL; ++j) {
         const int e = (j * kItemWaves + wave) * EPW + eg;
         off[j] = e < n_ent ? (uint32_t)((e0 + e) * ts * ES) + head_off : kBufOob;
@@ -870,7 +882,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         const uint32_t* ib = a.idx_enc + (int64_t)b * a.k + e0;
         for (uint32_t n = 0;; ++n) {
           bool missing = false;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < EPL; ++j) {
             const int e = (j * kItemWaves + wave) * EPW + eg;
             const uint32_t w = e < n_ent ? load_flag(ib + e) : 0u;
@@ -886,19 +898,19 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         }
       } else if (a.idx) {
         const int32_t* ib = a.idx + (int64_t)b * a.k + e0;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = (j * kItemWaves + wave) * EPW + eg;
           tok[j] = e < n_ent ? ib[e] : -1;
         }
       } else {  // no index list: the visual rows 0..k-1 themselves (a packed cache)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = (j * kItemWaves + wave) * EPW + eg;
           tok[j] = e < n_ent ? e0 + e : -1;
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < EPL; ++j) {
         const int t = tok[j];  // indices outside [0, N) are skipped
         off[j] = (t >= 0 && t < a.N) ? (uint32_t)(t * ts * ES) + head_off : kBufOob;
@@ -906,7 +918,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     }
 
     Vec<T> kx[EPL], vx[EPL];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < EPL; ++j) {
       kx[j].template load_buf<kCacheDefault>(krs, off[j], 0u);
       vx[j].template load_buf<kCacheDefault>(vrs, off[j], 0u);
@@ -914,27 +926,27 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
 
     if (!LIST && it == 0) init();  // after the loads are issued
 
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < EPL; ++j) {
       float kf[VE], vf[VE];
       kx[j].to_f32(kf);
       vx[j].to_f32(vf);
       float z[G];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < G; ++i) {
         float s = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
         z[i] = lane_group_sum<LPE>(s);
       }
       if (off[j] != kBufOob) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < G; ++i) {
           const float mn = fmaxf(m[i], z[i]);
           const float al = fast_exp2(m[i] - mn);  // m = -inf -> 0
           const float p = fast_exp2(z[i] - mn);
           l[i] = l[i] * al + p;
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
           m[i] = mn;
         }
@@ -948,7 +960,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
     // row-swap moves, no LDS trips).
     auto merge_groups = [&](auto off_tag) {
       constexpr int OFF = decltype(off_tag)::value;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < G; ++i) {
         const float mo = xor_partner<OFF>(m[i]);
         const float lo = xor_partner<OFF>(l[i]);
@@ -956,7 +968,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         const float al = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
         const float bo = (mo == -INFINITY) ? 0.f : fast_exp2(mo - mn);
         l[i] = l[i] * al + lo * bo;
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < VE; ++v) {
           const float ao = xor_partner<OFF>(acc[i][v]);
           acc[i][v] = acc[i][v] * al + ao * bo;

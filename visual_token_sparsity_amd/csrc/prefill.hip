@@ -329,6 +329,40 @@ __device__ __forceinline__ void select_sequence(const PrefillArgs& a, int b, cha
   const int chunks = seg / kWave;
   const int base = wave * seg + lane;
   uint32_t key[KPT];
+  if (N % 4 == 0 && chunks <= KPT && (((uintptr_t)a.scores | (uintptr_t)a.pscore) & 15) == 0) {
+    // Rows of whole 16-byte groups: thread t sums keys 4t .. 4t + 3 over the
+    // partial rows (one 16-byte load per row, up to 32 rows in flight, added
+    // in row order as below), then the sums reach the select's element layout
+    // through LDS.
+    float* ssum = reinterpret_cast<float*>(smem + sizeof(SelectSmem<NW>));
+    const BufRsrc rps = make_rsrc(ps, (uint32_t)((int64_t)a.NP * N * 4));
+    const BufRsrc rsr = make_rsrc(srow, (uint32_t)N * 4u);
+    for (int q = tid; q < N / 4; q += NW * kWave) {
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < a.NP; j0 += 32) {
+        f32x4v v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          v[j] = j0 + j < a.NP ? __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                     rps, (uint32_t)q * 16u, (uint32_t)((j0 + j) * N * 4), kCacheCoherent))
+                               : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if (j0 + j < a.NP) acc += v[j];
+      }
+      store4_dev(rsr, (uint32_t)q * 16u, __builtin_bit_cast(u32x4, acc));
+      *reinterpret_cast<f32x4v*>(ssum + 4 * q) = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = base + i * kWave;
+      key[i] = float_key(i < chunks && e < N ? ssum[e] : 0.f);
+    }
+    SelectSmem<NW>& sm = *reinterpret_cast<SelectSmem<NW>*>(smem);
+    block_topk<NW, KPT, false, true>(nullptr, N, a.k, a.idx + (int64_t)b * a.k, sm, key);
+    return;
+  }
   for (int i0 = 0; i0 < chunks; i0 += KPT) {
     float sum[KPT];
 #pragma unroll
@@ -386,6 +420,7 @@ struct PfKwShape {
   static constexpr int SKPT = 4;  // keys per thread kept in registers by the select (rows <= 2048)
   static_assert(VPL * kWave * 8 == kPfStage * D, "K and V stages split evenly over a wave");
   static_assert(LDS + 4 <= 160 * 1024, "one workgroup's LDS");
+  static_assert(SBYTES + 2048 * 4 <= MAIN, "select state plus the summed scores of a row");
 };
 
 template <int D>
