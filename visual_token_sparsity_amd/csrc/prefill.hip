@@ -737,32 +737,71 @@ __device__ __forceinline__ void pf_sum_item(const PrefillArgs& pa, const ScanArg
   uint32_t* lh = reinterpret_cast<uint32_t*>(smem);
   for (int i = tid; i < kLsBins; i += kItemThreads) lh[i] = 0u;
   __syncthreads();
-  const int e0 = p * kLsChunk + wave * (kLsChunk / kItemWaves) + lane;
   const float* ps = pa.pscore + (int64_t)b * pa.NP * N;
-  float sum[kSelKpt];
-#pragma unroll
-  for (int i = 0; i < kSelKpt; ++i) sum[i] = 0.f;
-  for (int j0 = 0; j0 < pa.NP; j0 += 4) {
-    float v[4][kSelKpt];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < kSelKpt; ++i) {
-        const int e = e0 + i * kWave;
-        v[j][i] = (j0 + j < pa.NP && e < N) ? ps[(int64_t)(j0 + j) * N + e] : 0.f;
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < kSelKpt; ++i) sum[i] += v[j][i];
-  }
   float* srow = sa.scores + (int64_t)b * N;
+  if (N % 4 == 0 && (int64_t)pa.NP * N * 4 < ((int64_t)1 << 31) &&
+      (((uintptr_t)pa.pscore | (uintptr_t)sa.scores) & 15) == 0) {
+    // Thread t: keys p 2048 + h 1024 + 4 t .. + 3 (h = 0, 1), one 16-byte load
+    // per partial row, 16 rows in flight, added in row order.
+    const BufRsrc rps = make_rsrc(ps, (uint32_t)((int64_t)pa.NP * N * 4));
+    const BufRsrc rsr = make_rsrc(srow, (uint32_t)N * 4u);
+    uint32_t off[2];
+    f32x4v s4[2];
 #pragma unroll
-  for (int i = 0; i < kSelKpt; ++i) {
-    const int e = e0 + i * kWave;
-    if (e < N) {
-      store_shared_dev(srow + e, sum[i]);
-      atomicAdd(&lh[digit1(float_key(sum[i]))], 1u);
+    for (int h = 0; h < 2; ++h) {
+      const int c = p * kLsChunk + h * (kLsChunk / 2) + 4 * tid;
+      off[h] = c < N ? (uint32_t)c * 4u : kBufOob;
+      s4[h] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j0 = 0; j0 < pa.NP; j0 += 16) {
+      f32x4v v[16][2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[j][h] = j0 + j < pa.NP ? __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rps, off[h], (uint32_t)((j0 + j) * N * 4), kCacheDefault))
+                                   : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < pa.NP) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) s4[h] += v[j][h];
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (off[h] == kBufOob) continue;
+      store4_dev(rsr, off[h], __builtin_bit_cast(u32x4, s4[h]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) atomicAdd(&lh[digit1(float_key(s4[h][r]))], 1u);
+    }
+  } else {
+    const int e0 = p * kLsChunk + wave * (kLsChunk / kItemWaves) + lane;
+    float sum[kSelKpt];
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) sum[i] = 0.f;
+    for (int j0 = 0; j0 < pa.NP; j0 += 4) {
+      float v[4][kSelKpt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i) {
+          const int e = e0 + i * kWave;
+          v[j][i] = (j0 + j < pa.NP && e < N) ? ps[(int64_t)(j0 + j) * N + e] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i) sum[i] += v[j][i];
+    }
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+      const int e = e0 + i * kWave;
+      if (e < N) {
+        store_shared_dev(srow + e, sum[i]);
+        atomicAdd(&lh[digit1(float_key(sum[i]))], 1u);
+      }
     }
   }
   __syncthreads();
