@@ -411,10 +411,10 @@ struct PfKwShape {
   static constexpr int WBYTES = VBYTES + KBYTES;             // one wave's stage buffers
   static constexpr int VPL = kPfStage * D / 8 / kWave;       // 16-byte chunks per lane (K or V)
   static constexpr int MSTR = D + 4;                         // floats per row of a merge slot
-  static constexpr int MBYTES = kPfRowsPerWave * MSTR * 4;   // one merge slot
+  static constexpr int MBYTES = kPfRowsPerWave * MSTR * 4;   // one merge slot (one per wave)
   static constexpr int QBYTES = 2 * KS * kWave * 16;          // Q^T fragments of the row block
   static constexpr int SBYTES = sizeof(SelectSmem<kPfKW>);
-  static constexpr int MAIN0 = kPfKW * WBYTES > kPfKW / 2 * MBYTES ? kPfKW * WBYTES : kPfKW / 2 * MBYTES;
+  static constexpr int MAIN0 = kPfKW * WBYTES > kPfKW * MBYTES ? kPfKW * WBYTES : kPfKW * MBYTES;
   static constexpr int MAIN = MAIN0 > SBYTES ? MAIN0 : SBYTES;  // stage buffers, merge slots, select
   static constexpr int LDS = MAIN + QBYTES;
   static constexpr int SKPT = 4;  // keys per thread kept in registers by the select (rows <= 2048)
@@ -657,56 +657,52 @@ __global__ __launch_bounds__(kPfKW* kWave, 2) void prefill_attn_kw_kernel(Prefil
       }
     }
   };
-  auto take = [&](int i) {
-    const float* sp = slot(i);
+  // Every wave puts its rows in its own slot; then wave w merges rows
+  // 4w .. 4w + 3 over the slots in wave order (16 lanes per row, D / 16 dims
+  // per lane) and writes them.
+  __syncthreads();  // every wave is past its stage buffers
+  put(wave);
+  __syncthreads();
+  {
+    constexpr int RPW = kPfRowsPerWave / kPfKW;  // rows merged per wave
+    constexpr int LPR = kWave / RPW;              // lanes per row
+    constexpr int DPL = D / LPR;                  // dims per lane
+    static_assert(RPW * kPfKW == kPfRowsPerWave && DPL % 4 == 0, "merge split");
+    const int row = wave * RPW + lane / LPR;
+    const int d0 = (lane % LPR) * DPL;
+    float M = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float* pr = sp + (16 * rb + li) * S::MSTR;
-      const float mo = pr[D], lo = pr[D + 1];
-      const float mn = fmaxf(m[rb], mo);
-      const float al = m[rb] == -INFINITY ? 0.f : fast_exp2(m[rb] - mn);
-      const float bo = mo == -INFINITY ? 0.f : fast_exp2(mo - mn);
+    for (int i = 0; i < kPfKW; ++i) M = fmaxf(M, slot(i)[row * S::MSTR + D]);
+    f32x4_t num[DPL / 4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[rb][db] = acc[rb][db] * al + *reinterpret_cast<const f32x4_t*>(pr + 16 * db + 4 * lg) * bo;
-      l[rb] = l[rb] * al + lo * bo;
-      m[rb] = mn;
+    for (int v = 0; v < DPL / 4; ++v) num[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPfKW; ++i) {
+      const float* pr = slot(i) + row * S::MSTR;
+      const float mi = pr[D];
+      const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+      den += pr[D + 1] * f;
+#pragma unroll
+      for (int v = 0; v < DPL / 4; ++v)
+        num[v] += *reinterpret_cast<const f32x4_t*>(pr + d0 + 4 * v) * f;
     }
-  };
-  // Halving merge: waves [h, 2h) put, waves [0, h) take (fixed order).
-#pragma unroll
-  for (int h = kPfKW / 2; h >= 1; h /= 2) {
-    __syncthreads();  // every wave is past its V buffer / the previous level
-    if (wave >= h && wave < 2 * h) put(wave - h);
-    __syncthreads();
-    if (wave < h) take(wave);
-  }
-  if (wave == 0) {
     if (C == 1) {
       // The only split: normalised output rows.
+      if (row < a.rows) {
+        const int tau = row / a.G, hh = row - tau * a.G;
+        float* o = a.out + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D + d0;
+        const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = 16 * rb + li;
-        if (row < a.rows) {
-          const int tau = row / a.G, hh = row - tau * a.G;
-          float* o = a.out + (((int64_t)b * a.Tq + tau) * a.Hq + g * a.G + hh) * D;
-          const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<f32x4_t*>(o + 16 * db + 4 * lg) = acc[rb][db] * inv;
-        }
+        for (int v = 0; v < DPL / 4; ++v) *reinterpret_cast<f32x4_t*>(o + 4 * v) = num[v] * inv;
       }
     } else {
-      float* part = a.part + ((int64_t)(b * a.Hkv + g) * C + c) * kPfRowsPerWave * (D + 4);
+      float* pr = a.part + (((int64_t)(b * a.Hkv + g) * C + c) * kPfRowsPerWave + row) * (D + 4);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float* pr = part + (int64_t)(16 * rb + li) * (D + 4);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(pr + 16 * db + 4 * lg) = acc[rb][db];
-        if (lg == 0) {
-          pr[D] = m[rb];
-          pr[D + 1] = l[rb];
-        }
+      for (int v = 0; v < DPL / 4; ++v) *reinterpret_cast<f32x4_t*>(pr + d0 + 4 * v) = num[v];
+      if (lane % LPR == 0) {
+        pr[D] = M;
+        pr[D + 1] = den;
       }
     }
   }
