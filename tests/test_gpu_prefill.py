@@ -135,3 +135,34 @@ def test_prefill_long_rows_workspace_reuse_new_inputs():
         torch.cuda.synchronize()
         ok, _, msgs = accept.check_index_sets(idx.cpu().numpy(), oracle.retrieval_scores(q, kv), k)
         assert ok, (seed, msgs[:3])
+
+
+@pytest.mark.parametrize("N,k,Tq", [(1440, 360, 8), (5000, 700, 4)], ids=["rows_1440", "rows_5000"])
+def test_prefill_scores_out_off_16_byte_alignment(N, k, Tq):
+    """The sums of the partial retrieval scores use 16-byte loads and stores
+    only when the score buffers are 16-byte aligned. A scores_out 4 bytes past
+    a 16-byte boundary takes the 4-byte path (the one-launch select at 1440
+    tokens, the long-row sum items at 5000) and gives the same scores and the
+    same selection as the aligned buffer."""
+    B, Hq, Hkv, D, Tmax = 2, 8, 8, 128, 40
+    _say("prefill scores_out alignment", B, Tq, Hq, Hkv, D, N, Tmax, k)
+    q, kv, vv, kt, vt = [t.to(DEV) for t in _inputs(B, Tq, Hq, Hkv, D, N, Tmax, seed=7)]
+    txt = torch.tensor([40, 17], dtype=torch.int32, device=DEV)
+    out_a, idx_a, sc_a = sv.prefill_attend_retrieve(q, kv, vv, kt, vt, txt, k, scores=True)
+    buf = torch.zeros(B * N + 4, dtype=torch.float32, device=DEV)
+    assert buf.data_ptr() % 16 == 0
+    sc_b = buf[1:1 + B * N]
+    out_b = torch.empty_like(out_a)
+    idx_b = torch.empty_like(idx_a)
+    ws = sv.new_workspace(sv.prefill_attend_retrieve_workspace_bytes(B, Tq, Hq, Hkv, D, N, Tmax), DEV)
+    lib = sv.load()
+    rc = lib.sv_prefill_attend_retrieve(
+        q.data_ptr(), B, Tq, Hq, kv.data_ptr(), vv.data_ptr(), kv.stride(0), kv.stride(1), N, Hkv,
+        D, kt.data_ptr(), vt.data_ptr(), kt.stride(0), kt.stride(1), txt.data_ptr(), Tmax,
+        sv.SV_BF16, 0.0, k, out_b.data_ptr(), idx_b.data_ptr(), sc_b.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), sv._stream(torch.device(DEV)))
+    torch.cuda.synchronize()
+    assert rc == 0, lib.sv_last_error().decode()
+    assert torch.equal(sc_b.view(B, N), sc_a)
+    assert torch.equal(idx_b, idx_a)
+    assert torch.equal(out_b, out_a)
