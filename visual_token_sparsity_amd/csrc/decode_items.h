@@ -939,17 +939,18 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int b, int g, int c
         for (int v = 0; v < VE; ++v) s = fmaf(qv[i][v], kf[v], s);
         z[i] = lane_group_sum<LPE>(s);
       }
-      if (off[j] != kBufOob) {
+      // No entry (offset past the extent, zeros loaded): weight 0, state kept.
+      // Selects, not a branch, so every load stays where it is issued.
+      const bool valid = off[j] != kBufOob;
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-          const float mn = fmaxf(m[i], z[i]);
-          const float al = fast_exp2(m[i] - mn);  // m = -inf -> 0
-          const float p = fast_exp2(z[i] - mn);
-          l[i] = l[i] * al + p;
+      for (int i = 0; i < G; ++i) {
+        const float mn = valid ? fmaxf(m[i], z[i]) : m[i];
+        const float al = valid ? fast_exp2(m[i] - mn) : 1.f;  // m = -inf -> 0
+        const float p = valid ? fast_exp2(z[i] - mn) : 0.f;
+        l[i] = l[i] * al + p;
 #pragma unroll
-          for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
-          m[i] = mn;
-        }
+        for (int v = 0; v < VE; ++v) acc[i][v] = fmaf(p, vf[v], acc[i][v] * al);
+        m[i] = mn;
       }
     }
     if constexpr (!LIST) break;
